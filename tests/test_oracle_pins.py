@@ -1,0 +1,488 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+library code tables, hand-worked cases, closed forms, invariants, library
+routines for special cases and brute force in exact rational arithmetic.
+
+Each `check_*` function takes the implementation under test so that the
+mutation tests at the bottom can plant a mistake in a copy of the oracle and
+show that some pin fails.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from lightning_indexer_top_04_amd import synth
+
+
+# ----------------------------------------------------------------------------
+# Decoders
+# ----------------------------------------------------------------------------
+
+def test_e4m3fn_full_table_matches_library_cast():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3fn(codes)
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_bf16_full_table_matches_library_cast():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_int4_nibble_table_by_enumeration():
+    # byte = hi<<4 | lo for every nibble pair; expected values written out
+    table = [0, 1, 2, 3, 4, 5, 6, 7, None, -7, -6, -5, -4, -3, -2, -1]
+    packed = np.array([[(hi << 4) | lo for lo in range(16)] for hi in range(16)],
+                      dtype=np.uint8).reshape(256, 1)
+    vals = O.decode_int4(packed, 2)
+    for b in range(256):
+        lo, hi = b & 0xF, b >> 4
+        for got, nib in ((vals[b, 0], lo), (vals[b, 1], hi)):
+            if table[nib] is None:
+                assert math.isnan(got)
+            else:
+                assert got == table[nib]
+
+
+def test_int4_encoder_round_trip():
+    x = torch.tensor([[7.0, -7.0, 3.5, -0.49, 0.0, 2.5, -2.5, 1.5]])
+    packed, scale = synth.encode_int4_rows(x)
+    assert scale.item() == 1.0
+    vals = O.decode_int4(packed.numpy(), 8)
+    # round half to even: 3.5->4, -0.49->0, 2.5->2, -2.5->-2, 1.5->2
+    assert vals.tolist() == [[7, -7, 4, 0, 0, 2, -2, 2]]
+
+
+# ----------------------------------------------------------------------------
+# Indexer scores
+# ----------------------------------------------------------------------------
+
+HAND_Q = np.array([[1.0, -2.0, 0.5], [0.25, 1.0, -1.0]])
+HAND_W = np.array([2.0, 0.5])
+HAND_K = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 1.0], [2.0, -1.0, 4.0],
+                   [-1.0, -1.0, -1.0]])
+HAND_SCALE = np.array([1.0, 1.0, 0.5, 3.0])
+# Worked by hand:
+#   k0: head dots (1, 0.25)        -> 2*1 + 0.5*0.25       = 2.125
+#   k1: head dots (-1.5, 0)        -> 0 + 0                = 0
+#   k2: head dots (6, -4.5)        -> 2*6 + 0              = 12
+#   k3: head dots (0.5, -0.25)     -> 2*0.5 + 0            = 1
+# with scale (1, 1, 0.5, 3) the dots of k2 halve and those of k3 triple:
+#   k2 -> 2*3 = 6, k3 -> 2*1.5 = 3
+HAND_I = [2.125, 0.0, 12.0, 1.0]
+HAND_I_SCALED = [2.125, 0.0, 6.0, 3.0]
+
+
+def check_hand_scores(f):
+    assert np.allclose(f(HAND_Q, HAND_W, HAND_K, None), HAND_I, rtol=0, atol=1e-15)
+    assert np.allclose(f(HAND_Q, HAND_W, HAND_K, HAND_SCALE), HAND_I_SCALED,
+                       rtol=0, atol=1e-15)
+
+
+def test_scores_hand_worked_case():
+    check_hand_scores(O.index_scores)
+
+
+def check_score_closed_forms(f):
+    rng = np.random.default_rng(11)
+    H, d, L = 5, 7, 40
+    q = rng.standard_normal((H, d))
+    w = rng.uniform(0, 1, H)
+    K = rng.standard_normal((L, d))
+    s = rng.uniform(0.5, 2, L)
+    base = f(q, w, K, s)
+    # basis-vector keys: k_s = c e_i gives I = sum_j w_j max(0, c q_ji)
+    for i in range(d):
+        for c in (1.5, -2.0):
+            e = np.zeros((1, d)); e[0, i] = c
+            want = sum(w[j] * max(0.0, c * q[j, i]) for j in range(H))
+            assert abs(f(q, w, e, None)[0] - want) <= 1e-12 * max(1, abs(want))
+    # one-hot weights select one head
+    for j in range(H):
+        oh = np.zeros(H); oh[j] = 1.0
+        got = f(q, oh, K, None)
+        assert np.allclose(got, np.maximum(K @ q[j], 0), rtol=1e-13, atol=1e-13)
+    # q = 0 gives zero everywhere
+    assert np.all(f(np.zeros((H, d)), w, K, s) == 0)
+    # homogeneity in w and in the per-token scale
+    assert np.allclose(f(q, 3 * w, K, s), 3 * base, rtol=1e-13, atol=1e-13)
+    s2 = s.copy(); s2[5] *= 4.0
+    got = f(q, w, K, s2)
+    assert np.isclose(got[5], 4 * base[5], rtol=1e-13, atol=1e-13)
+    assert np.allclose(np.delete(got, 5), np.delete(base, 5), rtol=0, atol=0)
+    # permuting tokens permutes scores
+    perm = rng.permutation(L)
+    assert np.allclose(f(q, w, K[perm], s[perm]), base[perm], rtol=1e-13, atol=1e-13)
+    # flipping the sign of one head's query switches the ReLU side
+    q2 = q.copy(); q2[0] = -q2[0]
+    d0 = K * s[:, None] @ q[0]
+    delta = f(q2, w, K, s) - base
+    assert np.allclose(delta, w[0] * (np.maximum(-d0, 0) - np.maximum(d0, 0)),
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_scores_closed_forms_and_invariants():
+    check_score_closed_forms(O.index_scores)
+
+
+def _exact_scores(q, w, K, s):
+    """Exact rational arithmetic over the same dyadic inputs."""
+    out = []
+    for t in range(K.shape[0]):
+        tot = Fraction(0)
+        for j in range(q.shape[0]):
+            dot = Fraction(0)
+            for i in range(q.shape[1]):
+                dot += Fraction(float(q[j, i])) * Fraction(float(K[t, i])) * Fraction(float(s[t]))
+            if dot > 0:
+                tot += Fraction(float(w[j])) * dot
+        out.append(tot)
+    return out
+
+
+def test_scores_match_exact_rationals_on_tiny_inputs():
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        H, d, L = rng.integers(1, 4), rng.integers(1, 9), rng.integers(1, 40)
+        # fp8-like and bf16-like dyadic values
+        q = np.round(rng.standard_normal((H, d)) * 64) / 64
+        w = np.round(rng.uniform(0, 1, H) * 32) / 32
+        K = O.decode_e4m3fn(rng.integers(0, 0x7E, size=(L, d)))
+        s = np.round(rng.uniform(0.1, 2, L) * 256) / 256
+        exact = _exact_scores(q, w, K, s)
+        got = O.index_scores(q, w, K, s)
+        for g, e in zip(got, exact):
+            assert abs(Fraction(float(g)) - e) <= Fraction(1, 10 ** 12) * max(1, abs(e))
+
+
+def test_score_magnitude_bounds_score():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 9)); w = rng.uniform(0, 1, 4)
+    K = rng.standard_normal((30, 9)); s = rng.uniform(0.5, 2, 30)
+    I = O.index_scores(q, w, K, s)
+    A = O.score_magnitude(q, w, K, s)
+    assert np.all(np.abs(I) <= A + 1e-12)
+    # a single positive head with all-positive products reaches the bound
+    assert np.isclose(O.score_magnitude(np.ones((1, 3)), np.ones(1), np.ones((1, 3)))[0], 3)
+
+
+# ----------------------------------------------------------------------------
+# Top-k
+# ----------------------------------------------------------------------------
+
+def check_topk_property(f):
+    rng = np.random.default_rng(7)
+    for L, k in ((50, 10), (200, 64), (9, 20), (64, 64)):
+        s = np.round(rng.standard_normal(L) * 4) / 4     # many ties
+        sel, tau = f(s, k)
+        n = min(k, L)
+        assert len(sel) == n and len(set(sel.tolist())) == n
+        rest = np.setdiff1d(np.arange(L), sel)
+        if len(rest):
+            assert s[sel].min() >= s[rest].max()
+            # ties at the threshold keep the lower positions
+            t = s[sel].min()
+            tied_out = rest[s[rest] == t]
+            tied_in = sel[s[sel] == t]
+            if len(tied_out):
+                assert tied_in.max() < tied_out.min()
+        if L >= k:
+            assert tau == s[sel].min()
+        else:
+            assert tau is None
+
+
+def test_topk_defining_property():
+    check_topk_property(O.topk)
+
+
+def test_topk_hand_case_and_signed_zero():
+    s = np.array([3.0, 1.0, 3.0, 2.0, -0.0, 0.0, -1.0])
+    sel, tau = O.topk(s, 3)
+    assert sel.tolist() == [0, 2, 3] and tau == 2.0
+    sel, tau = O.topk(s, 5)
+    assert sel.tolist() == [0, 2, 3, 1, 4] and tau == 0.0
+    sel, tau = O.topk(s, 6)
+    assert sel.tolist() == [0, 2, 3, 1, 4, 5]
+    sel, tau = O.topk(s, 10)
+    assert sorted(sel.tolist()) == list(range(7)) and tau is None
+
+
+def test_topk_agrees_with_argpartition_up_to_ties():
+    rng = np.random.default_rng(1)
+    s = rng.standard_normal(5000)
+    sel, tau = O.topk(s, 300)
+    ref = np.argpartition(-s, 299)[:300]
+    assert set(sel.tolist()) == set(ref.tolist())
+
+
+def test_band_contains_threshold_neighbours():
+    s = np.array([1.0, 1.0005, 0.9995, 2.0, 0.5])
+    assert O.band(s, 1.0, 1e-3).tolist() == [0, 1, 2]
+    assert O.band(s, None, 1e-3).size == 0
+
+
+def test_planted_recovery_tiny_f32():
+    """Planted tokens of the tiny case come back in the top-256 (floor 0.75
+    at its fixed seed; chance level is 256/4096)."""
+    di = synth.make_decode_inputs(synth.TINY_F32, with_attn=False)
+    L = int(di.seq_lens[0])
+    K = O.request_rows(di.ikeys.numpy().astype(np.float64), di.page_table[0].numpy(), L, 64)
+    I = O.index_scores(di.q_idx[0].double().numpy(), di.w[0].double().numpy(), K)
+    sel, _ = O.topk(I, 256)
+    r = O.recall(sel, di.planted[0])
+    assert r >= 0.75
+
+
+def test_planted_recovery_dsa_shape_small():
+    wl = synth.scaled(synth.DSA_128K, seq_lens=(8192,), n_planted=256, k=256)
+    di = synth.make_decode_inputs(wl, with_attn=False)
+    L = 8192
+    codes = O.request_rows(di.ikeys.numpy(), di.page_table[0].numpy(), L, 64)
+    sc = O.request_rows(di.iscale.numpy(), di.page_table[0].numpy(), L, 64)
+    K = O.decode_e4m3fn(codes)
+    q = O.decode_bf16(synth.bf16_bits(di.q_idx[0]))
+    I = O.index_scores(q, di.w[0].double().numpy(), K, sc)
+    sel, _ = O.topk(I, 256)
+    assert O.recall(sel, di.planted[0]) == 1.0
+
+
+# ----------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------
+
+def _sdpa(q, K, V, scale):
+    qt = torch.from_numpy(q)[None, :, None, :]           # [1][H][1][dk]
+    kt = torch.from_numpy(K)[None, None].expand(1, q.shape[0], *K.shape)
+    vt = torch.from_numpy(V)[None, None].expand(1, q.shape[0], *V.shape)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o[0, :, 0].numpy()
+
+
+def check_attention(f):
+    rng = np.random.default_rng(2)
+    H, n, dk, dv = 6, 37, 16, 12
+    q = rng.standard_normal((H, dk)); K = rng.standard_normal((n, dk))
+    V = rng.standard_normal((n, dv))
+    out, lse = f(q, K, V, 0.3)
+    assert np.allclose(out, _sdpa(q, K, V, 0.3), rtol=1e-12, atol=1e-12)
+    # lse by its definition through a library logsumexp
+    ref_lse = torch.logsumexp(torch.from_numpy(0.3 * q @ K.T), dim=1).numpy()
+    assert np.allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+    # one row: the output is that value row and lse is its logit
+    o1, l1 = f(q, K[3:4], V[3:4], 0.3)
+    assert np.allclose(o1, np.broadcast_to(V[3], o1.shape), rtol=0, atol=1e-15)
+    assert np.allclose(l1, 0.3 * q @ K[3], rtol=1e-14)
+    # identical keys: the mean of the values, lse = logit + ln n
+    Kc = np.broadcast_to(K[0], K.shape)
+    oc, lc = f(q, Kc, V, 0.3)
+    assert np.allclose(oc, np.broadcast_to(V.mean(0), oc.shape), atol=1e-12)
+    assert np.allclose(lc, 0.3 * q @ K[0] + math.log(n), atol=1e-12)
+    # a dominant logit takes all the weight
+    Kd = K.copy(); Kd[9] = 50.0 * q[0] / np.linalg.norm(q[0]) ** 2 / 0.3
+    od, _ = f(q[:1], Kd, V, 0.3)
+    assert np.allclose(od[0], V[9], atol=1e-12)
+    # row order does not matter
+    perm = rng.permutation(n)
+    op, lp = f(q, K[perm], V[perm], 0.3)
+    assert np.allclose(op, out, atol=1e-13) and np.allclose(lp, lse, atol=1e-13)
+
+
+def test_attention_pins():
+    check_attention(O.attention)
+
+
+def test_attention_empty_selection():
+    out, lse = O.attention(np.ones((2, 3)), np.zeros((0, 3)), np.zeros((0, 4)), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_mla_is_attention_with_latent_values():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((4, 24)); kv = rng.standard_normal((19, 24))
+    out, _ = O.mla_decode(q, kv, 16, 0.2)
+    assert np.allclose(out, _sdpa(q, kv, kv[:, :16].copy(), 0.2), atol=1e-12)
+
+
+def test_lse_merge_equals_whole():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((3, 8)); K = rng.standard_normal((50, 8))
+    V = rng.standard_normal((50, 5))
+    whole = O.attention(q, K, V, 0.5)
+    parts = [O.attention(q, K[a:b], V[a:b], 0.5) for a, b in ((0, 13), (13, 40), (40, 50))]
+    mo, ml = O.lse_merge(parts)
+    assert np.allclose(mo, whole[0], atol=1e-12) and np.allclose(ml, whole[1], atol=1e-12)
+
+
+def test_decode_step_dense_when_k_covers_all():
+    """k >= L: the step reduces to dense attention over the whole cache."""
+    rng = np.random.default_rng(8)
+    L, H, d = 30, 3, 6
+    qi = rng.standard_normal((H, d)); w = rng.uniform(0, 1, H)
+    ik = rng.standard_normal((L, d))
+    qa = rng.standard_normal((5, 10)); kv = rng.standard_normal((L, 10))
+    sel, tau, _, out, lse = O.decode_step(qi, w, ik, None, qa, kv, None, 64, 0.3, 7)
+    assert tau is None and sorted(sel.tolist()) == list(range(L))
+    assert np.allclose(out, _sdpa(qa, kv, kv[:, :7].copy(), 0.3), atol=1e-12)
+
+
+def test_request_rows_follow_page_table():
+    pool = np.arange(4 * 2 * 1).reshape(4, 2, 1)     # page p slot j -> 2p+j
+    rows = O.request_rows(pool, np.array([2, 0, 3]), 5, 2)
+    assert rows[:, 0].tolist() == [4, 5, 0, 1, 6]
+
+
+# ----------------------------------------------------------------------------
+# Two-stage search and prefill
+# ----------------------------------------------------------------------------
+
+def test_two_stage_reduces_to_exact_topk_when_all_kept():
+    rng = np.random.default_rng(9)
+    L, H, d = 300, 4, 8
+    q = rng.standard_normal((H, d)); w = rng.uniform(0, 1, H)
+    k8 = rng.standard_normal((L, d)); k4 = np.round(k8 * 2)
+    fin, cand = O.two_stage_topk(q, w, k4, None, k8, None, L, 20)
+    exact, _ = O.topk(O.index_scores(q, w, k8), 20)
+    assert sorted(fin.tolist()) == sorted(exact.tolist())
+    assert len(cand) == L
+
+
+def test_two_stage_recall_not_below_compact_only():
+    rng = np.random.default_rng(10)
+    L, H, d = 2000, 8, 16
+    q = rng.standard_normal((H, d)); w = rng.uniform(0, 1, H)
+    k8 = rng.standard_normal((L, d))
+    k4 = np.clip(np.round(k8 * 1.2), -7, 7)
+    fin, cand = O.two_stage_topk(q, w, k4, None, k8, None, 200, 50)
+    exact, _ = O.topk(O.index_scores(q, w, k8), 50)
+    only4, _ = O.topk(O.index_scores(q, w, k4), 50)
+    assert O.recall(fin, exact) >= O.recall(only4, exact)
+    assert set(fin.tolist()) <= set(cand.tolist())
+    # every exact winner that survived stage 1 is in the final set
+    assert set(exact.tolist()) & set(cand.tolist()) <= set(fin.tolist())
+
+
+def test_prefill_rows_equal_decode_on_visible_prefix_and_are_causal():
+    rng = np.random.default_rng(12)
+    hist, T, H, d, k = 40, 6, 3, 5, 16
+    q = rng.standard_normal((T, H, d)); w = rng.uniform(0, 1, (T, H))
+    K = rng.standard_normal((hist + T, d)); s = rng.uniform(0.5, 2, hist + T)
+    res = O.prefill_index_topk(q, w, K, s, hist, k)
+    for i in range(T):
+        vis = hist + i + 1
+        sel, tau, sc = res[i]
+        assert sc.shape == (vis,)
+        ref, _ = O.topk(O.index_scores(q[i], w[i], K[:vis], s[:vis]), k)
+        assert sel.tolist() == ref.tolist()
+    # changing a key beyond a query's position does not change its result
+    K2 = K.copy(); K2[hist + 3:] = 100.0
+    res2 = O.prefill_index_topk(q, w, K2, s, hist, k, rows=[0, 1, 2])
+    for i in (0, 1, 2):
+        assert res2[i][0].tolist() == res[i][0].tolist()
+
+
+# ----------------------------------------------------------------------------
+# Mutation tests: a plausible mistake planted in a copy of the oracle must
+# fail at least one pin above.
+# ----------------------------------------------------------------------------
+
+def _fails(check, impl):
+    try:
+        check(impl)
+    except AssertionError:
+        return True
+    return False
+
+
+def _scores_no_relu(q, w, K, s=None):
+    k = K * s[:, None] if s is not None else K
+    return (w[:, None] * (q @ k.T)).sum(0)
+
+
+def _scores_w_reversed(q, w, K, s=None):
+    return O.index_scores(q, w[::-1], K, s)
+
+
+def _scores_scale_squared(q, w, K, s=None):
+    return O.index_scores(q, w, K, None if s is None else s * s)
+
+
+def _scores_relu_after_sum(q, w, K, s=None):
+    k = K * s[:, None] if s is not None else K
+    return np.maximum((w[:, None] * (q @ k.T)).sum(0), 0)
+
+
+def _scores_transposed_query(q, w, K, s=None):
+    # reads the query matrix column-major by mistake where it is square enough
+    qq = q.reshape(q.shape[1], q.shape[0]).T if q.shape[0] != q.shape[1] else q.T
+    return O.index_scores(qq, w, K, s)
+
+
+@pytest.mark.parametrize("mut", [_scores_no_relu, _scores_w_reversed,
+                                 _scores_scale_squared, _scores_relu_after_sum,
+                                 _scores_transposed_query])
+def test_score_mutants_are_caught(mut):
+    assert _fails(check_hand_scores, mut) or _fails(check_score_closed_forms, mut)
+
+
+def _topk_ascending(s, k):
+    s = np.asarray(s); L = len(s)
+    order = np.lexsort((np.arange(L), s))
+    return order[:min(k, L)], (float(s[order[k - 1]]) if L >= k else None)
+
+
+def _topk_ties_high_position(s, k):
+    s = np.asarray(s); L = len(s)
+    order = np.lexsort((-np.arange(L), -s))
+    return order[:min(k, L)], (float(s[order[k - 1]]) if L >= k else None)
+
+
+def _topk_off_by_one(s, k):
+    sel, tau = O.topk(s, k)
+    return sel[:-1] if len(sel) > 1 else sel, tau
+
+
+@pytest.mark.parametrize("mut", [_topk_ascending, _topk_ties_high_position,
+                                 _topk_off_by_one])
+def test_topk_mutants_are_caught(mut):
+    assert _fails(check_topk_property, mut)
+
+
+def _attn_no_max_shift_wrong_lse(q, K, V, sc):
+    out, lse = O.attention(q, K, V, sc)
+    return out, lse - np.log(K.shape[0])
+
+
+def _attn_unscaled(q, K, V, sc):
+    return O.attention(q, K, V, 1.0)
+
+
+def _attn_values_from_keys(q, K, V, sc):
+    out, lse = O.attention(q, K, K[:, :V.shape[1]] if K.shape[1] >= V.shape[1]
+                           else V, sc)
+    return out, lse
+
+
+def _attn_no_normalise(q, K, V, sc):
+    logits = sc * (q @ K.T)
+    m = logits.max(1)
+    p = np.exp(logits - m[:, None])
+    return p @ V, m + np.log(p.sum(1))
+
+
+@pytest.mark.parametrize("mut", [_attn_no_max_shift_wrong_lse, _attn_unscaled,
+                                 _attn_values_from_keys, _attn_no_normalise])
+def test_attention_mutants_are_caught(mut):
+    assert _fails(check_attention, mut)
