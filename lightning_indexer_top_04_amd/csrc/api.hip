@@ -1,0 +1,588 @@
+// C ABI of liblsi: argument validation (before anything is enqueued),
+// workspace carving and the launch sequences of each entry point.
+#include <mutex>
+#include <string>
+
+#include "lsi_internal.hpp"
+
+namespace lsi {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int32_t fail(int32_t status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int32_t check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(LSI_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LSI_OK;
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define LSI_REQUIRE(cond, msg)                                   \
+  do {                                                           \
+    if (!(cond)) return fail(LSI_ERR_INVALID_ARG, (msg));        \
+  } while (0)
+#define LSI_SUPPORT(cond, msg)                                   \
+  do {                                                           \
+    if (!(cond)) return fail(LSI_ERR_UNSUPPORTED, (msg));        \
+  } while (0)
+#define LSI_TRY(expr)                                            \
+  do {                                                           \
+    const int32_t _st = (expr);                                  \
+    if (_st != LSI_OK) return _st;                               \
+  } while (0)
+
+int32_t check_batch(const lsi_batch* b, bool need_pages) {
+  LSI_REQUIRE(b != nullptr, "batch is NULL");
+  LSI_REQUIRE(b->num_req >= 1, "batch->num_req must be >= 1");
+  LSI_REQUIRE(b->max_seq_len >= 0, "batch->max_seq_len must be >= 0");
+  LSI_REQUIRE(b->reserved == 0, "batch->reserved must be 0");
+  LSI_REQUIRE(b->seq_lens != nullptr, "batch->seq_lens is NULL");
+  if (need_pages) {
+    LSI_REQUIRE(b->page_table != nullptr, "batch->page_table is NULL");
+    LSI_REQUIRE(b->max_pages >= 1, "batch->max_pages must be >= 1");
+  }
+  return LSI_OK;
+}
+
+int32_t check_cache(const lsi_paged_cache* c, const lsi_batch* b, const char* name) {
+  const std::string n(name);
+  LSI_REQUIRE(c != nullptr, n + " is NULL");
+  LSI_REQUIRE(c->data != nullptr, n + "->data is NULL");
+  LSI_REQUIRE(c->page_size >= 1, n + "->page_size must be >= 1");
+  LSI_REQUIRE(c->num_pages >= 1, n + "->num_pages must be >= 1");
+  LSI_REQUIRE(c->dim >= 1, n + "->dim must be >= 1");
+  LSI_REQUIRE((int64_t)c->num_pages * c->page_size <= INT32_MAX,
+              n + ": num_pages * page_size exceeds 2^31-1 tokens");
+  LSI_REQUIRE((int64_t)b->max_pages * c->page_size >= b->max_seq_len,
+              n + ": batch->max_seq_len exceeds max_pages * page_size");
+  LSI_REQUIRE(aligned(c->data, 16), n + "->data must be 16-byte aligned");
+  switch (c->dtype) {
+    case LSI_F32:
+    case LSI_BF16:
+      LSI_REQUIRE(c->scale == nullptr, n + "->scale must be NULL for f32/bf16 caches");
+      break;
+    case LSI_FP8_E4M3:
+    case LSI_INT4:
+      LSI_REQUIRE(c->scale != nullptr, n + "->scale is required for fp8/int4 caches");
+      break;
+    default:
+      return fail(LSI_ERR_INVALID_ARG, n + "->dtype is not an LSI element type");
+  }
+  return LSI_OK;
+}
+
+int32_t check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return LSI_OK;
+  if (ws == nullptr) return fail(LSI_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, kWsAlign)) return fail(LSI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need)
+    return fail(LSI_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                       " bytes, have " + std::to_string(have));
+  return LSI_OK;
+}
+
+// ---- indexer scan ----------------------------------------------------------
+// scores == nullptr with ld == 0 means the caller keeps scores internally
+int32_t validate_index(const lsi_paged_cache* ikeys, const lsi_batch* batch, const void* q,
+                       int32_t n_heads, int32_t dim, const float* w, const float* scores,
+                       int64_t ld, bool internal_scores = false) {
+  LSI_TRY(check_batch(batch, true));
+  LSI_TRY(check_cache(ikeys, batch, "ikeys"));
+  LSI_REQUIRE(q != nullptr && w != nullptr, "q and w must be non-NULL");
+  if (!internal_scores) {
+    LSI_REQUIRE(scores != nullptr, "scores must be non-NULL");
+    LSI_REQUIRE(ld >= batch->max_seq_len && ld >= 1, "ld must be >= max(1, batch->max_seq_len)");
+  }
+  LSI_REQUIRE(dim == ikeys->dim, "dim must equal ikeys->dim");
+  LSI_REQUIRE(n_heads >= 1, "n_heads must be >= 1");
+  if (ikeys->dtype == LSI_FP8_E4M3 || ikeys->dtype == LSI_INT4) {
+    LSI_SUPPORT(dim == 128 && n_heads == 64, "fp8/int4 indexer keys need 64 heads of dim 128");
+    LSI_SUPPORT(is_pow2(ikeys->page_size) && ikeys->page_size % 32 == 0,
+                "fp8/int4 indexer keys need a power-of-two page_size that is a multiple of 32");
+    LSI_REQUIRE(aligned(q, 16), "q must be 16-byte aligned");
+  } else if (ikeys->dtype == LSI_F32) {
+    LSI_SUPPORT(dim <= 256 && (int64_t)n_heads * dim <= 8192,
+                "f32 indexer keys support dim <= 256 and n_heads*dim <= 8192");
+  } else {
+    return fail(LSI_ERR_UNSUPPORTED, "indexer keys must be fp8, int4 or f32");
+  }
+  return LSI_OK;
+}
+
+ScanArgs scan_args(const lsi_paged_cache* ikeys, const lsi_batch* batch, const void* q,
+                   int32_t n_heads, int32_t dim, const float* w, float* scores, int64_t ld) {
+  ScanArgs a;
+  a.keys = ikeys->data;
+  a.kscale = ikeys->scale;
+  a.num_pages = ikeys->num_pages;
+  a.page_size = ikeys->page_size;
+  a.seq_lens = batch->seq_lens;
+  a.page_table = batch->page_table;
+  a.max_pages = batch->max_pages;
+  a.max_seq_len = batch->max_seq_len;
+  a.num_req = batch->num_req;
+  a.q = q;
+  a.w = w;
+  a.scores = scores;
+  a.ld = ld;
+  a.n_heads = n_heads;
+  a.dim = dim;
+  return a;
+}
+
+hipError_t run_scan(int dtype, const ScanArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case LSI_FP8_E4M3: return launch_scan_fp8(a, s);
+    case LSI_INT4: return launch_scan_int4(a, s);
+    default: return launch_scan_f32(a, s);
+  }
+}
+
+// ---- top-k -----------------------------------------------------------------
+int32_t validate_topk(const float* scores, int64_t ld, const lsi_batch* batch, int32_t k,
+                      const int32_t* idx, const int32_t* count) {
+  LSI_TRY(check_batch(batch, false));
+  LSI_REQUIRE(scores != nullptr && idx != nullptr && count != nullptr,
+              "scores, idx and count must be non-NULL");
+  LSI_REQUIRE(ld >= batch->max_seq_len && ld >= 1, "ld must be >= max(1, batch->max_seq_len)");
+  LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  return LSI_OK;
+}
+
+// ---- attention -------------------------------------------------------------
+int32_t validate_attn(const lsi_paged_cache* kv, const lsi_paged_cache* v, const lsi_batch* batch,
+                      const void* q, int32_t n_heads, int32_t dk, int32_t dv, const int32_t* idx,
+                      int32_t k, float sm_scale, const void* out, const float* lse) {
+  LSI_TRY(check_batch(batch, true));
+  LSI_TRY(check_cache(kv, batch, "kv"));
+  LSI_REQUIRE(q != nullptr && idx != nullptr && out != nullptr && lse != nullptr,
+              "q, idx, out and lse must be non-NULL");
+  LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  LSI_REQUIRE(n_heads >= 1, "n_heads must be >= 1");
+  LSI_REQUIRE(sm_scale == sm_scale && sm_scale > 0.f, "sm_scale must be a positive number");
+  LSI_REQUIRE(dk == kv->dim, "dk must equal kv->dim");
+  if (kv->dtype == LSI_BF16) {
+    LSI_SUPPORT(dk == 576 && dv == 512, "bf16 latent attention needs dk = 576 and dv = 512");
+    LSI_SUPPORT(n_heads % 64 == 0, "bf16 latent attention needs n_heads a multiple of 64");
+    LSI_REQUIRE(v == nullptr, "bf16 latent attention reads V from kv; v must be NULL");
+    LSI_REQUIRE(aligned(q, 16) && aligned(out, 16), "q and out must be 16-byte aligned");
+  } else if (kv->dtype == LSI_F32) {
+    LSI_SUPPORT(dk <= 256 && dv >= 1 && dv <= 256, "f32 attention supports dk, dv <= 256");
+    LSI_SUPPORT(n_heads <= 65535, "f32 attention supports n_heads <= 65535");
+    LSI_REQUIRE(v != nullptr, "f32 attention needs a separate value cache v");
+    LSI_TRY(check_cache(v, batch, "v"));
+    LSI_REQUIRE(v->dtype == LSI_F32 && v->dim == dv, "v must be f32 with dim == dv");
+    LSI_REQUIRE(v->page_size == kv->page_size && v->num_pages == kv->num_pages,
+                "v must share kv's page geometry");
+  } else {
+    return fail(LSI_ERR_UNSUPPORTED, "attention caches must be bf16 (latent) or f32");
+  }
+  return LSI_OK;
+}
+
+AttnArgs attn_args(const lsi_paged_cache* kv, const lsi_paged_cache* v, const lsi_batch* batch,
+                   const void* q, int32_t n_heads, int32_t dk, int32_t dv, const int32_t* idx,
+                   int32_t k, float sm_scale, void* out, float* lse, void* ws) {
+  AttnArgs a;
+  a.kv = kv->data;
+  a.v = v ? v->data : nullptr;
+  a.num_pages = kv->num_pages;
+  a.page_size = kv->page_size;
+  a.seq_lens = batch->seq_lens;
+  a.page_table = batch->page_table;
+  a.max_pages = batch->max_pages;
+  a.max_seq_len = batch->max_seq_len;
+  a.num_req = batch->num_req;
+  a.q = q;
+  a.n_heads = n_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.idx = idx;
+  a.k = k;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  return a;
+}
+
+size_t attn_ws(int dtype, int num_req, int n_heads, int dv, int k) {
+  return dtype == LSI_BF16 ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
+}
+
+hipError_t run_attn(int dtype, const AttnArgs& a, hipStream_t s) {
+  return dtype == LSI_BF16 ? launch_mla_bf16(a, s) : launch_attn_f32(a, s);
+}
+
+int64_t scores_ld(int max_seq_len) { return std::max<int64_t>(64, ceil_div(max_seq_len, 64) * 64); }
+
+// ---- prefill events ----------------------------------------------------------
+struct PrefillEvents {
+  hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+  bool ready = false;
+};
+std::mutex g_ev_mu;
+PrefillEvents g_ev[64];
+
+}  // namespace
+}  // namespace lsi
+
+using namespace lsi;
+
+extern "C" {
+
+int32_t lsi_version(void) { return 100; }
+
+const char* lsi_status_string(int32_t status) {
+  switch (status) {
+    case LSI_OK: return "ok";
+    case LSI_ERR_INVALID_ARG: return "invalid argument";
+    case LSI_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LSI_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LSI_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lsi_last_error(void) { return g_last_error.c_str(); }
+
+int32_t lsi_index_scores(const lsi_paged_cache* ikeys, const lsi_batch* batch, const void* q,
+                         int32_t n_heads, int32_t dim, const float* w, float* scores, int64_t ld,
+                         hipStream_t stream) {
+  LSI_TRY(validate_index(ikeys, batch, q, n_heads, dim, w, scores, ld));
+  const ScanArgs a = scan_args(ikeys, batch, q, n_heads, dim, w, scores, ld);
+  run_scan(ikeys->dtype, a, stream);
+  return check_launch("lsi_index_scores");
+}
+
+size_t lsi_topk_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k) {
+  (void)k;
+  if (num_req < 1 || max_seq_len < 0) return 0;
+  return topk_ws_bytes(num_req, max_seq_len);
+}
+
+int32_t lsi_topk(const float* scores, int64_t ld, const lsi_batch* batch, int32_t k, int32_t* idx,
+                 int32_t* count, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  LSI_TRY(validate_topk(scores, ld, batch, k, idx, count));
+  LSI_TRY(check_ws(workspace, ws_bytes, topk_ws_bytes(batch->num_req, batch->max_seq_len)));
+  TopkArgs t;
+  t.scores = scores;
+  t.ld = ld;
+  t.seq_lens = batch->seq_lens;
+  t.num_req = batch->num_req;
+  t.max_len = batch->max_seq_len;
+  t.k = k;
+  t.idx = idx;
+  t.count = count;
+  t.ws = workspace;
+  launch_topk(t, false, stream);
+  return check_launch("lsi_topk");
+}
+
+size_t lsi_sparse_mla_workspace_bytes(int32_t num_req, int32_t n_heads, int32_t dv, int32_t k) {
+  if (num_req < 1 || n_heads < 1 || dv < 1 || k < 1) return 0;
+  // the bf16 latent path is the only one with scratch
+  if (n_heads % 64 != 0 || dv != 512) return 0;
+  return mla_ws_bytes(num_req, n_heads, dv, k);
+}
+
+int32_t lsi_sparse_mla_decode(const lsi_paged_cache* kv, const lsi_paged_cache* v,
+                              const lsi_batch* batch, const void* q, int32_t n_heads, int32_t dk,
+                              int32_t dv, const int32_t* idx, int32_t k, float sm_scale, void* out,
+                              float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  LSI_TRY(validate_attn(kv, v, batch, q, n_heads, dk, dv, idx, k, sm_scale, out, lse));
+  LSI_TRY(check_ws(workspace, ws_bytes, attn_ws(kv->dtype, batch->num_req, n_heads, dv, k)));
+  const AttnArgs a = attn_args(kv, v, batch, q, n_heads, dk, dv, idx, k, sm_scale, out, lse, workspace);
+  run_attn(kv->dtype, a, stream);
+  return check_launch("lsi_sparse_mla_decode");
+}
+
+size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k,
+                                       int32_t n_heads, int32_t dv) {
+  if (num_req < 1 || max_seq_len < 0 || k < 1 || n_heads < 1) return 0;
+  const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
+  const size_t tk = topk_ws_bytes(num_req, max_seq_len);
+  const size_t at = (n_heads % 64 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
+  return sc + tk + at;
+}
+
+int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                        const lsi_paged_cache* v, const lsi_batch* batch, const void* q_idx,
+                        int32_t n_idx_heads, int32_t idx_dim, const float* w, const void* q_attn,
+                        int32_t n_heads, int32_t dk, int32_t dv, float sm_scale, int32_t k,
+                        int32_t* idx, int32_t* count, void* out, float* lse, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  LSI_TRY(check_batch(batch, true));
+  const int64_t ld = scores_ld(batch->max_seq_len);
+  LSI_TRY(validate_index(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, nullptr, 0, true));
+  LSI_REQUIRE(ikeys->page_size == kv->page_size, "ikeys and kv must share the page size");
+  LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  LSI_REQUIRE(idx != nullptr && count != nullptr, "idx and count must be non-NULL");
+  LSI_TRY(validate_attn(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse));
+  const size_t need = lsi_decode_step_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
+  LSI_TRY(check_ws(workspace, ws_bytes, need));
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
+  void* topk_ws = ws;
+  ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
+  void* attn_wsp = ws;
+
+  ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
+  sa.zero_ptr = static_cast<uint32_t*>(topk_ws);     // the scan clears the top-k counters
+  sa.zero_words = topk_zero_words(batch->num_req);
+  run_scan(ikeys->dtype, sa, stream);
+
+  TopkArgs t;
+  t.scores = scores;
+  t.ld = ld;
+  t.seq_lens = batch->seq_lens;
+  t.num_req = batch->num_req;
+  t.max_len = batch->max_seq_len;
+  t.k = k;
+  t.idx = idx;
+  t.count = count;
+  t.ws = topk_ws;
+  launch_topk(t, true, stream);
+
+  const AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
+  run_attn(kv->dtype, a, stream);
+  return check_launch("lsi_decode_step");
+}
+
+size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t n_cand,
+                                     int32_t k) {
+  if (num_req < 1 || max_seq_len < 0 || n_cand < 1 || k < 1) return 0;
+  (void)k;
+  const size_t s4 = align_up((size_t)num_req * scores_ld(max_seq_len) * 4, kWsAlign);
+  const size_t t1 = topk_ws_bytes(num_req, max_seq_len);
+  const size_t cand = align_up((size_t)num_req * n_cand * 4, kWsAlign);
+  const size_t ccount = align_up((size_t)num_req * 4, kWsAlign);
+  const size_t s8 = align_up((size_t)num_req * n_cand * 4, kWsAlign);
+  const size_t t2 = topk_ws_bytes(num_req, n_cand);
+  return s4 + t1 + cand + ccount + s8 + t2;
+}
+
+int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache* ikeys8,
+                           const lsi_batch* batch, const void* q, int32_t n_heads, int32_t dim,
+                           const float* w, int32_t n_cand, int32_t k, int32_t* idx,
+                           int32_t* count, int32_t* cand, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+  LSI_TRY(check_batch(batch, true));
+  const int64_t ld = scores_ld(batch->max_seq_len);
+  LSI_TRY(validate_index(ikeys4, batch, q, n_heads, dim, w, nullptr, 0, true));
+  LSI_TRY(validate_index(ikeys8, batch, q, n_heads, dim, w, nullptr, 0, true));
+  LSI_REQUIRE(ikeys4->dtype == LSI_INT4, "ikeys4 must be LSI_INT4");
+  LSI_REQUIRE(ikeys8->dtype == LSI_FP8_E4M3, "ikeys8 must be LSI_FP8_E4M3");
+  LSI_REQUIRE(ikeys4->page_size == ikeys8->page_size && ikeys4->num_pages == ikeys8->num_pages,
+              "ikeys4 and ikeys8 must share the page geometry");
+  LSI_REQUIRE(k >= 1 && n_cand >= k && n_cand <= 65536, "need 1 <= k <= n_cand <= 65536");
+  LSI_REQUIRE(idx != nullptr && count != nullptr, "idx and count must be non-NULL");
+  LSI_TRY(check_ws(workspace, ws_bytes,
+                   lsi_two_stage_workspace_bytes(batch->num_req, batch->max_seq_len, n_cand, k)));
+  const int B = batch->num_req;
+  char* ws = static_cast<char*>(workspace);
+  float* s4 = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * ld * 4, kWsAlign);
+  void* t1 = ws;
+  ws += topk_ws_bytes(B, batch->max_seq_len);
+  int32_t* cl = reinterpret_cast<int32_t*>(ws);
+  ws += align_up((size_t)B * n_cand * 4, kWsAlign);
+  int32_t* cc = reinterpret_cast<int32_t*>(ws);
+  ws += align_up((size_t)B * 4, kWsAlign);
+  float* s8 = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * n_cand * 4, kWsAlign);
+  void* t2 = ws;
+
+  // stage 1: compact keys over every token, keep n_cand
+  ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
+  a4.zero_ptr = static_cast<uint32_t*>(t1);
+  a4.zero_words = topk_zero_words(B);
+  launch_scan_int4(a4, stream);
+  TopkArgs ta;
+  ta.scores = s4;
+  ta.ld = ld;
+  ta.seq_lens = batch->seq_lens;
+  ta.num_req = B;
+  ta.max_len = batch->max_seq_len;
+  ta.k = n_cand;
+  ta.idx = cl;
+  ta.count = cc;
+  ta.ws = t1;
+  launch_topk(ta, true, stream);
+
+  // stage 2: exact fp8 scores of the candidates only, keep k
+  ScanArgs a8 = scan_args(ikeys8, batch, q, n_heads, dim, w, s8, n_cand);
+  a8.positions = cl;
+  a8.n_pos = n_cand;
+  a8.zero_ptr = static_cast<uint32_t*>(t2);
+  a8.zero_words = topk_zero_words(B);
+  launch_scan_fp8(a8, stream);
+  TopkArgs tb;
+  tb.scores = s8;
+  tb.ld = n_cand;
+  tb.seq_lens = cc;          // row length = number of stage-1 candidates
+  tb.num_req = B;
+  tb.max_len = n_cand;
+  tb.k = k;
+  tb.map = cl;               // slot -> position
+  tb.map_ld = n_cand;
+  tb.idx = idx;
+  tb.count = count;
+  tb.ws = t2;
+  launch_topk(tb, true, stream);
+  if (cand) {
+    const hipError_t e = hipMemcpyAsync(cand, cl, (size_t)B * n_cand * 4, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("lsi_two_stage_topk: ") + hipGetErrorString(e));
+  }
+  return check_launch("lsi_two_stage_topk");
+}
+
+size_t lsi_prefill_workspace_bytes(int32_t hist_len, int32_t T, int32_t dim, int32_t block_tokens,
+                                   int32_t k, int32_t scores_external) {
+  (void)k;
+  if (hist_len < 0 || T < 1 || dim < 1 || block_tokens < 1) return 0;
+  const int64_t ld = (int64_t)hist_len + T;
+  const size_t bufk = align_up((size_t)block_tokens * dim, kWsAlign);
+  const size_t bufs = align_up((size_t)block_tokens * 4, kWsAlign);
+  const size_t sc = scores_external ? 0 : align_up((size_t)T * ld * 4, kWsAlign);
+  return 2 * (bufk + bufs) + sc + topk_ws_bytes(T, (int)ld);
+}
+
+int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale, int32_t hist_len,
+                               const uint8_t* chunk_keys, const float* chunk_scale, int32_t T,
+                               const void* q, int32_t n_heads, int32_t dim, const float* w,
+                               int32_t k, int32_t block_tokens, int32_t* idx, int32_t* count,
+                               float* scores, void* workspace, size_t ws_bytes,
+                               hipStream_t s_compute, hipStream_t s_copy) {
+  LSI_REQUIRE(hist_len >= 0 && T >= 1, "need hist_len >= 0 and T >= 1");
+  LSI_REQUIRE((int64_t)hist_len + T <= INT32_MAX / 2, "hist_len + T too large");
+  LSI_REQUIRE(hist_len == 0 || (hist_keys != nullptr && hist_scale != nullptr),
+              "hist_keys and hist_scale are required when hist_len > 0");
+  LSI_REQUIRE(chunk_keys != nullptr && chunk_scale != nullptr, "chunk_keys and chunk_scale are required");
+  LSI_REQUIRE(q != nullptr && w != nullptr && idx != nullptr && count != nullptr,
+              "q, w, idx and count must be non-NULL");
+  LSI_SUPPORT(n_heads == 64 && dim == 128, "the prefill indexer needs 64 heads of dim 128");
+  LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  LSI_REQUIRE(block_tokens >= 32 && block_tokens % 32 == 0, "block_tokens must be a positive multiple of 32");
+  LSI_REQUIRE(aligned(q, 16) && aligned(chunk_keys, 16), "q and chunk_keys must be 16-byte aligned");
+  const size_t need = lsi_prefill_workspace_bytes(hist_len, T, dim, block_tokens, k, scores != nullptr);
+  LSI_TRY(check_ws(workspace, ws_bytes, need));
+  if (s_copy == nullptr) s_copy = s_compute;
+
+  const int64_t ld = (int64_t)hist_len + T;
+  char* ws = static_cast<char*>(workspace);
+  uint8_t* bufk[2];
+  float* bufs[2];
+  for (int i = 0; i < 2; ++i) {
+    bufk[i] = reinterpret_cast<uint8_t*>(ws);
+    ws += align_up((size_t)block_tokens * dim, kWsAlign);
+    bufs[i] = reinterpret_cast<float*>(ws);
+    ws += align_up((size_t)block_tokens * 4, kWsAlign);
+  }
+  float* sc = scores;
+  if (!sc) {
+    sc = reinterpret_cast<float*>(ws);
+    ws += align_up((size_t)T * ld * 4, kWsAlign);
+  }
+  void* tws = ws;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(LSI_ERR_HIP, "lsi_prefill_index_topk: no current device");
+  std::lock_guard<std::mutex> lock(g_ev_mu);
+  PrefillEvents& ev = g_ev[dev];
+  if (!ev.ready) {
+    hipError_t e = hipEventCreateWithFlags(&ev.start, hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&ev.copied[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ev.done[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
+    ev.ready = true;
+  }
+
+#define LSI_HIP(expr)                                                                     \
+  do {                                                                                    \
+    const hipError_t _e = (expr);                                                         \
+    if (_e != hipSuccess)                                                                 \
+      return fail(LSI_ERR_HIP, std::string("lsi_prefill_index_topk: ") + hipGetErrorString(_e)); \
+  } while (0)
+
+  // the copy stream must not overwrite buffers a previous call still reads
+  LSI_HIP(hipEventRecord(ev.start, s_compute));
+  LSI_HIP(hipStreamWaitEvent(s_copy, ev.start, 0));
+  PrefillScanArgs pa;
+  pa.q = q;
+  pa.w = w;
+  pa.T = T;
+  pa.hist_len = hist_len;
+  pa.scores = sc;
+  pa.ld = ld;
+  const int nblk = (int)ceil_div(hist_len, block_tokens);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int j = blk & 1;
+    const int tok0 = blk * block_tokens;
+    const int n = std::min(block_tokens, hist_len - tok0);
+    if (blk >= 2) LSI_HIP(hipStreamWaitEvent(s_copy, ev.done[j], 0));
+    LSI_HIP(hipMemcpyAsync(bufk[j], hist_keys + (size_t)tok0 * dim, (size_t)n * dim, hipMemcpyDefault, s_copy));
+    LSI_HIP(hipMemcpyAsync(bufs[j], hist_scale + tok0, (size_t)n * 4, hipMemcpyDefault, s_copy));
+    LSI_HIP(hipEventRecord(ev.copied[j], s_copy));
+    LSI_HIP(hipStreamWaitEvent(s_compute, ev.copied[j], 0));
+    pa.keys = bufk[j];
+    pa.kscale = bufs[j];
+    pa.tok0 = tok0;
+    pa.n_tok = n;
+    launch_prefill_scan(pa, s_compute);
+    LSI_HIP(hipEventRecord(ev.done[j], s_compute));
+  }
+  pa.keys = chunk_keys;
+  pa.kscale = chunk_scale;
+  pa.tok0 = hist_len;
+  pa.n_tok = T;
+  launch_prefill_scan(pa, s_compute);
+
+  TopkArgs t;
+  t.scores = sc;
+  t.ld = ld;
+  t.causal_base = hist_len;
+  t.num_req = T;
+  t.max_len = (int)ld;
+  t.k = k;
+  t.idx = idx;
+  t.count = count;
+  t.ws = tws;
+  launch_topk(t, false, s_compute);
+#undef LSI_HIP
+  return check_launch("lsi_prefill_index_topk");
+}
+
+}  // extern "C"

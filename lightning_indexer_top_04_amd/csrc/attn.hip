@@ -1,0 +1,341 @@
+// Sparse attention over the selected tokens (the "Multi-layer Indexer"
+// abstract: the layer attends only the k tokens its indexer kept).
+//
+// bf16 latent MLA (dk = 576 = 512 latent + 64 rope, dv = 512, one latent row
+// shared by all heads): a workgroup owns 64 heads of one request and one slice
+// of the selection; each of its 4 waves owns 16 heads.  Per 32-row tile the
+// selected rows are gathered through the page table into LDS twice: row-major
+// (the K operand) and transposed for the first 512 columns (the V operand).
+//   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, rows on M, heads on N, 18 K-steps)
+//   online softmax in the log2 domain, per head (lane column)
+//   O^T += V^T P^T (32 M-tiles of 16 latent dims, one K-step over the 32 rows)
+// The accumulator of S^T gives lane group g the rows {4g..4g+3, 16+4g..19+4g};
+// the transposed V tile stores its rows in exactly that order, so the
+// probabilities feed the second product straight from registers.  Splits of
+// the selection are merged with their log-sum-exp by a small combine kernel.
+#include "lsi_internal.hpp"
+
+namespace lsi {
+namespace {
+
+constexpr int kD = 576;
+constexpr int kDV = 512;
+constexpr int kRows = 32;        // rows per tile
+constexpr int kKStride = 584;    // bf16 elements per LDS row of the K tile
+constexpr int kVStride = 36;     // bf16 slots per LDS row of the V^T tile
+constexpr int kHeadsPerWg = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(4))) uint16_t u16x4;
+
+// slot of tile row rho inside a V^T row (see the header comment)
+__device__ __forceinline__ int vslot(int rho) {
+  return 8 * ((rho & 15) >> 2) + ((rho >> 4) << 2) + (rho & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
+                                                          int nsplit, float* part_o,
+                                                          float* part_lse) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDV * kVStride];
+  __shared__ int rowidx[kRows];
+
+  const int n_hg = a.n_heads / kHeadsPerWg;
+  const int bid = blockIdx.x;
+  const int split = bid % nsplit;
+  const int hg = (bid / nsplit) % n_hg;
+  const int b = bid / (nsplit * n_hg);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int head = hg * kHeadsPerWg + wave * 16 + n;
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int r0 = split * rows_per_split;
+  const int r1 = min(r0 + rows_per_split, a.k);
+
+  // query operand: lane holds Q[head][32u + 8g .. 32u + 8g + 7]
+  const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + head) * kD;
+  bf16x8 qr[kD / 32];
+#pragma unroll
+  for (int u = 0; u < kD / 32; ++u) qr[u] = *reinterpret_cast<const bf16x8*>(qh + 32 * u + 8 * g);
+
+  f32x4 o[kDV / 16];
+#pragma unroll
+  for (int j = 0; j < kDV / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  const float c = a.sm_scale * kLog2e;
+  const __bf16* kvb = static_cast<const __bf16*>(a.kv);
+  const int32_t* idxb = a.idx + (int64_t)b * a.k;
+
+  // Gather of one 32-row tile into registers: thread tid owns 16-byte chunks
+  // tid + 256*it of the tile (row = chunk / 72, column chunk = chunk % 72).
+  constexpr int kChunks = (kRows * (kD / 8)) / 256;   // 9
+  u32x4 pre[kChunks];
+  int pre_row = -1;                                   // tile row tid (tid < 32)
+  auto row_of = [&](int e) -> int {
+    if (e >= r1) return -1;
+    const int pos = idxb[e];
+    if (pos < 0 || pos >= L) return -1;
+    const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+    if ((unsigned)page >= (unsigned)a.num_pages) return -1;
+    return page * a.page_size + pos % a.page_size;
+  };
+  auto prefetch = [&](int base) {
+#pragma unroll
+    for (int it = 0; it < kChunks; ++it) {
+      const int ch = tid + 256 * it;
+      const int row = row_of(base + ch / (kD / 8));
+      pre[it] = row >= 0 ? *reinterpret_cast<const u32x4*>(kvb + (int64_t)row * kD + (ch % (kD / 8)) * 8)
+                         : u32x4{0, 0, 0, 0};
+    }
+    if (tid < kRows) pre_row = row_of(base + tid);
+  };
+  if (r0 < r1) prefetch(r0);
+
+  for (int base = r0; base < r1; base += kRows) {
+    if (tid < kRows) rowidx[tid] = pre_row;
+#pragma unroll
+    for (int it = 0; it < kChunks; ++it) {
+      const int ch = tid + 256 * it;
+      const int rr = ch / (kD / 8);
+      const int col = ch % (kD / 8);
+      const u32x4 v = pre[it];
+      *reinterpret_cast<u32x4*>(&Ks[rr * kKStride + col * 8]) = v;
+      if (col < kDV / 8) {
+        uint16_t* dst = Vt + (col * 8) * kVStride + vslot(rr);
+        dst[0 * kVStride] = (uint16_t)(v.x & 0xFFFF);
+        dst[1 * kVStride] = (uint16_t)(v.x >> 16);
+        dst[2 * kVStride] = (uint16_t)(v.y & 0xFFFF);
+        dst[3 * kVStride] = (uint16_t)(v.y >> 16);
+        dst[4 * kVStride] = (uint16_t)(v.z & 0xFFFF);
+        dst[5 * kVStride] = (uint16_t)(v.z >> 16);
+        dst[6 * kVStride] = (uint16_t)(v.w & 0xFFFF);
+        dst[7 * kVStride] = (uint16_t)(v.w >> 16);
+      }
+    }
+    __syncthreads();
+    if (base + kRows < r1) prefetch(base + kRows);
+
+    // S^T for rows 0..15 and 16..31 of the tile, heads of this wave
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kD / 32; ++u) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Ks[n * kKStride + 32 * u + 8 * g]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Ks[(16 + n) * kKStride + 32 * u + 8 * g]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qr[u], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qr[u], s1, 0, 0, 0);
+    }
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = rowidx[4 * g + r] >= 0 ? s0[r] * c : -INFINITY;
+      x[4 + r] = rowidx[16 + 4 * g + r] >= 0 ? s1[r] * c : -INFINITY;
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    float p[8];
+    float alpha = 1.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = 0.f;
+    } else {
+      alpha = exp2f(m_run - m_new);   // m_run = -inf gives 0
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = exp2f(x[i] - m_new);
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) psum += p[i];
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                pack_bf16x2(p[6], p[7])};
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    // the running max rarely moves after the first tiles: rescale only then
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int j = 0; j < kDV / 16; ++j) o[j] *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < kDV / 16; ++j) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[(16 * j + n) * kVStride + 8 * g]);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  float l = l_part;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse2 = l > 0.f ? m_run + log2f(l) : -INFINITY;
+  const int64_t bh = (int64_t)b * a.n_heads + head;
+  if (nsplit == 1) {
+    __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV;
+#pragma unroll
+    for (int j = 0; j < kDV / 16; ++j) {
+      u32x2 w2 = {pack_bf16x2(o[j][0] * inv, o[j][1] * inv), pack_bf16x2(o[j][2] * inv, o[j][3] * inv)};
+      *reinterpret_cast<u32x2*>(ob + 16 * j + 4 * g) = w2;
+    }
+    if (g == 0) a.lse[bh] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+  } else {
+    float* po = part_o + (bh * nsplit + split) * kDV;
+#pragma unroll
+    for (int j = 0; j < kDV / 16; ++j)
+      *reinterpret_cast<f32x4*>(po + 16 * j + 4 * g) = o[j] * inv;
+    if (g == 0) part_lse[bh * nsplit + split] = lse2;
+  }
+}
+
+// Merge split partials: out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+__global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit,
+                                                           const float* part_o,
+                                                           const float* part_lse) {
+  const int64_t bh = blockIdx.x;
+  const float* pl = part_lse + bh * nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pl[s]);
+  const int d0 = threadIdx.x * 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ls = pl[s];
+      if (ls == -INFINITY) continue;
+      const float wgt = exp2f(ls - M);
+      wsum += wgt;
+      acc += wgt * *reinterpret_cast<const f32x4*>(part_o + (bh * nsplit + s) * kDV + d0);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV;
+  u32x2 w2 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(ob + d0) = w2;
+  if (threadIdx.x == 0) a.lse[bh] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 generic path: separate K and V caches, one K/V head, any head count.
+// One workgroup per (request, head); rows in blocks of 256, online softmax.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+  extern __shared__ float sm[];
+  float* qs = sm;                    // [dk]
+  float* ps = sm + a.dk;             // [256]
+  int* rows = reinterpret_cast<int*>(ps + 256);   // [256]
+  float* red = reinterpret_cast<float*>(rows + 256);  // [8]
+  const int head = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t bh = (int64_t)b * a.n_heads + head;
+  const float* qg = static_cast<const float*>(a.q) + bh * a.dk;
+  for (int i = tid; i < a.dk; i += 256) qs[i] = qg[i];
+  __syncthreads();
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const float* K = static_cast<const float*>(a.kv);
+  const float* V = static_cast<const float*>(a.v);
+  float m_run = -INFINITY, l_run = 0.f, o = 0.f;
+  for (int base = 0; base < a.k; base += 256) {
+    const int e = base + tid;
+    int row = -1;
+    if (e < a.k) {
+      const int pos = a.idx[(int64_t)b * a.k + e];
+      if (pos >= 0 && pos < L) {
+        const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+        if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+      }
+    }
+    float logit = -INFINITY;
+    if (row >= 0) {
+      const float* kr = K + (int64_t)row * a.dk;
+      float dot = 0.f;
+      for (int i = 0; i < a.dk; ++i) dot = fmaf(qs[i], kr[i], dot);
+      logit = dot * a.sm_scale;
+    }
+    rows[tid] = row;
+    float mx = wave_max(logit);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float m_new = fmaxf(m_run, mx);
+    float p = 0.f, alpha = 1.f;
+    if (m_new != -INFINITY) {
+      alpha = expf(m_run - m_new);
+      p = row >= 0 ? expf(logit - m_new) : 0.f;
+    }
+    ps[tid] = p;
+    float sum = wave_sum(p);
+    __syncthreads();
+    if (lane == 0) red[4 + wave] = sum;
+    __syncthreads();
+    sum = red[4] + red[5] + red[6] + red[7];
+    l_run = l_run * alpha + sum;
+    m_run = m_new;
+    if (tid < a.dv) {
+      o *= alpha;
+      for (int r = 0; r < 256; ++r) {
+        const int rw = rows[r];
+        if (rw >= 0) o = fmaf(ps[r], V[(int64_t)rw * a.dv + tid], o);
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < a.dv) static_cast<float*>(a.out)[bh * a.dv + tid] = l_run > 0.f ? o / l_run : 0.f;
+  if (tid == 0) a.lse[bh] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+}
+
+int pick_nsplit(int num_req, int n_heads, int k) {
+  const int groups = num_req * (n_heads / kHeadsPerWg);
+  const int tiles = (k + kRows - 1) / kRows;
+  // ~2 workgroups per CU, at least 4 tiles per split
+  int ns = (int)ceil_div((int64_t)num_cus() * 2, std::max(groups, 1));
+  ns = std::min(ns, std::max(1, tiles / 4));
+  return std::max(ns, 1);
+}
+
+}  // namespace
+
+size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k) {
+  const int ns = pick_nsplit(num_req, n_heads, k);
+  if (ns == 1) return 0;
+  return align_up((size_t)num_req * n_heads * ns * (dv + 1) * sizeof(float), 256);
+}
+
+hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
+  const int ns = pick_nsplit(a.num_req, a.n_heads, a.k);
+  const int tiles = (a.k + kRows - 1) / kRows;
+  const int rows_per_split = (int)ceil_div(tiles, ns) * kRows;
+  const int nsplit = (int)ceil_div(a.k, rows_per_split);
+  float* part_o = static_cast<float*>(a.ws);
+  float* part_lse = part_o ? part_o + (size_t)a.num_req * a.n_heads * nsplit * kDV : nullptr;
+  const int grid = a.num_req * (a.n_heads / kHeadsPerWg) * nsplit;
+  hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(256), 0, s, a, rows_per_split, nsplit,
+                     part_o, part_lse);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_req * a.n_heads), dim3(kDV / 4), 0, s, a,
+                       nsplit, part_o, part_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
+  const size_t smem = sizeof(float) * (a.dk + 256 + 256 + 8);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.n_heads, a.num_req), dim3(256), smem, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lsi

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/lsi.h declares, and rejects bad arguments before touching the GPU.
+No compute call is made here."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from lightning_indexer_top_04_amd import lsi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsi.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsi_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lsi.LIB_PATH):
+        pytest.skip("liblsi.so not built")
+    return lsi.lib()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(lsi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", lsi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared():
+        assert name in syms, name
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.lsi_version() == 100
+    assert L.lsi_status_string(0) == b"ok"
+    assert b"invalid" in L.lsi_status_string(1)
+    assert b"workspace" in L.lsi_status_string(3)
+
+
+def _batch(B=1, max_pages=4, max_len=256):
+    return lsi.Batch(B, max_pages, max_len, 0, 0x1000, 0x2000)
+
+
+def _cache(dtype=lsi.FP8_E4M3, page=64, pages=8, dim=128, scale=0x3000):
+    return lsi.PagedCache(dtype, page, pages, dim, 0x4000, scale)
+
+
+def _index(L, cache, batch, q=0x5000, H=64, d=128, w=0x6000, scores=0x7000, ld=256):
+    return L.lsi_index_scores(C.byref(cache) if cache is not None else None,
+                              C.byref(batch) if batch is not None else None,
+                              q, H, d, w, scores, ld, None)
+
+
+def test_index_scores_validation(L):
+    ok_b, ok_c = _batch(), _cache()
+    assert _index(L, None, ok_b) == lsi.ERR_INVALID_ARG
+    assert _index(L, ok_c, None) == lsi.ERR_INVALID_ARG
+    assert _index(L, ok_c, ok_b, q=None) == lsi.ERR_INVALID_ARG
+    assert _index(L, ok_c, ok_b, ld=100) == lsi.ERR_INVALID_ARG          # ld < max_seq_len
+    assert _index(L, ok_c, _batch(max_len=257 * 4)) == lsi.ERR_INVALID_ARG  # > max_pages*page
+    assert _index(L, _cache(scale=None), ok_b) == lsi.ERR_INVALID_ARG     # fp8 needs a scale
+    assert _index(L, ok_c, ok_b, H=32) == lsi.ERR_UNSUPPORTED
+    assert _index(L, _cache(dim=64), ok_b, d=64) == lsi.ERR_UNSUPPORTED
+    assert _index(L, _cache(page=48), _batch(max_len=192), ld=192) == lsi.ERR_UNSUPPORTED
+    assert _index(L, _cache(dtype=9), ok_b) == lsi.ERR_INVALID_ARG
+    b = _batch(); b.reserved = 1
+    assert _index(L, ok_c, b) == lsi.ERR_INVALID_ARG
+    assert b"reserved" in L.lsi_last_error()
+
+
+def test_topk_validation_and_workspace(L):
+    b = _batch(B=2, max_len=1000)
+    need = L.lsi_topk_workspace_bytes(2, 1000, 64)
+    assert need >= 2 * 1000 * 4 and need % 256 == 0
+    args = (0x1000, 1000, C.byref(b))
+    assert L.lsi_topk(*args, 0, 0x2000, 0x3000, 0x100000, need, None) == lsi.ERR_INVALID_ARG
+    assert L.lsi_topk(*args, 64, None, 0x3000, 0x100000, need, None) == lsi.ERR_INVALID_ARG
+    assert L.lsi_topk(*args, 64, 0x2000, 0x3000, None, need, None) == lsi.ERR_WORKSPACE
+    assert L.lsi_topk(*args, 64, 0x2000, 0x3000, 0x100010, need, None) == lsi.ERR_WORKSPACE
+    assert L.lsi_topk(*args, 64, 0x2000, 0x3000, 0x100000, need - 4, None) == lsi.ERR_WORKSPACE
+    assert L.lsi_topk(0x1000, 999, C.byref(b), 64, 0x2000, 0x3000, 0x100000, need,
+                      None) == lsi.ERR_INVALID_ARG
+
+
+def test_attention_validation(L):
+    b = _batch()
+    kv = lsi.PagedCache(lsi.BF16, 64, 8, 576, 0x4000, None)
+    def call(kvc, v=None, H=128, dk=576, dv=512, sm=0.04, q=0x5000):
+        return L.lsi_sparse_mla_decode(C.byref(kvc), None if v is None else C.byref(v),
+                                       C.byref(b), q, H, dk, dv, 0x6000, 2048, sm,
+                                       0x7000, 0x8000, 0x100000, 1 << 30, None)
+    assert call(kv, H=96) == lsi.ERR_UNSUPPORTED
+    assert call(kv, dv=256) == lsi.ERR_UNSUPPORTED
+    assert call(kv, sm=0.0) == lsi.ERR_INVALID_ARG
+    assert call(kv, sm=float("nan")) == lsi.ERR_INVALID_ARG
+    assert call(kv, q=None) == lsi.ERR_INVALID_ARG
+    assert call(kv, v=kv) == lsi.ERR_INVALID_ARG          # latent path reads V from kv
+    kvs = lsi.PagedCache(lsi.BF16, 64, 8, 576, 0x4000, 0x9000)
+    assert call(kvs) == lsi.ERR_INVALID_ARG               # bf16 cache takes no scale
+    kf = lsi.PagedCache(lsi.F32, 64, 8, 64, 0x4000, None)
+    assert call(kf, H=8, dk=64, dv=64) == lsi.ERR_INVALID_ARG   # f32 needs a value cache
+
+
+def test_prefill_and_two_stage_validation(L):
+    assert L.lsi_prefill_index_topk(None, None, 10, 0x1000, 0x2000, 4, 0x3000, 64, 128,
+                                    0x4000, 16, 32, 0x5000, 0x6000, None, 0x100000, 1 << 30,
+                                    None, None) == lsi.ERR_INVALID_ARG
+    assert L.lsi_prefill_index_topk(None, None, 0, 0x1000, 0x2000, 4, 0x3000, 64, 128,
+                                    0x4000, 16, 33, 0x5000, 0x6000, None, 0x100000, 1 << 30,
+                                    None, None) == lsi.ERR_INVALID_ARG
+    assert L.lsi_prefill_index_topk(None, None, 0, 0x1000, 0x2000, 4, 0x3000, 32, 128,
+                                    0x4000, 16, 32, 0x5000, 0x6000, None, 0x100000, 1 << 30,
+                                    None, None) == lsi.ERR_UNSUPPORTED
+    b = _batch()
+    k4 = lsi.PagedCache(lsi.INT4, 64, 8, 128, 0x4000, 0x3000)
+    k8 = _cache()
+    # k > n_cand
+    assert L.lsi_two_stage_topk(C.byref(k4), C.byref(k8), C.byref(b), 0x5000, 64, 128,
+                                0x6000, 100, 200, 0x7000, 0x8000, None, 0x100000, 1 << 30,
+                                None) == lsi.ERR_INVALID_ARG
+    # swapped caches
+    assert L.lsi_two_stage_topk(C.byref(k8), C.byref(k4), C.byref(b), 0x5000, 64, 128,
+                                0x6000, 200, 100, 0x7000, 0x8000, None, 0x100000, 1 << 30,
+                                None) == lsi.ERR_INVALID_ARG
