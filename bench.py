@@ -1,0 +1,209 @@
+"""Benchmark of the DSA-style decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets R] [--no-cpu]
+
+Workload: one request with 131072 cached tokens (64 indexer heads x 128,
+fp8 E4M3FN keys with per-token scales, bf16 queries; k = 2048; sparse MLA with
+128 heads over 576-wide bf16 latent rows).  A step is one lsi_decode_step call
+(indexer scan -> top-k -> sparse MLA).  To keep every step's reads cold, R
+independent requests live in one page pool (R*2048 pages, one global random
+page permutation) and step i runs request i % R; with R = 32 the rotation
+touches ~5.4 GB, far beyond the 256 MB last-level cache.
+
+Printed (one JSON line): tokens/s = 131072 * steps / time (whole step timed,
+inputs resident in HBM), decode steps/s, per-phase averages from HIP events on
+the launch stream, the scan's roofline (algorithmic 132 B per token against
+8 TB/s), a sustained scan of 32 x 128K tokens in one launch, and the CPU
+oracle's throughput on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer-scanned tokens/s and decode steps/s (index+top-k+sparse attn) @128K ctx"
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_TOKEN = 132          # 128 fp8 key bytes + 4-byte scale
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sets", type=int, default=32)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def event_loop(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n      # ms per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from lightning_indexer_top_04_amd import lsi, synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    R = args.sets
+    L = 131072
+    wl = synth.scaled(synth.DSA_128K, seq_lens=tuple([L] * R), num_req=R)
+    t0 = time.time()
+    di = synth.make_decode_inputs(wl, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs drawn in {time.time() - t0:.1f}s ({R} sets)", file=sys.stderr, flush=True)
+
+    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    kv = lsi.Cache(di.kv, None, "bf16", 576)
+    reqs = [lsi.Requests(di.seq_lens[r:r + 1], di.page_table[r:r + 1], L) for r in range(R)]
+    k, H, dv = 2048, 128, 512
+    idx = torch.empty(1, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(1, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(lsi.decode_step_workspace_bytes(1, L, k, H, dv), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = i % R
+        lsi.decode_step(ik, kv, None, reqs[r], di.q_idx[r:r + 1], di.w[r:r + 1],
+                        di.q_attn[r:r + 1], k, wl.sm_scale, dv, out=out, lse=lse, idx=idx,
+                        count=cnt, ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    tokens_s = L * args.steps / dt
+    print(f"# decode step {ms_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # ---- per-phase timing through the separate entry points -------------
+    scores = torch.empty(1, L, dtype=torch.float32, device=dev)
+    n_ph = max(args.steps, 50)
+    t_scan = event_loop(lambda i: lsi.index_scores(ik, reqs[i % R], di.q_idx[i % R:i % R + 1],
+                                                   di.w[i % R:i % R + 1], scores=scores,
+                                                   stream=stream), n_ph, stream)
+    t_topk = event_loop(lambda i: lsi.topk(scores, reqs[0], k, stream=stream), n_ph, stream)
+    idx_fixed = lsi.topk(scores, reqs[0], k, stream=stream)[0]
+    t_mla = event_loop(lambda i: lsi.sparse_mla_decode(kv, None, reqs[0], di.q_attn[0:1],
+                                                       idx_fixed, wl.sm_scale, dv,
+                                                       stream=stream), n_ph, stream)
+    scan_gbs = L * BYTES_PER_TOKEN / (t_scan * 1e-3) / 1e9
+
+    # ---- sustained scan: all R requests in one launch ---------------------
+    req_all = lsi.Requests(di.seq_lens, di.page_table, L)
+    scores_all = torch.empty(R, L, dtype=torch.float32, device=dev)
+    n_sus = 20
+    for _ in range(3):
+        lsi.index_scores(ik, req_all, di.q_idx, di.w, scores=scores_all, stream=stream)
+    t_sus = event_loop(lambda i: lsi.index_scores(ik, req_all, di.q_idx, di.w,
+                                                  scores=scores_all, stream=stream),
+                       n_sus, stream)
+    sus_gbs = R * L * BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; fp8 keys N(0,1) quantised per token, 2048 planted tokens)",
+        "config": {"workload": "dsa-decode-L131072", "num_req": 1, "seq_len": L, "k": k,
+                   "indexer_heads": 64, "indexer_dim": 128, "mla_heads": H, "dk": 576,
+                   "dv": dv, "page_size": 64, "rotating_sets": R},
+        "decode_steps_per_s": 1e3 / ms_step,
+        "phases_us": {"scan": t_scan * 1e3, "topk": t_topk * 1e3, "mla": t_mla * 1e3},
+        "roofline": {"kernel": "scan_fp8_kernel", "bound": "hbm", "achieved": scan_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "note": "131072 tokens x 132 B per launch / HIP-event launch time"},
+        "scan_sustained": {"tokens": R * L, "us": t_sus * 1e3,
+                           "tokens_per_s": R * L / (t_sus * 1e-3), "GB_s": sus_gbs,
+                           "frac": sus_gbs / HBM_PEAK_GBS},
+    }
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(di, wl, L, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+def cpu_baseline(di, wl, L, seconds):
+    """The oracle's decode step for one 128K request, repeated for ~`seconds`."""
+    import numpy as np
+
+    import oracle as O
+    from lightning_indexer_top_04_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    pt = di.page_table[0].cpu().numpy()
+    n_pages = L // 64
+    pages = di.page_table[0, :n_pages].long()
+    codes = synth.u8_bits(di.ikeys[pages])              # this request's pages, in order
+    scale = di.iscale[pages].cpu().numpy()
+    kvp = di.kv[pages].contiguous()
+    kv_bits = synth.bf16_bits(kvp)
+    q_idx = synth.bf16_bits(di.q_idx[0])
+    w = di.w[0].cpu().double().numpy()
+    q_attn = synth.bf16_bits(di.q_attn[0])
+    local_pt = np.arange(n_pages)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        K = O.decode_e4m3fn(O.request_rows(codes, local_pt, L, 64))
+        s = O.request_rows(scale, local_pt, L, 64)
+        I = O.index_scores(O.decode_bf16(q_idx), w, K, s)
+        sel, _ = O.topk(I, 2048)
+        rows = O.request_rows(kv_bits, local_pt, L, 64)[np.sort(sel)]
+        O.mla_decode(O.decode_bf16(q_attn), O.decode_bf16(rows), 512, wl.sm_scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 50:
+            break
+    del pt
+    return {"value": L * n / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "steps_per_s": n / el,
+            "sample": f"{n} oracle decode steps of one 131072-token request "
+                      f"(numpy float64, {el:.1f}s)"}
+
+
+if __name__ == "__main__":
+    main()
