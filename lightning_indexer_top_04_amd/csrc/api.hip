@@ -302,7 +302,7 @@ int32_t lsi_topk(const float* scores, int64_t ld, const lsi_batch* batch, int32_
   t.idx = idx;
   t.count = count;
   t.ws = workspace;
-  launch_topk(t, false, stream);
+  launch_topk(t, 0, stream);
   return check_launch("lsi_topk");
 }
 
@@ -356,9 +356,15 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
   void* attn_wsp = ws;
 
+  // clear the top-k counters, then let the scan build the first-digit
+  // histogram of its own scores (MFMA paths)
+  launch_zero(static_cast<uint32_t*>(topk_ws), topk_zero_words(batch->num_req), stream);
   ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
-  sa.zero_ptr = static_cast<uint32_t*>(topk_ws);     // the scan clears the top-k counters
-  sa.zero_words = topk_zero_words(batch->num_req);
+  const bool fused = ikeys->dtype != LSI_F32;
+  if (fused) {
+    sa.topk_ws = topk_ws;
+    sa.topk_k = k;
+  }
   run_scan(ikeys->dtype, sa, stream);
 
   TopkArgs t;
@@ -371,7 +377,7 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.idx = idx;
   t.count = count;
   t.ws = topk_ws;
-  launch_topk(t, true, stream);
+  launch_topk(t, fused ? 2 : 1, stream);
 
   const AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
   run_attn(kv->dtype, a, stream);
@@ -423,9 +429,10 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   void* t2 = ws;
 
   // stage 1: compact keys over every token, keep n_cand
+  launch_zero(static_cast<uint32_t*>(t1), topk_zero_words(B), stream);
   ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
-  a4.zero_ptr = static_cast<uint32_t*>(t1);
-  a4.zero_words = topk_zero_words(B);
+  a4.topk_ws = t1;
+  a4.topk_k = n_cand;
   launch_scan_int4(a4, stream);
   TopkArgs ta;
   ta.scores = s4;
@@ -437,14 +444,12 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ta.idx = cl;
   ta.count = cc;
   ta.ws = t1;
-  launch_topk(ta, true, stream);
+  launch_topk(ta, 2, stream);
 
   // stage 2: exact fp8 scores of the candidates only, keep k
   ScanArgs a8 = scan_args(ikeys8, batch, q, n_heads, dim, w, s8, n_cand);
   a8.positions = cl;
   a8.n_pos = n_cand;
-  a8.zero_ptr = static_cast<uint32_t*>(t2);
-  a8.zero_words = topk_zero_words(B);
   launch_scan_fp8(a8, stream);
   TopkArgs tb;
   tb.scores = s8;
@@ -458,7 +463,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   tb.idx = idx;
   tb.count = count;
   tb.ws = t2;
-  launch_topk(tb, true, stream);
+  launch_topk(tb, 0, stream);
   if (cand) {
     const hipError_t e = hipMemcpyAsync(cand, cl, (size_t)B * n_cand * 4, hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("lsi_two_stage_topk: ") + hipGetErrorString(e));
@@ -580,7 +585,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   t.idx = idx;
   t.count = count;
   t.ws = tws;
-  launch_topk(t, false, s_compute);
+  launch_topk(t, 0, s_compute);
 #undef LSI_HIP
   return check_launch("lsi_prefill_index_topk");
 }

@@ -24,6 +24,7 @@ constexpr int kRows = 32;        // rows per tile
 constexpr int kKStride = 584;    // bf16 elements per LDS row of the K tile
 constexpr int kVStride = 36;     // bf16 slots per LDS row of the V^T tile
 constexpr int kHeadsPerWg = 64;
+constexpr int kMaxSplitRows = 512;  // selection rows one workgroup handles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_p
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[kDV * kVStride];
   __shared__ int rowidx[kRows];
+  __shared__ int rows_all[kMaxSplitRows];
 
   const int n_hg = a.n_heads / kHeadsPerWg;
   const int bid = blockIdx.x;
@@ -76,19 +78,24 @@ __global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_p
   const __bf16* kvb = static_cast<const __bf16*>(a.kv);
   const int32_t* idxb = a.idx + (int64_t)b * a.k;
 
+  // Physical rows of the whole slice, resolved once (index -> page table).
+  for (int e = tid; e < r1 - r0; e += 256) {
+    const int pos = idxb[r0 + e];
+    int row = -1;
+    if (pos >= 0 && pos < L) {
+      const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+      if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+    }
+    rows_all[e] = row;
+  }
+  __syncthreads();
+
   // Gather of one 32-row tile into registers: thread tid owns 16-byte chunks
   // tid + 256*it of the tile (row = chunk / 72, column chunk = chunk % 72).
   constexpr int kChunks = (kRows * (kD / 8)) / 256;   // 9
   u32x4 pre[kChunks];
   int pre_row = -1;                                   // tile row tid (tid < 32)
-  auto row_of = [&](int e) -> int {
-    if (e >= r1) return -1;
-    const int pos = idxb[e];
-    if (pos < 0 || pos >= L) return -1;
-    const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-    if ((unsigned)page >= (unsigned)a.num_pages) return -1;
-    return page * a.page_size + pos % a.page_size;
-  };
+  auto row_of = [&](int e) -> int { return e < r1 ? rows_all[e - r0] : -1; };
   auto prefetch = [&](int base) {
 #pragma unroll
     for (int it = 0; it < kChunks; ++it) {
@@ -305,6 +312,7 @@ int pick_nsplit(int num_req, int n_heads, int k) {
   // ~2 workgroups per CU, at least 4 tiles per split
   int ns = (int)ceil_div((int64_t)num_cus() * 2, std::max(groups, 1));
   ns = std::min(ns, std::max(1, tiles / 4));
+  ns = std::max(ns, (int)ceil_div(tiles, kMaxSplitRows / kRows));
   return std::max(ns, 1);
 }
 

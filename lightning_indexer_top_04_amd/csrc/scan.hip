@@ -6,139 +6,47 @@
 // the matrix cores as two v_mfma_f32_32x32x16 per K-step, heads on the
 // accumulator rows, tokens on the lanes.  Each lane owns one token of the
 // 32-token tile and half of its key row (64 contiguous bytes for fp8, 32 for
-// int4), so a tile is fetched with 16-byte loads straight from the page and no
-// LDS staging.  The dot product does not depend on the order of the K index,
+// int4), so a tile is fetched with 16-byte loads straight from the page, with
+// no LDS staging.  The dot product does not depend on the order of the K index,
 // so the query rows are loaded in exactly the order the key bytes arrive.
 // ReLU, the head weights and the head sum stay in registers: a lane sums the
 // 32 heads it holds, one cross-half swap adds the other 32, and lanes 0..31
 // store 32 consecutive scores.
+//
+// Latency hiding: the page ids of a workgroup's slice are staged in LDS before
+// the tile loop, so a tile's key loads never wait on a page-table load, and
+// every wave keeps two tiles of keys in flight while it computes a third.
+//
+// Optionally the scan also builds the top-k's first-digit histogram of its
+// scores (LDS atomics, one flush of the non-empty bins per workgroup), and the
+// last workgroup of each request picks the bin that holds the k-th score, so
+// the selection needs a single further pass.
 #include "lsi_internal.hpp"
+#include "topk_common.hpp"
 
 namespace lsi {
 namespace {
 
-constexpr int kTile = 32;     // tokens per MFMA tile
-constexpr int kWaves = 4;     // waves per workgroup
+constexpr int kTile = 32;        // tokens per MFMA tile
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kThreads = kWaves * 64;
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
+constexpr int kMaxChunk = 8192;  // tokens per workgroup (contiguous mode)
+constexpr int kMaxChunkPages = kMaxChunk / 32;
+constexpr int KIND_FP8 = 0;
+constexpr int KIND_INT4 = 1;
 
 struct TileFetch {
   u32x4 raw[4];   // fp8: 64 bytes of the key row; int4: raw[0..1] = 32 bytes
   float scale;
   int item;
-  bool valid;     // item inside the request
-  bool ok;        // page id in range
+  bool valid;     // the slot exists (write a score)
+  bool ok;        // the token exists and its page is in range
 };
 
-__device__ __forceinline__ void zero_words(uint32_t* p, int64_t n) {
-  if (!p) return;
-  const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
-  const int64_t tid =
-      ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-  for (int64_t i = tid; i < n; i += nthreads) p[i] = 0u;
-}
-
-// Locate item `item` of request b and fetch its key half (ROW_BYTES/2 bytes
-// starting at half h) and per-token scale.
-template <bool GATHER, int ROW_BYTES>
-__device__ __forceinline__ TileFetch fetch_tile(const ScanArgs& a, int b, int L,
-                                                int item, int end, int h,
-                                                int page_shift) {
-  TileFetch f;
-  f.item = item;
-  f.valid = item < end;
-  int pos = item;
-  if (GATHER) {
-    pos = f.valid ? a.positions[(int64_t)b * a.n_pos + item] : -1;
-    f.valid = f.valid && pos >= 0 && pos < L;
-    // an invalid slot still gets a score (-inf) when item < end
-  }
-  int page = -1;
-  if (f.valid) page = a.page_table[(int64_t)b * a.max_pages + (pos >> page_shift)];
-  f.ok = f.valid && (unsigned)page < (unsigned)a.num_pages;
-  const int64_t row = (int64_t)page * a.page_size + (pos & (a.page_size - 1));
-  if (f.ok) {
-    const u32x4* kp = reinterpret_cast<const u32x4*>(
-        static_cast<const uint8_t*>(a.keys) + row * ROW_BYTES + h * (ROW_BYTES / 2));
-#pragma unroll
-    for (int i = 0; i < ROW_BYTES / 32; ++i) f.raw[i] = __builtin_nontemporal_load(kp + i);
-    f.scale = a.kscale[row];
-  } else {
-#pragma unroll
-    for (int i = 0; i < ROW_BYTES / 32; ++i) f.raw[i] = u32x4{0, 0, 0, 0};
-    f.scale = 0.f;
-  }
-  if (GATHER) f.valid = item < end;  // slot exists: write a score for it
-  return f;
-}
-
 // ---------------------------------------------------------------------------
-// fp8 E4M3FN keys, bf16 queries, bf16 MFMA on exactly converted keys
-// ---------------------------------------------------------------------------
-template <bool GATHER>
-__global__ __launch_bounds__(256, 2) void scan_fp8_kernel(ScanArgs a, int chunk,
-                                                           int page_shift) {
-  zero_words(a.zero_ptr, a.zero_words);
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int m = lane & 31;
-  const int h = lane >> 5;
-  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-  const int n_items = GATHER ? a.n_pos : L;
-  const int begin = blockIdx.x * chunk;
-  const int end = min(begin + chunk, n_items);
-  if (begin >= end) return;
-  const int ntile = (end - begin + kTile - 1) / kTile;
-  if (wave >= ntile) return;
-
-  // Query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7.
-  const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
-  bf16x8 qa[2][8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      qa[mt][t] = *reinterpret_cast<const bf16x8*>(qb + (32 * mt + m) * kDim + 64 * h + 8 * t);
-  // Head weights of the accumulator rows this lane holds:
-  // row of register r in a 32x32 tile = 8*(r/4) + 4*h + r%4.
-  float wv[2][16];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wv[mt][r] = a.w[(int64_t)b * kHeads + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3)];
-
-  TileFetch cur = fetch_tile<GATHER, kDim>(a, b, L, begin + wave * kTile + m, end, h, page_shift);
-  for (int tile = wave; tile < ntile; tile += kWaves) {
-    const int nt = tile + kWaves;
-    TileFetch nxt;
-    if (nt < ntile) nxt = fetch_tile<GATHER, kDim>(a, b, L, begin + nt * kTile + m, end, h, page_shift);
-
-    f32x16 acc0 = {};
-    f32x16 acc1 = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 r4 = cur.raw[t >> 1];
-      const bf16x8 kb = (t & 1) ? fp8x8_to_bf16x8(r4.z, r4.w) : fp8x8_to_bf16x8(r4.x, r4.y);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][t], kb, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][t], kb, acc1, 0, 0, 0);
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part += wv[0][r] * fmaxf(acc0[r], 0.f);
-      part += wv[1][r] * fmaxf(acc1[r], 0.f);
-    }
-    const float total = half_swap_sum(part);
-    if (h == 0 && cur.valid)
-      a.scores[(int64_t)b * a.ld + cur.item] = cur.ok ? total * cur.scale : -INFINITY;
-    if (nt < ntile) cur = nxt;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// int4 keys (compact keys of the two-stage search), fp16 MFMA.
+// int4 keys (compact keys of the two-stage search) run on fp16 MFMA.
 // A nibble n in [-7,7] becomes the fp16 value n exactly: (n ^ 8) | 0x6400 is
 // the fp16 number 1032 + n, and one packed fp16 add of -1032 leaves n.
 // The bf16 query is scaled per head by a power of two 2^E_j that puts its
@@ -157,92 +65,173 @@ __device__ __forceinline__ f16x8 int4x8_to_f16x8(uint32_t d) {
   return r;
 }
 
-template <bool GATHER>
-__global__ __launch_bounds__(256, 2) void scan_int4_kernel(ScanArgs a, int chunk,
-                                                            int page_shift) {
-  __shared__ float inv_scale[kWaves][kHeads];
-  zero_words(a.zero_ptr, a.zero_words);
+template <int KIND>
+struct QOp {
+  using T = typename std::conditional<KIND == KIND_FP8, bf16x8, f16x8>::type;
+};
+
+template <int KIND, bool GATHER, bool HIST>
+__global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk, int page_shift) {
+  constexpr int ROW = KIND == KIND_FP8 ? kDim : kDim / 2;   // key bytes per token
+  using QT = typename QOp<KIND>::T;
+  __shared__ int pages[GATHER ? 1 : kMaxChunkPages];
+  __shared__ uint32_t hist[HIST ? topk::kBins : 1];
+  __shared__ uint32_t tmp[32];
+  __shared__ int flag;
+  __shared__ float inv_scale[KIND == KIND_INT4 ? kWaves * kHeads : 1];
+
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int m = lane & 31;
   const int h = lane >> 5;
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int n_items = GATHER ? a.n_pos : L;
+  const int nprod = max(1, (n_items + chunk - 1) / chunk);
+  if ((int)blockIdx.x >= nprod) return;
   const int begin = blockIdx.x * chunk;
   const int end = min(begin + chunk, n_items);
-  if (begin >= end) return;
-  const int ntile = (end - begin + kTile - 1) / kTile;
+  const int ntile = max(0, (end - begin + kTile - 1) / kTile);
 
+  if (!GATHER) {
+    const int npg = (end - begin + a.page_size - 1) >> page_shift;
+    const int pg0 = begin >> page_shift;
+    for (int i = tid; i < npg; i += kThreads)
+      pages[i] = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
+  }
+  if (HIST)
+    for (int i = tid; i < topk::kBins; i += kThreads) hist[i] = 0u;
+
+  // query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7
   const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
-  f16x8 qa[2][8];
+  QT qa[2][8];
+  if constexpr (KIND == KIND_FP8) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int head = 32 * mt + m;
-    bf16x8 raw[8];
-    float amax = 0.f;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      raw[t] = *reinterpret_cast<const bf16x8*>(qb + head * kDim + 64 * h + 8 * t);
+      for (int t = 0; t < 8; ++t)
+        qa[mt][t] = *reinterpret_cast<const bf16x8*>(qb + (32 * mt + m) * kDim + 64 * h + 8 * t);
+  } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[t][e]));
-    }
-    {
-      uint32_t u = __float_as_uint(amax);
-      auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    int e2 = 0;
-    if (amax > 0.f) (void)frexpf(amax, &e2);
-    const int E = (amax > 0.f) ? 15 - e2 : 0;
-    const float sc = ldexpf(1.0f, E);
-    if (h == 0) inv_scale[wave][head] = ldexpf(1.0f, -E);
+    for (int mt = 0; mt < 2; ++mt) {
+      const int head = 32 * mt + m;
+      bf16x8 raw[8];
+      float amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-      f16x8 v;
+      for (int t = 0; t < 8; ++t) {
+        raw[t] = *reinterpret_cast<const bf16x8*>(qb + head * kDim + 64 * h + 8 * t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)raw[t][order[e]] * sc);
-      qa[mt][t] = v;
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[t][e]));
+      }
+      {
+        const uint32_t u = __float_as_uint(amax);
+        auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      int e2 = 0;
+      if (amax > 0.f) (void)frexpf(amax, &e2);
+      const int E = (amax > 0.f) ? 15 - e2 : 0;
+      const float sc = ldexpf(1.0f, E);
+      if (h == 0) inv_scale[wave * kHeads + head] = ldexpf(1.0f, -E);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        constexpr int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)raw[t][order[e]] * sc);
+        qa[mt][t] = v;
+      }
     }
   }
   __syncthreads();
-  if (wave >= ntile) return;
+
+  // head weights of the accumulator rows this lane holds:
+  // row of register r in a 32x32 tile = 8*(r/4) + 4*h + r%4
   float wv[2][16];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int head = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-      wv[mt][r] = a.w[(int64_t)b * kHeads + head] * inv_scale[wave][head];
+      float wj = a.w[(int64_t)b * kHeads + head];
+      if constexpr (KIND == KIND_INT4) wj *= inv_scale[wave * kHeads + head];
+      wv[mt][r] = wj;
     }
 
-  TileFetch cur = fetch_tile<GATHER, kDim / 2>(a, b, L, begin + wave * kTile + m, end, h, page_shift);
-  for (int tile = wave; tile < ntile; tile += kWaves) {
-    const int nt = tile + kWaves;
-    TileFetch nxt;
-    if (nt < ntile) nxt = fetch_tile<GATHER, kDim / 2>(a, b, L, begin + nt * kTile + m, end, h, page_shift);
-    f32x16 acc0 = {};
-    f32x16 acc1 = {};
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 r4 = cur.raw[t >> 2];
-      const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
-      const f16x8 kb = int4x8_to_f16x8(d);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][t], kb, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][t], kb, acc1, 0, 0, 0);
+  auto fetch = [&](int tile) {
+    TileFetch f;
+    const int item = begin + tile * kTile + m;
+    f.item = item;
+    f.valid = item < end;
+    int pos = item;
+    int page = -1;
+    if (GATHER) {
+      pos = f.valid ? a.positions[(int64_t)b * a.n_pos + item] : -1;
+      const bool in = f.valid && pos >= 0 && pos < L;
+      if (in) page = a.page_table[(int64_t)b * a.max_pages + (pos >> page_shift)];
+    } else if (f.valid) {
+      page = pages[(tile * kTile + m) >> page_shift];
     }
-    float part = 0.f;
+    f.ok = page >= 0 && page < a.num_pages;
+    const int64_t row = (int64_t)page * a.page_size + (pos & (a.page_size - 1));
+    if (f.ok) {
+      const u32x4* kp = reinterpret_cast<const u32x4*>(
+          static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part += wv[0][r] * fmaxf(acc0[r], 0.f);
-      part += wv[1][r] * fmaxf(acc1[r], 0.f);
+      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
+      f.scale = a.kscale[row];
+    } else {
+#pragma unroll
+      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = u32x4{0, 0, 0, 0};
+      f.scale = 0.f;
     }
-    const float total = half_swap_sum(part);
-    if (h == 0 && cur.valid)
-      a.scores[(int64_t)b * a.ld + cur.item] = cur.ok ? total * cur.scale : -INFINITY;
-    if (nt < ntile) cur = nxt;
+    return f;
+  };
+
+  if (wave < ntile) {
+    TileFetch f0 = fetch(wave);
+    TileFetch f1;
+    if (wave + kWaves < ntile) f1 = fetch(wave + kWaves);
+    for (int tile = wave; tile < ntile; tile += kWaves) {
+      TileFetch f2;
+      if (tile + 2 * kWaves < ntile) f2 = fetch(tile + 2 * kWaves);
+      f32x16 acc0 = {};
+      f32x16 acc1 = {};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if constexpr (KIND == KIND_FP8) {
+          const u32x4 r4 = f0.raw[t >> 1];
+          const bf16x8 kb = (t & 1) ? fp8x8_to_bf16x8(r4.z, r4.w) : fp8x8_to_bf16x8(r4.x, r4.y);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][t], kb, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][t], kb, acc1, 0, 0, 0);
+        } else {
+          const u32x4 r4 = f0.raw[t >> 2];
+          const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
+          const f16x8 kb = int4x8_to_f16x8(d);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][t], kb, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][t], kb, acc1, 0, 0, 0);
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        part += wv[0][r] * fmaxf(acc0[r], 0.f);
+        part += wv[1][r] * fmaxf(acc1[r], 0.f);
+      }
+      const float total = half_swap_sum(part);
+      if (h == 0 && f0.valid) {
+        const float sc = f0.ok ? total * f0.scale : -INFINITY;
+        a.scores[(int64_t)b * a.ld + f0.item] = sc;
+        if (HIST) atomicAdd(&hist[float_key(sc) >> 20], 1u);
+      }
+      f0 = f1;
+      f1 = f2;
+    }
   }
+  if (HIST)
+    topk::hist_flush_and_decide<kThreads>(topk::carve(a.topk_ws, a.num_req), b, L, a.topk_k,
+                                          nprod, hist, tmp, &flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,7 +239,6 @@ __global__ __launch_bounds__(256, 2) void scan_int4_kernel(ScanArgs a, int chunk
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
   extern __shared__ float smem[];
-  zero_words(a.zero_ptr, a.zero_words);
   const int H = a.n_heads;
   const int d = a.dim;
   float* qs = smem;           // [H][d]
@@ -279,47 +267,39 @@ __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
   a.scores[(int64_t)b * a.ld + s] = total;
 }
 
-int pick_chunk(int64_t num_req, int64_t max_items) {
-  // aim at ~4 workgroups per CU over the whole batch; at least 8 tiles each
+int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather) {
+  // aim at ~4 workgroups per CU over the whole batch
   const int64_t target = (int64_t)num_cus() * 4;
+  const int64_t unit = std::max<int64_t>(kTile * kWaves, gather ? 1 : page_size);
   int64_t chunk = ceil_div(num_req * max_items, target);
-  chunk = ceil_div(chunk, kTile * kWaves) * (kTile * kWaves);
-  if (chunk < 256) chunk = 256;
-  if (chunk > (1 << 22)) chunk = 1 << 22;
-  return (int)chunk;
+  chunk = ceil_div(std::max<int64_t>(chunk, 256), unit) * unit;
+  if (!gather) chunk = std::min<int64_t>(chunk, std::max<int64_t>(kMaxChunk, unit));
+  return (int)std::min<int64_t>(chunk, 1 << 24);
+}
+
+template <int KIND>
+hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
+  const bool gather = a.positions != nullptr;
+  const int max_items = gather ? a.n_pos : a.max_seq_len;
+  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather);
+  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
+  const int ps = ilog2(a.page_size);
+  if (gather)
+    hipLaunchKernelGGL((scan_kernel<KIND, true, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+  else if (a.topk_ws)
+    hipLaunchKernelGGL((scan_kernel<KIND, false, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+  else
+    hipLaunchKernelGGL((scan_kernel<KIND, false, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s) {
-  const int max_items = a.positions ? a.n_pos : a.max_seq_len;
-  const int chunk = pick_chunk(a.num_req, max_items);
-  dim3 grid((unsigned)ceil_div(max_items, chunk), (unsigned)a.num_req);
-  if (grid.x == 0) grid.x = 1;
-  const int ps = ilog2(a.page_size);
-  if (a.positions)
-    hipLaunchKernelGGL(scan_fp8_kernel<true>, grid, dim3(256), 0, s, a, chunk, ps);
-  else
-    hipLaunchKernelGGL(scan_fp8_kernel<false>, grid, dim3(256), 0, s, a, chunk, ps);
-  return hipGetLastError();
-}
-
-hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s) {
-  const int max_items = a.positions ? a.n_pos : a.max_seq_len;
-  const int chunk = pick_chunk(a.num_req, max_items);
-  dim3 grid((unsigned)ceil_div(max_items, chunk), (unsigned)a.num_req);
-  if (grid.x == 0) grid.x = 1;
-  const int ps = ilog2(a.page_size);
-  if (a.positions)
-    hipLaunchKernelGGL(scan_int4_kernel<true>, grid, dim3(256), 0, s, a, chunk, ps);
-  else
-    hipLaunchKernelGGL(scan_int4_kernel<false>, grid, dim3(256), 0, s, a, chunk, ps);
-  return hipGetLastError();
-}
+hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s) { return launch_mfma_scan<KIND_FP8>(a, s); }
+hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s) { return launch_mfma_scan<KIND_INT4>(a, s); }
 
 hipError_t launch_scan_f32(const ScanArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(a.max_seq_len, 256), (unsigned)a.num_req);
-  if (grid.x == 0) grid.x = 1;
+  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_seq_len, 256)), (unsigned)a.num_req);
   const size_t smem = sizeof(float) * ((size_t)a.n_heads * a.dim + a.n_heads);
   hipLaunchKernelGGL(scan_f32_kernel, grid, dim3(256), smem, s, a);
   return hipGetLastError();

@@ -1,0 +1,173 @@
+"""GPU vs oracle at the full workload sizes:
+
+* dsa-decode-L131072: one request of 131072 tokens, planted and un-planted;
+  every score, the whole selection and the attention output are checked.
+* ragged-decode-B64: 64 requests of 10K..195K tokens in one launch; every
+  request's selection is checked for validity, sampled requests fully.
+* two-stage-L524288: int4 stage (8192 candidates) then exact fp8 rerank
+  (2048); both stages against the oracle, recall against the exact fp8 scan
+  reported.
+* prefill-T4096-H65536: 4096 queries, 65536 history tokens streamed from pinned
+  host memory through two 8192-token buffers, causal; sampled query rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from acceptance import OracleView, check_attention, check_scores, check_topk
+from lightning_indexer_top_04_amd import lsi, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _objs(di, max_len):
+    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    kv = lsi.Cache(di.kv, None, "bf16", 576)
+    req = lsi.Requests(di.seq_lens, di.page_table, max_len)
+    return ik, kv, req
+
+
+@pytest.mark.parametrize("planted", [True, False])
+def test_dsa_128k_decode_step(planted):
+    wl = synth.DSA_128K
+    di = synth.make_decode_inputs(wl, device=DEV, planted=planted)
+    ov = OracleView(di)
+    ik, kv, req = _objs(di, 131072)
+    scores = lsi.index_scores(ik, req, di.q_idx, di.w)
+    idx, cnt, out, lse = lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, 2048,
+                                         wl.sm_scale, 512)
+    torch.cuda.synchronize()
+    I, A = ov.scores(0)
+    st = check_scores(scores[0].cpu().numpy(), I, A, "scan 128K")
+    st.update(check_topk(idx[0].cpu().numpy(), cnt[0].item(), I, 2048, "topk 128K"))
+    sel = idx[0, :cnt[0]].cpu().numpy()
+    ro, rl = ov.attention(0, sel)
+    st.update(check_attention(out[0].float().cpu().numpy(), ro, "mla 128K"))
+    assert np.allclose(lse[0].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
+    if planted:
+        assert O.recall(sel, di.planted[0]) == 1.0
+    print("128K", "planted" if planted else "unplanted", st)
+
+
+def test_ragged_batch_64_decode_step():
+    wl = synth.BATCH_RAGGED
+    di = synth.make_decode_inputs(wl, device=DEV)
+    seq = di.seq_lens.cpu().numpy()
+    ik, kv, req = _objs(di, int(seq.max()))
+    idx, cnt, out, lse = lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, 2048,
+                                         wl.sm_scale, 512)
+    torch.cuda.synchronize()
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(len(seq)):
+        n = min(2048, seq[b])
+        assert cnt_h[b] == n
+        s = idx_h[b, :n]
+        assert np.all((s >= 0) & (s < seq[b])) and len(np.unique(s)) == n
+        assert np.all(idx_h[b, n:] == -1)
+        assert np.all(np.isfinite(out[b].float().cpu().numpy()))
+    ov = OracleView(di)
+    sample = sorted({int(np.argmin(seq)), int(np.argmax(seq)), 7, 33, 63})
+    for b in sample:
+        I, _ = ov.scores(b)
+        st = check_topk(idx_h[b], cnt_h[b], I, 2048, f"req {b}")
+        ro, _ = ov.attention(b, idx_h[b, :cnt_h[b]])
+        st.update(check_attention(out[b].float().cpu().numpy(), ro, f"req {b}"))
+        assert O.recall(idx_h[b, :cnt_h[b]], di.planted[b]) == 1.0
+        print("ragged req", b, "L", seq[b], st)
+
+
+@pytest.mark.parametrize("planted", [True, False])
+def test_two_stage_512k(planted):
+    wl = synth.TWO_STAGE_512K
+    di = synth.make_decode_inputs(wl, device=DEV, planted=planted, with_int4=True)
+    ov = OracleView(di)
+    ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, 524288)
+    idx, cnt, cand = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048, want_cand=True)
+    torch.cuda.synchronize()
+    cand_h = cand[0].cpu().numpy()
+    K4, s4 = ov.keys4(0)
+    I4 = O.index_scores(ov.q_idx[0], ov.w[0], K4, s4)
+    st1 = check_topk(cand_h, 8192, I4, 8192, "stage 1")
+    # stage 2 given the GPU's candidates: exact fp8 scores of exactly those
+    K8, s8 = ov.keys(0)
+    I8 = O.index_scores(ov.q_idx[0], ov.w[0], K8, s8)
+    fin = idx[0, :cnt[0]].cpu().numpy()
+    assert cnt[0].item() == 2048 and set(fin.tolist()) <= set(cand_h.tolist())
+    c_sorted = np.sort(cand_h)
+    pos_in = np.searchsorted(c_sorted, fin)
+    fake_idx = np.full(2048, -1)
+    fake_idx[:len(fin)] = pos_in
+    st2 = check_topk(fake_idx, len(fin), I8[c_sorted], 2048, "stage 2")
+    exact, _ = O.topk(I8, 2048)
+    rec = O.recall(fin, exact)
+    rec4 = O.recall(O.topk(I4, 2048)[0], exact)
+    print("two-stage", "planted" if planted else "unplanted", st1, st2,
+          f"recall {rec:.4f} (int4-only {rec4:.4f})")
+    assert rec >= rec4 - 1e-9
+    if planted:
+        assert rec == 1.0
+
+
+def test_prefill_chunk_4096_over_65536():
+    wl = synth.PREFILL_CHUNK
+    pi = synth.make_prefill_inputs(wl, device=DEV)
+    H = pi.hist_len
+    hist_k = pi.keys[:H].cpu().pin_memory()
+    hist_s = pi.scale[:H].cpu().pin_memory()
+    chunk_k = pi.keys[H:].contiguous()
+    chunk_s = pi.scale[H:].contiguous()
+    copy_stream = torch.cuda.Stream()
+    idx, cnt, sc = lsi.prefill_index_topk(hist_k, hist_s, chunk_k, chunk_s, pi.q, pi.w, 2048,
+                                          8192, want_scores=True, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy()
+    assert np.all(cnt_h == 2048)
+    keys = O.decode_e4m3fn(synth.u8_bits(pi.keys))
+    scale = pi.scale.cpu().double().numpy()
+    q = O.decode_bf16(synth.bf16_bits(pi.q))
+    w = pi.w.cpu().double().numpy()
+    rows = [0, 1, 2, 31, 32, 1000, 2047, 2048, 4094, 4095]
+    res = O.prefill_index_topk(q, w, keys, scale, H, 2048, rows=rows)
+    for i in rows:
+        sel_ref, tau, s_ref = res[i]
+        vis = H + i + 1
+        mag = O.score_magnitude(q[i], w[i], keys[:vis], scale[:vis])
+        st = check_scores(sc[i, :vis].cpu().numpy(), s_ref, mag, f"prefill row {i}")
+        st.update(check_topk(idx[i].cpu().numpy(), cnt_h[i], s_ref, 2048, f"prefill row {i}"))
+        print("prefill row", i, st)
+    # history streamed from the host equals history read from the device
+    idx2, cnt2 = lsi.prefill_index_topk(pi.keys[:H], pi.scale[:H], chunk_k, chunk_s, pi.q, pi.w,
+                                        2048, 8192)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, cnt2)
+    a = torch.sort(idx, dim=1).values
+    b = torch.sort(idx2, dim=1).values
+    assert torch.equal(a, b)
+
+
+def test_prefill_small_history_and_partial_blocks():
+    """hist_len not a multiple of the block, T not a multiple of 4, k above
+    the visible count for the first queries."""
+    wl = synth.scaled(synth.PREFILL_CHUNK, seq_lens=(1000,), chunk=37, block_tokens=256, seed=9)
+    pi = synth.make_prefill_inputs(wl, device=DEV)
+    H = pi.hist_len
+    k = 1010
+    idx, cnt, sc = lsi.prefill_index_topk(pi.keys[:H].cpu().pin_memory(),
+                                          pi.scale[:H].cpu().pin_memory(), pi.keys[H:],
+                                          pi.scale[H:], pi.q, pi.w, k, 256, want_scores=True)
+    torch.cuda.synchronize()
+    keys = O.decode_e4m3fn(synth.u8_bits(pi.keys))
+    scale = pi.scale.cpu().double().numpy()
+    q = O.decode_bf16(synth.bf16_bits(pi.q))
+    w = pi.w.cpu().double().numpy()
+    res = O.prefill_index_topk(q, w, keys, scale, H, k)
+    for i in range(37):
+        sel_ref, tau, s_ref = res[i]
+        vis = H + i + 1
+        mag = O.score_magnitude(q[i], w[i], keys[:vis], scale[:vis])
+        check_scores(sc[i, :vis].cpu().numpy(), s_ref, mag, f"row {i}")
+        check_topk(idx[i].cpu().numpy(), cnt[i].item(), s_ref, k, f"row {i}")
