@@ -356,15 +356,10 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
   void* attn_wsp = ws;
 
-  // clear the top-k counters, then let the scan build the first-digit
-  // histogram of its own scores (MFMA paths)
-  launch_zero(static_cast<uint32_t*>(topk_ws), topk_zero_words(batch->num_req), stream);
+  // the scan also clears the top-k counters that the selection uses next
   ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
-  const bool fused = ikeys->dtype != LSI_F32;
-  if (fused) {
-    sa.topk_ws = topk_ws;
-    sa.topk_k = k;
-  }
+  sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
+  sa.zero_words = topk_zero_words(batch->num_req);
   run_scan(ikeys->dtype, sa, stream);
 
   TopkArgs t;
@@ -377,7 +372,7 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.idx = idx;
   t.count = count;
   t.ws = topk_ws;
-  launch_topk(t, fused ? 2 : 1, stream);
+  launch_topk(t, 1, stream);
 
   const AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
   run_attn(kv->dtype, a, stream);
@@ -429,10 +424,9 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   void* t2 = ws;
 
   // stage 1: compact keys over every token, keep n_cand
-  launch_zero(static_cast<uint32_t*>(t1), topk_zero_words(B), stream);
   ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
-  a4.topk_ws = t1;
-  a4.topk_k = n_cand;
+  a4.zero_ptr = static_cast<uint32_t*>(t1);
+  a4.zero_words = topk_zero_words(B);
   launch_scan_int4(a4, stream);
   TopkArgs ta;
   ta.scores = s4;
@@ -444,12 +438,14 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ta.idx = cl;
   ta.count = cc;
   ta.ws = t1;
-  launch_topk(ta, 2, stream);
+  launch_topk(ta, 1, stream);
 
   // stage 2: exact fp8 scores of the candidates only, keep k
   ScanArgs a8 = scan_args(ikeys8, batch, q, n_heads, dim, w, s8, n_cand);
   a8.positions = cl;
   a8.n_pos = n_cand;
+  a8.zero_ptr = static_cast<uint32_t*>(t2);
+  a8.zero_words = topk_zero_words(B);
   launch_scan_fp8(a8, stream);
   TopkArgs tb;
   tb.scores = s8;
@@ -463,7 +459,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   tb.idx = idx;
   tb.count = count;
   tb.ws = t2;
-  launch_topk(tb, 0, stream);
+  launch_topk(tb, 1, stream);
   if (cand) {
     const hipError_t e = hipMemcpyAsync(cand, cl, (size_t)B * n_cand * 4, hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("lsi_two_stage_topk: ") + hipGetErrorString(e));

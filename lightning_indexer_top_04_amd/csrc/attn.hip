@@ -90,21 +90,24 @@ __global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_p
   }
   __syncthreads();
 
-  // Gather of one 32-row tile into registers: thread tid owns 16-byte chunks
-  // tid + 256*it of the tile (row = chunk / 72, column chunk = chunk % 72).
+  // Gather of one 32-row tile into registers.  Thread tid owns tile row
+  // tid % 32 and the 16-byte column chunks tid / 32 + 8*it (it = 0..8), so
+  // the 32 lanes of a half-wave hold 32 different rows of one column: the
+  // transposed V writes below then spread over the LDS banks.
   constexpr int kChunks = (kRows * (kD / 8)) / 256;   // 9
+  const int my_row = tid & (kRows - 1);
+  const int my_col0 = tid >> 5;
   u32x4 pre[kChunks];
-  int pre_row = -1;                                   // tile row tid (tid < 32)
+  int pre_row = -1;
   auto row_of = [&](int e) -> int { return e < r1 ? rows_all[e - r0] : -1; };
   auto prefetch = [&](int base) {
+    pre_row = row_of(base + my_row);
+    const __bf16* src = kvb + (int64_t)(pre_row < 0 ? 0 : pre_row) * kD;
 #pragma unroll
     for (int it = 0; it < kChunks; ++it) {
-      const int ch = tid + 256 * it;
-      const int row = row_of(base + ch / (kD / 8));
-      pre[it] = row >= 0 ? *reinterpret_cast<const u32x4*>(kvb + (int64_t)row * kD + (ch % (kD / 8)) * 8)
-                         : u32x4{0, 0, 0, 0};
+      const int col = my_col0 + 8 * it;
+      pre[it] = pre_row >= 0 ? *reinterpret_cast<const u32x4*>(src + col * 8) : u32x4{0, 0, 0, 0};
     }
-    if (tid < kRows) pre_row = row_of(base + tid);
   };
   if (r0 < r1) prefetch(r0);
 
@@ -112,9 +115,8 @@ __global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_p
     if (tid < kRows) rowidx[tid] = pre_row;
 #pragma unroll
     for (int it = 0; it < kChunks; ++it) {
-      const int ch = tid + 256 * it;
-      const int rr = ch / (kD / 8);
-      const int col = ch % (kD / 8);
+      const int rr = my_row;
+      const int col = my_col0 + 8 * it;
       const u32x4 v = pre[it];
       *reinterpret_cast<u32x4*>(&Ks[rr * kKStride + col * 8]) = v;
       if (col < kDV / 8) {
@@ -153,14 +155,19 @@ __global__ __launch_bounds__(256, 1) void mla_bf16_kernel(AttnArgs a, int rows_p
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    // Lazy rescaling: the reference max m_run only moves when the tile max
+    // exceeds it by more than 8 (log2 units), so probabilities stay below
+    // 2^8 and O / l are rescaled rarely (O starts at zero, so the first move
+    // needs no rescale either).
+    const bool first = m_run == -INFINITY;
+    const float m_new = (first || tmax > m_run + 8.f) ? fmaxf(m_run, tmax) : m_run;
     float p[8];
     float alpha = 1.f;
     if (m_new == -INFINITY) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = 0.f;
     } else {
-      alpha = exp2f(m_run - m_new);   // m_run = -inf gives 0
+      if (!first) alpha = exp2f(m_run - m_new);
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = exp2f(x[i] - m_new);
     }

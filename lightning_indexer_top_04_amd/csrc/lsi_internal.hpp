@@ -27,10 +27,10 @@ struct ScanArgs {
   int n_pos = 0;
   int n_heads = 0;
   int dim = 0;
-  // optional: build the first-digit histogram of the top-k of each request
-  // (topk_ws is a top-k workspace whose counters are zero; topk_k its k)
-  void* topk_ws = nullptr;
-  int topk_k = 0;
+  // optional: clear this many uint32 words at zero_ptr (grid-stride), so a
+  // top-k that follows finds its counters at zero without another launch
+  uint32_t* zero_ptr = nullptr;
+  int64_t zero_words = 0;
 };
 
 hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s);
@@ -56,8 +56,7 @@ struct TopkArgs {
 size_t topk_ws_bytes(int num_req, int max_len);
 // words of the workspace that must be zero when the top-k starts
 int64_t topk_zero_words(int num_req);
-// ws_state: 0 = counters not cleared (clear them first), 1 = cleared,
-// 2 = cleared and the first-digit histogram already built (by the scan)
+// ws_state: 0 = counters not cleared (clear them first), 1 = already cleared
 hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s);
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t s);
 

@@ -16,13 +16,7 @@
 // Latency hiding: the page ids of a workgroup's slice are staged in LDS before
 // the tile loop, so a tile's key loads never wait on a page-table load, and
 // every wave keeps two tiles of keys in flight while it computes a third.
-//
-// Optionally the scan also builds the top-k's first-digit histogram of its
-// scores (LDS atomics, one flush of the non-empty bins per workgroup), and the
-// last workgroup of each request picks the bin that holds the k-th score, so
-// the selection needs a single further pass.
 #include "lsi_internal.hpp"
-#include "topk_common.hpp"
 
 namespace lsi {
 namespace {
@@ -70,16 +64,19 @@ struct QOp {
   using T = typename std::conditional<KIND == KIND_FP8, bf16x8, f16x8>::type;
 };
 
-template <int KIND, bool GATHER, bool HIST>
+template <int KIND, bool GATHER>
 __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk, int page_shift) {
   constexpr int ROW = KIND == KIND_FP8 ? kDim : kDim / 2;   // key bytes per token
   using QT = typename QOp<KIND>::T;
   __shared__ int pages[GATHER ? 1 : kMaxChunkPages];
-  __shared__ uint32_t hist[HIST ? topk::kBins : 1];
-  __shared__ uint32_t tmp[32];
-  __shared__ int flag;
   __shared__ float inv_scale[KIND == KIND_INT4 ? kWaves * kHeads : 1];
 
+  if (a.zero_ptr) {
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * kThreads;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+         i < a.zero_words; i += nthreads)
+      a.zero_ptr[i] = 0u;
+  }
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,8 +97,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
     for (int i = tid; i < npg; i += kThreads)
       pages[i] = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
   }
-  if (HIST)
-    for (int i = tid; i < topk::kBins; i += kThreads) hist[i] = 0u;
 
   // query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7
   const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
@@ -223,15 +218,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
       if (h == 0 && f0.valid) {
         const float sc = f0.ok ? total * f0.scale : -INFINITY;
         a.scores[(int64_t)b * a.ld + f0.item] = sc;
-        if (HIST) atomicAdd(&hist[float_key(sc) >> 20], 1u);
       }
       f0 = f1;
       f1 = f2;
     }
   }
-  if (HIST)
-    topk::hist_flush_and_decide<kThreads>(topk::carve(a.topk_ws, a.num_req), b, L, a.topk_k,
-                                          nprod, hist, tmp, &flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -239,6 +230,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
   extern __shared__ float smem[];
+  if (a.zero_ptr) {
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+         i < a.zero_words; i += nthreads)
+      a.zero_ptr[i] = 0u;
+  }
   const int H = a.n_heads;
   const int d = a.dim;
   float* qs = smem;           // [H][d]
@@ -285,11 +282,9 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   const int ps = ilog2(a.page_size);
   if (gather)
-    hipLaunchKernelGGL((scan_kernel<KIND, true, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
-  else if (a.topk_ws)
-    hipLaunchKernelGGL((scan_kernel<KIND, false, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+    hipLaunchKernelGGL((scan_kernel<KIND, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   else
-    hipLaunchKernelGGL((scan_kernel<KIND, false, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+    hipLaunchKernelGGL((scan_kernel<KIND, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   return hipGetLastError();
 }
 

@@ -2,19 +2,20 @@
 // abstract: keep the k=2048 highest-scoring tokens of the whole cache).
 //
 // Radix select over the order-preserving 32-bit key of each score, never a
-// sort:
-//   1. first-digit histogram: every workgroup builds an LDS histogram of the
-//      top 12 key bits of its slice and adds the non-empty bins to the row's
-//      global histogram; the last workgroup of the row (arrival counter)
-//      finds the bin holding the k-th largest key.  The indexer scan can do
-//      this step itself on the scores it has just produced.
-//   2. topk_select: every workgroup classifies its slice: keys above that bin
-//      go straight to the output, keys inside it to a candidate list.  Slots
-//      come from a block scan plus one atomic per workgroup and counter.
-//      The last workgroup of the row refines the candidates alone, in LDS
-//      once they fit: 12 more key bits, the last 8 key bits, then the
-//      position (ascending) for exact ties, each a 4096-bin LDS histogram
-//      and an ordered in-place compaction.
+// sort.  Three launches, handing over only at kernel boundaries (on this
+// GPU an agent-scope fence in hundreds of workgroups costs tens of
+// microseconds, so no workgroup waits for or signals another one):
+//   1. topk_hist: each workgroup builds an LDS histogram of the top 12 key
+//      bits of its slice and adds the non-empty bins to the row's global
+//      histogram (a few dozen atomics per hot bin).
+//   2. topk_select: each workgroup reads the row histogram, finds the bin
+//      that holds the k-th largest key, writes the keys above it straight to
+//      the output and collects the bin's members; slots come from a block
+//      scan and one atomic per workgroup and counter.
+//   3. topk_refine: one workgroup per row refines the candidates in LDS:
+//      12 more key bits, the last 8 key bits, then positions (ascending) for
+//      exact ties; each stage is a 4096-bin LDS histogram and an ordered
+//      in-place compaction.  It also writes the padding and the count.
 #include "lsi_internal.hpp"
 #include "topk_common.hpp"
 
@@ -48,22 +49,21 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint32_t* p, int64_t n) {
 
 __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a, int chunk) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t tmp[32];
-  __shared__ int flag;
   const int r = blockIdx.y;
   const int L = row_len(a, r);
-  const int nprod = max(1, (L + chunk - 1) / chunk);
-  if ((int)blockIdx.x >= nprod) return;
+  if (L <= a.k) return;
+  const int begin = blockIdx.x * chunk;
+  if (begin >= L) return;
+  const int end = min(begin + chunk, L);
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
   __syncthreads();
-  if (L > a.k) {
-    const int begin = blockIdx.x * chunk;
-    const int end = min(begin + chunk, L);
-    const float* row = a.scores + (int64_t)r * a.ld;
-    for (int i = begin + threadIdx.x; i < end; i += kBlock)
-      atomicAdd(&hist[float_key(row[i]) >> 20], 1u);
-  }
-  hist_flush_and_decide<kBlock>(carve(a.ws, a.num_req), r, L, a.k, nprod, hist, tmp, &flag);
+  const float* row = a.scores + (int64_t)r * a.ld;
+  for (int i = begin + threadIdx.x; i < end; i += kBlock)
+    atomicAdd(&hist[float_key(row[i]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* gh = carve(a.ws, a.num_req).hist + (size_t)r * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kBlock)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
 // The single-workgroup refinement of a row's candidate list.
@@ -72,9 +72,9 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
   const float* row = a.scores + (int64_t)r * a.ld;
   int32_t* list = ws.cand + (size_t)r * a.max_len;
   int32_t* out = a.idx + (int64_t)r * a.k;
-  uint32_t n = atomic_load(st + ST_CAND);
-  uint32_t need = atomic_load(st + ST_NEED);
-  uint32_t out_pos = atomic_load(st + ST_OUT);
+  uint32_t n = st[ST_CAND];
+  uint32_t need = st[ST_NEED];
+  uint32_t out_pos = st[ST_OUT];
   bool in_lds = false;
   // stages: key bits [19:8], key bits [7:0], then position bits
   // [31:20], [19:8], [7:0] ascending
@@ -151,80 +151,86 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
 
 __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t tmp[32];
+  __shared__ uint32_t bases[2];
+  const int r = blockIdx.y;
+  const int L = row_len(a, r);
+  const int begin = blockIdx.x * kSelChunk;
+  if (begin >= max(L, 1)) return;
+  const int end = min(begin + kSelChunk, L);
+  int32_t* out = a.idx + (int64_t)r * a.k;
+  if (L <= a.k) {
+    // every element is kept; workgroup 0 also pads and counts
+    for (int i = begin + threadIdx.x; i < end; i += kBlock) out[i] = out_value(a, r, i);
+    if (blockIdx.x == 0) {
+      for (int i = L + threadIdx.x; i < a.k; i += kBlock) out[i] = -1;
+      if (threadIdx.x == 0) a.count[r] = L;
+    }
+    return;
+  }
+  const Ws ws = carve(a.ws, a.num_req);
+  uint32_t* st = ws.state + (size_t)r * kState;
+  const uint32_t* gh = ws.hist + (size_t)r * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = gh[i];
+  __syncthreads();
+  uint32_t better;
+  const uint32_t digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
+  if (blockIdx.x == 0 && threadIdx.x == 0) st[ST_NEED] = (uint32_t)a.k - better;
+  const float* row = a.scores + (int64_t)r * a.ld;
+  int32_t* list = ws.cand + (size_t)r * a.max_len;
+  // thread t owns elements begin + t*kPer .. +kPer (contiguous, 32 bytes)
+  const int i0 = begin + threadIdx.x * kPer;
+  uint32_t win = 0, eq = 0;      // bit masks over the kPer elements
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = i0 + j;
+    if (i < end) {
+      const uint32_t d = float_key(row[i]) >> 20;
+      win |= (uint32_t)(d > digit) << j;
+      eq |= (uint32_t)(d == digit) << j;
+    }
+  }
+  uint32_t tot;
+  const uint32_t pre = block_excl_scan<kBlock>(__popc(win) | (__popc(eq) << 16), tmp, &tot);
+  if (threadIdx.x == 0) {
+    bases[0] = (tot & 0xFFFF) ? atomicAdd(&st[ST_OUT], tot & 0xFFFF) : 0u;
+    bases[1] = (tot >> 16) ? atomicAdd(&st[ST_CAND], tot >> 16) : 0u;
+  }
+  __syncthreads();
+  uint32_t ow = bases[0] + (pre & 0xFFFF);
+  uint32_t oc = bases[1] + (pre >> 16);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if ((win >> j) & 1u) {
+      if (ow < (uint32_t)a.k) out[ow] = out_value(a, r, i0 + j);
+      ++ow;
+    }
+    if ((eq >> j) & 1u) {
+      if (oc < (uint32_t)a.max_len) list[oc] = i0 + j;
+      ++oc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t lkey[kLdsCand];
   __shared__ int32_t lslot[kLdsCand];
   __shared__ uint32_t tmp[32];
-  __shared__ uint32_t bases[2];
-  __shared__ int is_last;
-  const int r = blockIdx.y;
+  const int r = blockIdx.x;
   const int L = row_len(a, r);
-  const int nchunks = max(1, (L + kSelChunk - 1) / kSelChunk);
-  if ((int)blockIdx.x >= nchunks) return;
+  if (L <= a.k) return;
   const Ws ws = carve(a.ws, a.num_req);
-  uint32_t* st = ws.state + (size_t)r * kState;
-  const int mode = (int)st[ST_MODE];
-  const int begin = blockIdx.x * kSelChunk;
-  const int end = min(begin + kSelChunk, L);
-  int32_t* out = a.idx + (int64_t)r * a.k;
-  if (mode == 1) {
-    for (int i = begin + threadIdx.x; i < end && i < a.k; i += kBlock) out[i] = out_value(a, r, i);
-  } else {
-    const uint32_t digit = st[ST_DIGIT];
-    const float* row = a.scores + (int64_t)r * a.ld;
-    int32_t* list = ws.cand + (size_t)r * a.max_len;
-    // thread t owns elements begin + t*kPer .. +kPer (contiguous, 32 bytes)
-    const int i0 = begin + threadIdx.x * kPer;
-    uint32_t win = 0, eq = 0;      // bit masks over the kPer elements
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = i0 + j;
-      if (i < end) {
-        const uint32_t d = float_key(row[i]) >> 20;
-        win |= (uint32_t)(d > digit) << j;
-        eq |= (uint32_t)(d == digit) << j;
-      }
-    }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<kBlock>(__popc(win) | (__popc(eq) << 16), tmp, &tot);
-    if (threadIdx.x == 0) {
-      bases[0] = (tot & 0xFFFF) ? atomicAdd(&st[ST_OUT], tot & 0xFFFF) : 0u;
-      bases[1] = (tot >> 16) ? atomicAdd(&st[ST_CAND], tot >> 16) : 0u;
-    }
-    __syncthreads();
-    uint32_t ow = bases[0] + (pre & 0xFFFF);
-    uint32_t oc = bases[1] + (pre >> 16);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if ((win >> j) & 1u) {
-        if (ow < (uint32_t)a.k) out[ow] = out_value(a, r, i0 + j);
-        ++ow;
-      }
-      if ((eq >> j) & 1u) {
-        if (oc < (uint32_t)a.max_len) list[oc] = i0 + j;
-        ++oc;
-      }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = (atomicAdd(&st[ST_SEL_DONE], 1u) == (uint32_t)(nchunks - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (mode == 1) {
-    for (int i = L + threadIdx.x; i < a.k; i += kBlock) out[i] = -1;
-    if (threadIdx.x == 0) a.count[r] = min(L, a.k);
-    return;
-  }
-  refine_row(a, r, ws, st, hist, tmp, lkey, lslot);
+  refine_row(a, r, ws, ws.state + (size_t)r * kState, hist, tmp, lkey, lslot);
 }
 
+// a few dozen workgroups per row at most, so a hot bin sees few atomics
 int pick_hist_chunk(int64_t rows, int64_t max_len) {
   const int64_t target = (int64_t)num_cus() * 4;
   int64_t c = ceil_div(rows * max_len, target);
+  c = std::max<int64_t>(c, ceil_div(max_len, 32));
   c = ceil_div(c, kBlock) * kBlock;
-  if (c < 2048) c = 2048;
+  if (c < 4096) c = 4096;
   if (c > 65536) c = 65536;
   return (int)c;
 }
@@ -245,13 +251,12 @@ hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   if (ws_state == 0) launch_zero(static_cast<uint32_t*>(a.ws), topk_zero_words(a.num_req), s);
-  if (ws_state <= 1) {
-    const int chunk = pick_hist_chunk(a.num_req, a.max_len);
-    dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, chunk)), (unsigned)a.num_req);
-    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kBlock), 0, s, a, chunk);
-  }
-  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, kSelChunk)), (unsigned)a.num_req);
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kBlock), 0, s, a);
+  const int chunk = pick_hist_chunk(a.num_req, a.max_len);
+  dim3 hgrid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, chunk)), (unsigned)a.num_req);
+  hipLaunchKernelGGL(topk_hist_kernel, hgrid, dim3(kBlock), 0, s, a, chunk);
+  dim3 sgrid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, kSelChunk)), (unsigned)a.num_req);
+  hipLaunchKernelGGL(topk_select_kernel, sgrid, dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
