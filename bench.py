@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--sets", type=int, default=32)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a 512 MiB device copy (known traffic) for counter scaling")
     return p.parse_args()
 
 
@@ -157,6 +159,15 @@ def main():
                            "tokens_per_s": R * L / (t_sus * 1e-3), "GB_s": sus_gbs,
                            "frac": sus_gbs / HBM_PEAK_GBS},
     }
+
+    if args.calib_copy:
+        # a plain copy of known size: 512 MiB read + 512 MiB written per call
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = 512 << 20
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(di, wl, L, args.cpu_seconds)

@@ -27,9 +27,13 @@ FLAGS = [
 
 SOURCES = ["api.hip", "scan.hip", "topk.hip", "attn.hip", "prefill.hip"]
 
+# The score kernels take ReLU of MFMA results; NaN inputs (fp8 NaN codes) are
+# invalid by contract, so these files skip NaN canonicalisation before max().
+EXTRA = {"scan.hip": ["-fno-honor-nans"], "prefill.hip": ["-fno-honor-nans"]}
+
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

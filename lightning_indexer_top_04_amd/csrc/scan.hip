@@ -13,9 +13,14 @@
 // 32 heads it holds, one cross-half swap adds the other 32, and lanes 0..31
 // store 32 consecutive scores.
 //
-// Latency hiding: the page ids of a workgroup's slice are staged in LDS before
-// the tile loop, so a tile's key loads never wait on a page-table load, and
-// every wave keeps two tiles of keys in flight while it computes a third.
+// Memory path (contiguous mode): a 32-token tile is one contiguous block of a
+// page (4 KB of fp8 codes, 2 KB of int4), fetched with 16-byte loads in which
+// each instruction covers 1 KB contiguously; every wave keeps four tiles in
+// flight in registers while it computes one, and passes each tile
+// through its own padded LDS slot to reach the MFMA lane layout (row n of
+// the tile to lanes n and n+32).  The page ids of the workgroup's slice are
+// staged in LDS first, so no key load waits on the page table.  In gather
+// mode (scattered positions) each lane loads its own row directly.
 #include "lsi_internal.hpp"
 
 namespace lsi {
@@ -32,11 +37,14 @@ constexpr int KIND_FP8 = 0;
 constexpr int KIND_INT4 = 1;
 
 struct TileFetch {
-  u32x4 raw[4];   // fp8: 64 bytes of the key row; int4: raw[0..1] = 32 bytes
+  // contiguous mode: instruction i of the tile (1 KB each); gather mode: the
+  // lane's own key half (fp8: 64 bytes, int4: raw[0..1] = 32 bytes)
+  u32x4 raw[4];
   float scale;
   int item;
   bool valid;     // the slot exists (write a score)
-  bool ok;        // the token exists and its page is in range
+  bool ok;        // the token exists and its page is in range (gather mode)
+  bool tile_ok;   // the tile's page is in range (contiguous mode)
 };
 
 // ---------------------------------------------------------------------------
@@ -68,8 +76,11 @@ template <int KIND, bool GATHER>
 __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk, int page_shift) {
   constexpr int ROW = KIND == KIND_FP8 ? kDim : kDim / 2;   // key bytes per token
   using QT = typename QOp<KIND>::T;
+  constexpr int NINS = (kTile * ROW) / 1024;                // load instructions per tile
+  constexpr int LROW = ROW + 16;                            // padded LDS row (bytes)
   __shared__ int pages[GATHER ? 1 : kMaxChunkPages];
   __shared__ float inv_scale[KIND == KIND_INT4 ? kWaves * kHeads : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[GATHER ? 16 : kWaves * kTile * LROW];
 
   if (a.zero_ptr) {
     const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * kThreads;
@@ -159,68 +170,120 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
     const int item = begin + tile * kTile + m;
     f.item = item;
     f.valid = item < end;
-    int pos = item;
-    int page = -1;
     if (GATHER) {
-      pos = f.valid ? a.positions[(int64_t)b * a.n_pos + item] : -1;
+      const int pos = f.valid ? a.positions[(int64_t)b * a.n_pos + item] : -1;
       const bool in = f.valid && pos >= 0 && pos < L;
-      if (in) page = a.page_table[(int64_t)b * a.max_pages + (pos >> page_shift)];
-    } else if (f.valid) {
-      page = pages[(tile * kTile + m) >> page_shift];
-    }
-    f.ok = page >= 0 && page < a.num_pages;
-    const int64_t row = (int64_t)page * a.page_size + (pos & (a.page_size - 1));
-    if (f.ok) {
-      const u32x4* kp = reinterpret_cast<const u32x4*>(
-          static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
+      const int page = in ? a.page_table[(int64_t)b * a.max_pages + (pos >> page_shift)] : -1;
+      f.ok = page >= 0 && page < a.num_pages;
+      const int64_t row = (int64_t)page * a.page_size + (pos & (a.page_size - 1));
+      if (f.ok) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(
+            static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
 #pragma unroll
-      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
-      f.scale = a.kscale[row];
+        for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
+        f.scale = a.kscale[row];
+      } else {
+#pragma unroll
+        for (int i = 0; i < ROW / 32; ++i) f.raw[i] = u32x4{0, 0, 0, 0};
+        f.scale = 0.f;
+      }
+      f.tile_ok = true;
     } else {
+      // the whole tile lies in one page: tile_start .. +32 tokens
+      const int t0 = tile * kTile;                              // offset in the slice
+      const int page = pages[t0 >> page_shift];
+      f.tile_ok = page >= 0 && page < a.num_pages;
+      f.ok = f.tile_ok;
+      const int64_t row0 = (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1));
+      const int ntok = min(kTile, end - (begin + t0));        // tokens present in the tile
+      const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.keys) + row0 * ROW);
+      if (f.tile_ok && ntok == kTile) {                         // wave-uniform fast path
 #pragma unroll
-      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = u32x4{0, 0, 0, 0};
-      f.scale = 0.f;
+        for (int i = 0; i < NINS; ++i) f.raw[i] = tb[i * 64 + lane];
+        f.scale = a.kscale[row0 + m];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NINS; ++i) {
+          const int chunk = i * 64 + lane;                      // 16-byte chunk of the tile
+          f.raw[i] = (f.tile_ok && chunk * 16 < ntok * ROW) ? tb[chunk] : u32x4{0, 0, 0, 0};
+        }
+        f.scale = (f.tile_ok && m < ntok) ? a.kscale[row0 + m] : 0.f;
+      }
     }
     return f;
   };
+  // Contiguous mode: route a fetched tile through this wave's LDS slot and
+  // return the lane's key half (row m, bytes h*ROW/2 ..) as dwords.
+  uint8_t* my_stage = stage + (GATHER ? 0 : wave * kTile * LROW);
+  auto transpose = [&](const TileFetch& f, u32x4* out) {
+#pragma unroll
+    for (int i = 0; i < NINS; ++i) {
+      const int byte = (i * 64 + lane) * 16;
+      *reinterpret_cast<u32x4*>(my_stage + (byte / ROW) * LROW + (byte % ROW)) = f.raw[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < ROW / 32; ++i)
+      out[i] = *reinterpret_cast<const u32x4*>(my_stage + m * LROW + h * (ROW / 2) + 16 * i);
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Consume tile `tile` held in f, refill f with the tile four wave-steps
+  // ahead, then compute and store.  Four TileFetch registers form a ring that
+  // the loop below walks with static names, so four tiles stay in flight.
+  auto consume = [&](TileFetch& f, int tile) {
+    u32x4 kr[ROW / 32];
+    if (GATHER) {
+#pragma unroll
+      for (int i = 0; i < ROW / 32; ++i) kr[i] = f.raw[i];
+    } else {
+      transpose(f, kr);
+    }
+    const float scale = f.scale;
+    const int item = f.item;
+    const bool valid = f.valid;
+    const bool ok = f.ok;
+    if (tile + 4 * kWaves < ntile) f = fetch(tile + 4 * kWaves);
+    f32x16 acc0 = {};
+    f32x16 acc1 = {};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (KIND == KIND_FP8) {
+        const u32x4 r4 = kr[t >> 1];
+        const bf16x8 kb = (t & 1) ? fp8x8_to_bf16x8(r4.z, r4.w) : fp8x8_to_bf16x8(r4.x, r4.y);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][t], kb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][t], kb, acc1, 0, 0, 0);
+      } else {
+        const u32x4 r4 = kr[t >> 2];
+        const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
+        const f16x8 kb = int4x8_to_f16x8(d);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][t], kb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][t], kb, acc1, 0, 0, 0);
+      }
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part += wv[0][r] * fmaxf(acc0[r], 0.f);
+      part += wv[1][r] * fmaxf(acc1[r], 0.f);
+    }
+    const float total = half_swap_sum(part);
+    if (h == 0 && valid) a.scores[(int64_t)b * a.ld + item] = ok ? total * scale : -INFINITY;
+  };
 
   if (wave < ntile) {
-    TileFetch f0 = fetch(wave);
-    TileFetch f1;
+    TileFetch f0 = fetch(wave), f1, f2, f3;
     if (wave + kWaves < ntile) f1 = fetch(wave + kWaves);
-    for (int tile = wave; tile < ntile; tile += kWaves) {
-      TileFetch f2;
-      if (tile + 2 * kWaves < ntile) f2 = fetch(tile + 2 * kWaves);
-      f32x16 acc0 = {};
-      f32x16 acc1 = {};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if constexpr (KIND == KIND_FP8) {
-          const u32x4 r4 = f0.raw[t >> 1];
-          const bf16x8 kb = (t & 1) ? fp8x8_to_bf16x8(r4.z, r4.w) : fp8x8_to_bf16x8(r4.x, r4.y);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][t], kb, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][t], kb, acc1, 0, 0, 0);
-        } else {
-          const u32x4 r4 = f0.raw[t >> 2];
-          const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
-          const f16x8 kb = int4x8_to_f16x8(d);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][t], kb, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][t], kb, acc1, 0, 0, 0);
-        }
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part += wv[0][r] * fmaxf(acc0[r], 0.f);
-        part += wv[1][r] * fmaxf(acc1[r], 0.f);
-      }
-      const float total = half_swap_sum(part);
-      if (h == 0 && f0.valid) {
-        const float sc = f0.ok ? total * f0.scale : -INFINITY;
-        a.scores[(int64_t)b * a.ld + f0.item] = sc;
-      }
-      f0 = f1;
-      f1 = f2;
+    if (wave + 2 * kWaves < ntile) f2 = fetch(wave + 2 * kWaves);
+    if (wave + 3 * kWaves < ntile) f3 = fetch(wave + 3 * kWaves);
+    for (int tile = wave; tile < ntile; tile += 4 * kWaves) {
+      consume(f0, tile);
+      if (tile + kWaves >= ntile) break;
+      consume(f1, tile + kWaves);
+      if (tile + 2 * kWaves >= ntile) break;
+      consume(f2, tile + 2 * kWaves);
+      if (tile + 3 * kWaves >= ntile) break;
+      consume(f3, tile + 3 * kWaves);
     }
   }
 }
@@ -265,8 +328,8 @@ __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
 }
 
 int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather) {
-  // aim at ~4 workgroups per CU over the whole batch
-  const int64_t target = (int64_t)num_cus() * 4;
+  // aim at ~2 resident workgroups per CU over the whole batch
+  const int64_t target = (int64_t)num_cus() * 2;
   const int64_t unit = std::max<int64_t>(kTile * kWaves, gather ? 1 : page_size);
   int64_t chunk = ceil_div(num_req * max_items, target);
   chunk = ceil_div(std::max<int64_t>(chunk, 256), unit) * unit;
