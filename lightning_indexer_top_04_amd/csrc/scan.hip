@@ -2,9 +2,19 @@
 // cached token (the lightning indexer of the "Multi-layer Indexer" abstract
 // scores the whole cache of a layer).
 //
-// fp8 / int4 keys: the contraction [64 heads x 128] x [128 x 32 tokens] runs on
-// the matrix cores as two v_mfma_f32_32x32x16 per K-step, heads on the
-// accumulator rows, tokens on the lanes.  Each lane owns one token of the
+// fp8 keys: the contraction [64 heads x 128] x [128 x 32 tokens] runs on the
+// fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales), heads on
+// the accumulator rows, tokens on the lanes, with the key bytes fed to the
+// MFMA as stored (no conversion instruction).  The bf16 query is split
+// exactly into two fp8 parts: per head a power of two 2^E puts the largest
+// |q| in [128, 256), hi = RNE_e4m3(q 2^E) and lo = e4m3(q 2^E - hi).  A bf16
+// value has 8 significant bits and hi carries the top 4 (with rounding), so
+// the remainder has at most 4 and lo holds it exactly whenever the scaled
+// value is at least 2^-2 (the lowest e4m3 binade with a 2^-9 step); smaller
+// elements, below 2^-10 of their head's largest, keep an error under 2^-10
+// in scaled units.  acc += hi.k + lo.k, and the head weight absorbs 2^-E.
+// int4 keys (compact keys of the two-stage search) use v_mfma_f32_32x32x16_f16
+// (below).  Each lane owns one token of the
 // 32-token tile and half of its key row (64 contiguous bytes for fp8, 32 for
 // int4), so a tile is fetched with 16-byte loads straight from the page, with
 // no LDS staging.  The dot product does not depend on the order of the K index,
@@ -36,15 +46,15 @@ constexpr int kMaxChunkPages = kMaxChunk / 32;
 constexpr int KIND_FP8 = 0;
 constexpr int KIND_INT4 = 1;
 
+// Bits of the scale word that mark a gathered row as absent (a NaN, which no
+// valid per-token scale is).
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;
+
 struct TileFetch {
   // contiguous mode: instruction i of the tile (1 KB each); gather mode: the
   // lane's own key half (fp8: 64 bytes, int4: raw[0..1] = 32 bytes)
   u32x4 raw[4];
-  float scale;
-  int item;
-  bool valid;     // the slot exists (write a score)
-  bool ok;        // the token exists and its page is in range (gather mode)
-  bool tile_ok;   // the tile's page is in range (contiguous mode)
+  float scale;    // gather mode: kAbsent when the position or page is invalid
 };
 
 // ---------------------------------------------------------------------------
@@ -77,9 +87,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   constexpr int ROW = KIND == KIND_FP8 ? kDim : kDim / 2;   // key bytes per token
   using QT = typename QOp<KIND>::T;
   constexpr int NINS = (kTile * ROW) / 1024;                // load instructions per tile
+  constexpr int kRing = GATHER ? 2 : 4;                     // tiles in the prefetch ring
   constexpr int LROW = ROW + 16;                            // padded LDS row (bytes)
   __shared__ int pages[GATHER ? 1 : kMaxChunkPages];
-  __shared__ float inv_scale[KIND == KIND_INT4 ? kWaves * kHeads : 1];
+  __shared__ float inv_scale[kWaves * kHeads];
+  __shared__ __attribute__((aligned(16))) float wl[kWaves * kHeads];   // w_j * 2^-E_j
   __shared__ __attribute__((aligned(16))) uint8_t stage[GATHER ? 16 : kWaves * kTile * LROW];
 
   if (a.zero_ptr) {
@@ -112,12 +124,60 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   // query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7
   const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
   QT qa[2][8];
+  // fp8 path: qs[mt][part*2 + s] = 32 fp8 bytes (dims 64h + 32s ..) of the hi
+  // (part 0) or lo (part 1) split of head 32*mt + m
+  i32x8 qs[2][4];
   if constexpr (KIND == KIND_FP8) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      const int head = 32 * mt + m;
+      bf16x8 raw[8];
+      float amax = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        qa[mt][t] = *reinterpret_cast<const bf16x8*>(qb + (32 * mt + m) * kDim + 64 * h + 8 * t);
+      for (int t = 0; t < 8; ++t) {
+        raw[t] = *reinterpret_cast<const bf16x8*>(qb + head * kDim + 64 * h + 8 * t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[t][e]));
+      }
+      {
+        const uint32_t u = __float_as_uint(amax);
+        auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        amax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      int e2 = 0;
+      if (amax > 0.f) (void)frexpf(amax, &e2);
+      const int E = (amax > 0.f) ? 8 - e2 : 0;
+      const float sc = ldexpf(1.0f, E);
+      if (h == 0) inv_scale[wave * kHeads + head] = ldexpf(1.0f, -E);
+#pragma unroll
+      for (int sI = 0; sI < 2; ++sI) {
+        i32x8 hi, lo;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {          // dword d: dims 64h + 32 sI + 4d .. +3
+          const int t = sI * 4 + (d >> 1);
+          const int e0 = (d & 1) * 4;
+          float x[4], rem[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = (float)raw[t][e0 + j] * sc;
+          int ph = 0;
+          ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], ph, false);
+          ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], ph, true);
+          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, false);
+          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, true);
+          rem[0] = x[0] - h01[0];
+          rem[1] = x[1] - h01[1];
+          rem[2] = x[2] - h23[0];
+          rem[3] = x[3] - h23[1];
+          int pl = 0;
+          pl = __builtin_amdgcn_cvt_pk_fp8_f32(rem[0], rem[1], pl, false);
+          pl = __builtin_amdgcn_cvt_pk_fp8_f32(rem[2], rem[3], pl, true);
+          hi[d] = ph;
+          lo[d] = pl;
+        }
+        qs[mt][sI] = hi;
+        qs[mt][2 + sI] = lo;
+      }
+    }
   } else {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -152,63 +212,45 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   }
   __syncthreads();
 
-  // head weights of the accumulator rows this lane holds:
-  // row of register r in a 32x32 tile = 8*(r/4) + 4*h + r%4
-  float wv[2][16];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-      float wj = a.w[(int64_t)b * kHeads + head];
-      if constexpr (KIND == KIND_INT4) wj *= inv_scale[wave * kHeads + head];
-      wv[mt][r] = wj;
-    }
+  // head weights (with the query scale folded in), read per tile from LDS:
+  // the accumulator row of register r in a 32x32 tile is 8*(r/4) + 4*h + r%4,
+  // so each group of four registers needs four consecutive weights
+  if (lane < kHeads) wl[wave * kHeads + lane] = a.w[(int64_t)b * kHeads + lane] * inv_scale[wave * kHeads + lane];
+  __builtin_amdgcn_wave_barrier();
+  const f32x4* wl4 = reinterpret_cast<const f32x4*>(wl + wave * kHeads + 4 * h);
 
-  auto fetch = [&](int tile) {
+  // Every load below is unconditional and in bounds by construction, so the
+  // compiler can keep all tiles of the ring in flight (a conditional load at a
+  // join point makes it drain every outstanding load): the tile index is
+  // clamped to the last tile of the slice, an out-of-range page or position
+  // reads row 0 of the pool and is reported as -inf, and tokens past the end of
+  // a request still lie inside their allocated page and are never stored.
+  auto fetch = [&](int tile_in) {
     TileFetch f;
-    const int item = begin + tile * kTile + m;
-    f.item = item;
-    f.valid = item < end;
+    const int tile = min(tile_in, ntile - 1);
     if (GATHER) {
-      const int pos = f.valid ? a.positions[(int64_t)b * a.n_pos + item] : -1;
-      const bool in = f.valid && pos >= 0 && pos < L;
-      const int page = in ? a.page_table[(int64_t)b * a.max_pages + (pos >> page_shift)] : -1;
-      f.ok = page >= 0 && page < a.num_pages;
-      const int64_t row = (int64_t)page * a.page_size + (pos & (a.page_size - 1));
-      if (f.ok) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(
-            static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
+      const int it = min(begin + tile * kTile + m, end - 1);
+      const int pos = a.positions[(int64_t)b * a.n_pos + it];
+      const bool in = pos >= 0 && pos < L;
+      const int page = a.page_table[(int64_t)b * a.max_pages + ((in ? pos : 0) >> page_shift)];
+      const bool ok = in && page >= 0 && page < a.num_pages;
+      const int64_t row = ok ? (int64_t)page * a.page_size + (pos & (a.page_size - 1)) : 0;
+      const u32x4* kp = reinterpret_cast<const u32x4*>(
+          static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
 #pragma unroll
-        for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
-        f.scale = a.kscale[row];
-      } else {
-#pragma unroll
-        for (int i = 0; i < ROW / 32; ++i) f.raw[i] = u32x4{0, 0, 0, 0};
-        f.scale = 0.f;
-      }
-      f.tile_ok = true;
+      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
+      const float sc = a.kscale[row];
+      f.scale = ok ? sc : __uint_as_float(kAbsent);
     } else {
-      // the whole tile lies in one page: tile_start .. +32 tokens
+      // the whole tile lies in one page
       const int t0 = tile * kTile;                              // offset in the slice
       const int page = pages[t0 >> page_shift];
-      f.tile_ok = page >= 0 && page < a.num_pages;
-      f.ok = f.tile_ok;
-      const int64_t row0 = (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1));
-      const int ntok = min(kTile, end - (begin + t0));        // tokens present in the tile
+      const bool ok = page >= 0 && page < a.num_pages;
+      const int64_t row0 = ok ? (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1)) : 0;
       const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.keys) + row0 * ROW);
-      if (f.tile_ok && ntok == kTile) {                         // wave-uniform fast path
 #pragma unroll
-        for (int i = 0; i < NINS; ++i) f.raw[i] = tb[i * 64 + lane];
-        f.scale = a.kscale[row0 + m];
-      } else {
-#pragma unroll
-        for (int i = 0; i < NINS; ++i) {
-          const int chunk = i * 64 + lane;                      // 16-byte chunk of the tile
-          f.raw[i] = (f.tile_ok && chunk * 16 < ntok * ROW) ? tb[chunk] : u32x4{0, 0, 0, 0};
-        }
-        f.scale = (f.tile_ok && m < ntok) ? a.kscale[row0 + m] : 0.f;
-      }
+      for (int i = 0; i < NINS; ++i) f.raw[i] = tb[i * 64 + lane];
+      f.scale = a.kscale[row0 + m];
     }
     return f;
   };
@@ -240,19 +282,37 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
       transpose(f, kr);
     }
     const float scale = f.scale;
-    const int item = f.item;
-    const bool valid = f.valid;
-    const bool ok = f.ok;
-    if (tile + 4 * kWaves < ntile) f = fetch(tile + 4 * kWaves);
+    const int item = begin + tile * kTile + m;
+    const bool valid = item < end;
+    bool ok;
+    if (GATHER) {
+      ok = __float_as_uint(scale) != kAbsent;
+    } else {
+      const int page = pages[(tile * kTile) >> page_shift];
+      ok = page >= 0 && page < a.num_pages;
+    }
+    f = fetch(tile + kRing * kWaves);   // clamped at the end of the slice
     f32x16 acc0 = {};
     f32x16 acc1 = {};
+    if constexpr (KIND == KIND_FP8) {
+#pragma unroll
+      for (int sI = 0; sI < 2; ++sI) {
+        const u32x4 k0 = kr[2 * sI];
+        const u32x4 k1 = kr[2 * sI + 1];
+        const i32x8 kb = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                          (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[0][part * 2 + sI], kb, acc0,
+                                                                 0, 0, 0, 127, 0, 127);
+          acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[1][part * 2 + sI], kb, acc1,
+                                                                 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if constexpr (KIND == KIND_FP8) {
-        const u32x4 r4 = kr[t >> 1];
-        const bf16x8 kb = (t & 1) ? fp8x8_to_bf16x8(r4.z, r4.w) : fp8x8_to_bf16x8(r4.x, r4.y);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][t], kb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][t], kb, acc1, 0, 0, 0);
       } else {
         const u32x4 r4 = kr[t >> 2];
         const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
@@ -263,27 +323,42 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
     }
     float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part += wv[0][r] * fmaxf(acc0[r], 0.f);
-      part += wv[1][r] * fmaxf(acc1[r], 0.f);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w0 = wl4[2 * q];        // heads 8q + 4h + 0..3
+      const f32x4 w1 = wl4[8 + 2 * q];    // heads 32 + 8q + 4h + 0..3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        part += w0[j] * fmaxf(acc0[4 * q + j], 0.f);
+        part += w1[j] * fmaxf(acc1[4 * q + j], 0.f);
+      }
     }
     const float total = half_swap_sum(part);
     if (h == 0 && valid) a.scores[(int64_t)b * a.ld + item] = ok ? total * scale : -INFINITY;
   };
 
   if (wave < ntile) {
-    TileFetch f0 = fetch(wave), f1, f2, f3;
-    if (wave + kWaves < ntile) f1 = fetch(wave + kWaves);
-    if (wave + 2 * kWaves < ntile) f2 = fetch(wave + 2 * kWaves);
-    if (wave + 3 * kWaves < ntile) f3 = fetch(wave + 3 * kWaves);
-    for (int tile = wave; tile < ntile; tile += 4 * kWaves) {
-      consume(f0, tile);
-      if (tile + kWaves >= ntile) break;
-      consume(f1, tile + kWaves);
-      if (tile + 2 * kWaves >= ntile) break;
-      consume(f2, tile + 2 * kWaves);
-      if (tile + 3 * kWaves >= ntile) break;
-      consume(f3, tile + 3 * kWaves);
+    if constexpr (kRing == 4) {
+      TileFetch f0 = fetch(wave);
+      TileFetch f1 = fetch(wave + kWaves);
+      TileFetch f2 = fetch(wave + 2 * kWaves);
+      TileFetch f3 = fetch(wave + 3 * kWaves);
+      for (int tile = wave; tile < ntile; tile += 4 * kWaves) {
+        consume(f0, tile);
+        if (tile + kWaves >= ntile) break;
+        consume(f1, tile + kWaves);
+        if (tile + 2 * kWaves >= ntile) break;
+        consume(f2, tile + 2 * kWaves);
+        if (tile + 3 * kWaves >= ntile) break;
+        consume(f3, tile + 3 * kWaves);
+      }
+    } else {
+      TileFetch f0 = fetch(wave);
+      TileFetch f1 = fetch(wave + kWaves);
+      for (int tile = wave; tile < ntile; tile += 2 * kWaves) {
+        consume(f0, tile);
+        if (tile + kWaves >= ntile) break;
+        consume(f1, tile + kWaves);
+      }
     }
   }
 }
