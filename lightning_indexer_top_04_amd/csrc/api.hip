@@ -329,8 +329,9 @@ size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len, int
   if (num_req < 1 || max_seq_len < 0 || k < 1 || n_heads < 1) return 0;
   const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
   const size_t tk = topk_ws_bytes(num_req, max_seq_len);
+  const size_t ph = align_up((size_t)num_req * k * sizeof(int32_t), kWsAlign);
   const size_t at = (n_heads % 64 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
-  return sc + tk + at;
+  return sc + tk + ph + at;
 }
 
 int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
@@ -354,6 +355,8 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
   void* topk_ws = ws;
   ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
+  int32_t* phys = reinterpret_cast<int32_t*>(ws);   // physical rows of the selection
+  ws += align_up((size_t)batch->num_req * k * sizeof(int32_t), kWsAlign);
   void* attn_wsp = ws;
 
   // the scan also clears the top-k counters that the selection uses next
@@ -372,9 +375,15 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.idx = idx;
   t.count = count;
   t.ws = topk_ws;
+  t.phys = phys;
+  t.page_table = batch->page_table;
+  t.max_pages = batch->max_pages;
+  t.page_size = kv->page_size;
+  t.num_pages = kv->num_pages;
   launch_topk(t, 1, stream);
 
-  const AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
+  AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
+  a.phys = phys;
   run_attn(kv->dtype, a, stream);
   return check_launch("lsi_decode_step");
 }

@@ -52,6 +52,13 @@ struct TopkArgs {
   int32_t* idx = nullptr;          // [num_req][k]
   int32_t* count = nullptr;        // [num_req]
   void* ws = nullptr;              // workspace (topk_ws_bytes)
+  // optional: also write the physical cache row of every kept position
+  // (page_table[r][pos / page_size] * page_size + pos % page_size, or -1)
+  int32_t* phys = nullptr;         // [num_req][k]
+  const int32_t* page_table = nullptr;
+  int max_pages = 0;
+  int page_size = 1;
+  int num_pages = 0;
 };
 size_t topk_ws_bytes(int num_req, int max_len);
 // words of the workspace that must be zero when the top-k starts
@@ -76,6 +83,7 @@ struct AttnArgs {
   int dk = 0;
   int dv = 0;
   const int32_t* idx = nullptr;    // [num_req][k]
+  const int32_t* phys = nullptr;   // optional [num_req][k] physical rows of idx (-1 = skip)
   int k = 0;
   float sm_scale = 0.f;
   void* out = nullptr;             // [num_req][H][dv]

@@ -41,6 +41,20 @@ __device__ __forceinline__ int out_value(const TopkArgs& a, int r, int slot) {
   return a.map ? a.map[(int64_t)r * a.map_ld + slot] : slot;
 }
 
+// Write kept position `pos` at output slot `o` of row r (and its physical
+// cache row when requested).
+__device__ __forceinline__ void emit(const TopkArgs& a, int r, int o, int pos) {
+  a.idx[(int64_t)r * a.k + o] = pos;
+  if (a.phys) {
+    int row = -1;
+    if (pos >= 0) {
+      const int page = a.page_table[(int64_t)r * a.max_pages + pos / a.page_size];
+      if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+    }
+    a.phys[(int64_t)r * a.k + o] = row;
+  }
+}
+
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void zero_kernel(uint32_t* p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -71,7 +85,6 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
                            uint32_t* tmp, uint32_t* lkey, int32_t* lslot) {
   const float* row = a.scores + (int64_t)r * a.ld;
   int32_t* list = ws.cand + (size_t)r * a.max_len;
-  int32_t* out = a.idx + (int64_t)r * a.k;
   uint32_t n = st[ST_CAND];
   uint32_t need = st[ST_NEED];
   uint32_t out_pos = st[ST_OUT];
@@ -122,7 +135,7 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
       uint32_t tot;
       const uint32_t pre = block_excl_scan<kBlock>(flag_win | (flag_eq << 16), tmp, &tot);
       if (flag_win && out_pos + (pre & 0xFFFF) < (uint32_t)a.k)
-        out[out_pos + (pre & 0xFFFF)] = out_value(a, r, slot);
+        emit(a, r, out_pos + (pre & 0xFFFF), out_value(a, r, slot));
       if (flag_eq) {
         const uint32_t j = keep + (pre >> 16);
         if (in_lds) {
@@ -142,10 +155,10 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
   // whatever remains is taken whole (n <= need here)
   const uint32_t take = min(n, need);
   for (uint32_t i = threadIdx.x; i < take && out_pos + i < (uint32_t)a.k; i += kBlock)
-    out[out_pos + i] = out_value(a, r, in_lds ? lslot[i] : list[i]);
+    emit(a, r, out_pos + i, out_value(a, r, in_lds ? lslot[i] : list[i]));
   out_pos += take;
   __syncthreads();
-  for (int i = (int)out_pos + threadIdx.x; i < a.k; i += kBlock) out[i] = -1;
+  for (int i = (int)out_pos + threadIdx.x; i < a.k; i += kBlock) emit(a, r, i, -1);
   if (threadIdx.x == 0) a.count[r] = (int32_t)min(out_pos, (uint32_t)a.k);
 }
 
@@ -158,12 +171,11 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   const int begin = blockIdx.x * kSelChunk;
   if (begin >= max(L, 1)) return;
   const int end = min(begin + kSelChunk, L);
-  int32_t* out = a.idx + (int64_t)r * a.k;
   if (L <= a.k) {
     // every element is kept; workgroup 0 also pads and counts
-    for (int i = begin + threadIdx.x; i < end; i += kBlock) out[i] = out_value(a, r, i);
+    for (int i = begin + threadIdx.x; i < end; i += kBlock) emit(a, r, i, out_value(a, r, i));
     if (blockIdx.x == 0) {
-      for (int i = L + threadIdx.x; i < a.k; i += kBlock) out[i] = -1;
+      for (int i = L + threadIdx.x; i < a.k; i += kBlock) emit(a, r, i, -1);
       if (threadIdx.x == 0) a.count[r] = L;
     }
     return;
@@ -202,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     if ((win >> j) & 1u) {
-      if (ow < (uint32_t)a.k) out[ow] = out_value(a, r, i0 + j);
+      if (ow < (uint32_t)a.k) emit(a, r, ow, out_value(a, r, i0 + j));
       ++ow;
     }
     if ((eq >> j) & 1u) {
