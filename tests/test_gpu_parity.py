@@ -256,3 +256,49 @@ def test_decode_step_unplanted():
     wl = synth.scaled(synth.DSA_128K, seed=21, seq_lens=(20000,), n_planted=0)
     di = synth.make_decode_inputs(wl, device=DEV, planted=False)
     print(_check_step(di, 2048))
+
+
+def test_decode_step_graph_replays_match_eager():
+    """The fused step captured in a HIP graph: every replay (with eager work
+    and synchronisations in between) reproduces the eager result."""
+    di = small_dsa([9000, 3000, 700], k=2048)
+    ik, req, kv, _ = objs(di)
+    B, k, H, dv = 3, 2048, 128, 512
+    idx = torch.empty(B, k, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, H, dv, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(lsi.decode_step_workspace_bytes(B, req.max_seq_len, k, H, dv),
+                     dtype=torch.uint8, device=DEV)
+
+    def run():
+        lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k, di.wl.sm_scale, dv,
+                        out=out, lse=lse, idx=idx, count=cnt, ws=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e_idx = torch.sort(idx, dim=1).values.clone()
+    e_cnt = cnt.clone()
+    e_out = out.float().clone()
+    e_lse = lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        out.zero_()
+        idx.fill_(-7)
+        lse.fill_(123.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cnt, e_cnt), rep
+        assert torch.equal(torch.sort(idx, dim=1).values, e_idx), rep
+        for b in range(B):
+            check_attention(out[b].float().cpu().numpy(), e_out[b].cpu().numpy().astype(np.float64),
+                            f"replay {rep} req {b}")
+        assert torch.allclose(lse, e_lse, rtol=1e-5, atol=1e-5), rep
