@@ -364,6 +364,323 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
 }
 
 // ---------------------------------------------------------------------------
+// fp8 keys, contiguous page walk: the prefetch ring lives in LDS and is filled
+// by global->LDS DMA (global_load_lds_dwordx4), so no VGPRs hold tiles in
+// flight and no instruction copies them into LDS.  Each DMA instruction moves
+// 1 KB (8 token rows) contiguously; a lane's 16 bytes land at base + 16*lane,
+// so the lane fetches the chunk that belongs at that LDS position: row r of
+// the 8, chunk c ^ r.  Stored this way (16-byte chunk j of row m at chunk
+// j ^ (m & 7)), the per-lane 16-byte reads of the MFMA layout hit eight
+// different bank groups in every group of eight lanes.
+// The query split (hi/lo fp8 per head, as above) is computed once per
+// workgroup, 16 heads per wave, and handed to every wave through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kTileBytes = kTile * kDim;    // 4 KB of fp8 codes
+constexpr int kSlotBytes = kTileBytes + 256; // codes + the 32 scales, twice
+constexpr int kFlushTiles = 32;             // tiles of scores staged per wave (4 KB)
+
+// Key tiles are read once: the non-temporal hint keeps them from evicting the
+// freshly written scores from L2, whose write-back would otherwise interleave
+// with the key stream in HBM.
+constexpr int kNonTemporal = 2;
+
+template <int OFF>
+__device__ __forceinline__ void lds_dma16(uint8_t* lds, const uint8_t* g) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, OFF, kNonTemporal);
+}
+// The four 16-byte reads of a lane's key half, with their wait in the same
+// statement.  Written out because the compiler, not knowing which DMA wrote
+// which ring position, would otherwise wait for every DMA in flight first.
+__device__ __forceinline__ void lds_read_tile(u32x4 (&kr)[4], const uint8_t* slot, const uint32_t (&rd)[4]) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)slot;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3])
+      : "v"(base + rd[0]), "v"(base + rd[1]), "v"(base + rd[2]), "v"(base + rd[3])
+      : "memory");
+}
+// Workgroup barrier for LDS data only.  __syncthreads() also releases global
+// memory, which waits for every DMA in flight; here only LDS writes need to
+// be visible to the other waves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ float lds_read_f32(const uint8_t* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+  float v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_dma4(uint8_t* lds, const float* g) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, kNonTemporal);
+}
+
+// Wait until the tile issued RING - 1 refills ago has landed: every refill
+// is 5 vector-memory operations.
+template <int RING>
+__device__ __forceinline__ void wait_ring_tile() {
+  static_assert(RING >= 2 && RING <= 4, "ring of 2 to 4 tiles");
+  if constexpr (RING == 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  if constexpr (RING == 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  if constexpr (RING == 4) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+}
+
+template <int RING>
+__global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kernel(ScanArgs a, int chunk,
+                                                                                   int page_shift) {
+  static_assert(kTileBytes == 4 * 1024, "four 1 KB DMA instructions per tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING][kWaves * kSlotBytes];
+  __shared__ int pages[kMaxChunkPages];
+  __shared__ __attribute__((aligned(16))) float wl[kHeads];   // w_j * 2^-E_j
+  __shared__ __attribute__((aligned(16))) float sbuf[kWaves][kFlushTiles * kTile];
+
+  if (a.zero_ptr) {
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * kThreads;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+         i < a.zero_words; i += nthreads)
+      a.zero_ptr[i] = 0u;
+  }
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int h = lane >> 5;
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int nprod = max(1, (L + chunk - 1) / chunk);
+  if ((int)blockIdx.x >= nprod) return;
+  const int begin = blockIdx.x * chunk;
+  const int end = min(begin + chunk, L);
+  const int ntile = max(0, (end - begin + kTile - 1) / kTile);
+  {
+    const int npg = (end - begin + a.page_size - 1) >> page_shift;
+    const int pg0 = begin >> page_shift;
+    for (int i = tid; i < npg; i += kThreads)
+      pages[i] = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
+  }
+  __syncthreads();
+
+  // A wave takes a contiguous run of the slice's tiles, so its scores form
+  // one contiguous range.
+  const int per = (ntile + kWaves - 1) / kWaves;
+  const int my0 = wv * per;
+  const int myn = max(0, min(ntile - my0, per));
+  const int r8 = lane >> 3;
+  const uint32_t goff = 128 * r8 + 16 * ((lane & 7) ^ r8);
+  uint32_t rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rd[i] = m * 128 + 16 * ((4 * h + i) ^ (m & 7));
+  const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
+
+  // Every refill is issued, clamped to the wave's last tile, so the count of
+  // vector-memory operations between a tile's DMA and its use is the same at
+  // every step: RING - 1 later tiles of 5 DMAs each (four 1 KB key moves and
+  // one for the 32 scales, which lanes 32..63 copy a second time).  vmcnt
+  // counts loads in issue order, so waiting until at most that many are
+  // outstanding means the tile has landed in LDS.  (A wave without tiles
+  // fetches the slice's first tile into its own slots, which keeps the waits
+  // of every wave the same.)
+  auto issue = [&](int j, uint8_t* slot) {
+    const int t0 = (myn > 0 ? my0 + min(j, myn - 1) : 0) * kTile;
+    const int page = __builtin_amdgcn_readfirstlane(pages[t0 >> page_shift]);
+    const bool ok = page >= 0 && page < a.num_pages;
+    const int64_t row0 = ok ? (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1)) : 0;
+    const uint8_t* g = keys + row0 * kDim + goff;
+    asm volatile("" ::: "memory");
+    lds_dma16<0>(slot, g);
+    lds_dma16<1024>(slot, g);
+    lds_dma16<2048>(slot, g);
+    lds_dma16<3072>(slot, g);
+    lds_dma4(slot + kTileBytes, a.kscale + row0 + m);
+  };
+  uint8_t* slot[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) slot[r] = &ring[r][0] + wv * kSlotBytes;
+
+  // The query split is computed while the first key tiles are on their way.
+  // The query rows of the wave's 16 heads (4 KB) and the 64 head weights come
+  // in by DMA as well, into the last ring position: an ordinary load issued
+  // ahead of the tile DMAs would be waited for with every DMA behind it.
+  // Issue order: query + weights (5 operations), then tiles 0 .. RING-2
+  // (5 each); the last ring position gets its tile once the split is done.
+  {
+    uint8_t* qslot = slot[RING - 1];
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
+                                                        ((int64_t)b * kHeads + 16 * wv) * kDim) + 16 * lane;
+    asm volatile("" ::: "memory");
+    lds_dma16<0>(qslot, qg);
+    lds_dma16<1024>(qslot, qg);
+    lds_dma16<2048>(qslot, qg);
+    lds_dma16<3072>(qslot, qg);
+    lds_dma4(qslot + kTileBytes, a.w + (int64_t)b * kHeads + lane);
+  }
+#pragma unroll
+  for (int r = 0; r + 1 < RING; ++r) issue(r, slot[r]);
+  wait_ring_tile<RING>();     // the query DMAs, RING - 1 tile groups ago
+  const int qhead = 16 * wv + (lane >> 2);
+  const int d0 = 32 * (lane & 3);
+  bf16x8 raw[4];
+  float wq;
+  {
+    u32x4 qr[4];
+    uint32_t qoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qoff[t] = (lane >> 2) * 2 * kDim + 2 * d0 + 16 * t;
+    lds_read_tile(qr, slot[RING - 1], qoff);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) raw[t] = __builtin_bit_cast(bf16x8, qr[t]);
+    wq = lds_read_f32(slot[RING - 1] + kTileBytes + 4 * qhead);
+  }
+
+  // Query split into the score staging buffer (free until the first tile is
+  // scored): row `head` holds 16 chunks of 16 bytes, hi dims then lo dims,
+  // chunk c stored at position c ^ (head % 16) so that the reads below, 16
+  // rows at a time at one logical chunk, spread over all banks.
+  uint8_t* qx = reinterpret_cast<uint8_t*>(&sbuf[0][0]);
+  static_assert(sizeof(sbuf) == kHeads * 2 * kDim, "query split fills the staging buffer");
+  {
+    float amax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[t][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    int e2 = 0;
+    if (amax > 0.f) (void)frexpf(amax, &e2);
+    const int E = (amax > 0.f) ? 8 - e2 : 0;
+    const float sc = ldexpf(1.0f, E);
+    if ((lane & 3) == 0) wl[qhead] = wq * ldexpf(1.0f, -E);
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {              // dword d: dims d0 + 4d .. +3
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = (float)raw[d >> 1][(d & 1) * 4 + j] * sc;
+      int ph = 0;
+      ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], ph, false);
+      ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], ph, true);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, false);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, true);
+      int pl = 0;
+      pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], pl, false);
+      pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], pl, true);
+      hi[d] = (uint32_t)ph;
+      lo[d] = (uint32_t)pl;
+    }
+    uint8_t* row = qx + qhead * 2 * kDim;
+    const int sw = qhead & 15;
+    const int c0 = d0 / 16;
+    *reinterpret_cast<u32x4*>(row + 16 * (c0 ^ sw)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4*>(row + 16 * ((c0 + 1) ^ sw)) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    *reinterpret_cast<u32x4*>(row + 16 * ((8 + c0) ^ sw)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    *reinterpret_cast<u32x4*>(row + 16 * ((9 + c0) ^ sw)) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  }
+  lds_barrier();
+  // qs[mt][part*2 + sI]: 32 bytes (dims 64h + 32 sI ..) of part `part` of head 32 mt + m
+  i32x8 qs[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int sI = 0; sI < 2; ++sI) {
+        const int head = 32 * mt + m;
+        const uint8_t* row = qx + head * 2 * kDim;
+        const int c = part * 8 + 4 * h + 2 * sI;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(row + 16 * (c ^ (head & 15)));
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(row + 16 * ((c + 1) ^ (head & 15)));
+        qs[mt][part * 2 + sI] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      }
+  lds_barrier();   // the staging buffer takes scores from here on
+  const f32x4* wl4 = reinterpret_cast<const f32x4*>(wl + 4 * h);
+  issue(RING - 1, slot[RING - 1]);    // the query rows are no longer needed
+
+  // Score of token m of the wave's j-th tile (the same in lanes m and m + 32).
+  auto consume = [&](int j, uint8_t* slot) -> float {
+    wait_ring_tile<RING>();
+    u32x4 kr[4];
+    lds_read_tile(kr, slot, rd);
+    const float scale = *reinterpret_cast<const float*>(slot + kTileBytes + 4 * lane);
+    const int page = pages[((my0 + j) * kTile) >> page_shift];
+    const bool ok = page >= 0 && page < a.num_pages;
+    f32x16 acc0 = {};
+    f32x16 acc1 = {};
+#pragma unroll
+    for (int sI = 0; sI < 2; ++sI) {
+      const u32x4 k0 = kr[2 * sI];
+      const u32x4 k1 = kr[2 * sI + 1];
+      const i32x8 kb = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                        (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[0][part * 2 + sI], kb, acc0,
+                                                               0, 0, 0, 127, 0, 127);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[1][part * 2 + sI], kb, acc1,
+                                                               0, 0, 0, 127, 0, 127);
+      }
+    }
+    // the slot's reads are complete (the MFMAs consumed them): refill it
+    issue(j + RING, slot);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 w0 = wl4[2 * q];        // heads 8q + 4h + 0..3
+      const f32x4 w1 = wl4[8 + 2 * q];    // heads 32 + 8q + 4h + 0..3
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        part += w0[jj] * fmaxf(acc0[4 * q + jj], 0.f);
+        part += w1[jj] * fmaxf(acc1[4 * q + jj], 0.f);
+      }
+    }
+    const float total = half_swap_sum(part);
+    return ok ? total * scale : -INFINITY;
+  };
+
+  // Scores are staged per wave in LDS and written kFlushTiles tiles (4 KB)
+  // at a time: a trickle of small score stores from every wave, each to its
+  // own DRAM row, slows the key stream far beyond the bytes it adds.
+  float* out = a.scores + (int64_t)b * a.ld + begin;
+  float* stage = sbuf[wv];
+  auto stage_score = [&](int j, float v) {
+    if (h == 0) stage[(j % kFlushTiles) * kTile + m] = v;
+  };
+  auto flush = [&](int j) {                  // after tile j, the last of its group
+    const int first = j - j % kFlushTiles;
+    const int pos0 = (my0 + first) * kTile;
+    const int n = min((j - first + 1) * kTile, (end - begin) - pos0);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 4 * lane; i < n; i += 4 * 64) {
+      if (i + 4 <= n) {
+        *reinterpret_cast<f32x4*>(out + pos0 + i) = *reinterpret_cast<const f32x4*>(stage + i);
+      } else {
+        for (int k = i; k < n; ++k) out[pos0 + k] = stage[k];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  for (int j = 0; j < myn; j += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int jr = j + r;
+      if (jr >= myn) break;
+      stage_score(jr, consume(jr, slot[r]));
+      if (jr + 1 == myn || (jr + 1) % kFlushTiles == 0) flush(jr);
+    }
+  }
+  // no DMA may still be writing this workgroup's LDS when it retires
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // fp32 keys (small generic case): one thread per token, fp32 FMAs in order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
@@ -402,9 +719,9 @@ __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
   a.scores[(int64_t)b * a.ld + s] = total;
 }
 
-int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather) {
-  // aim at ~2 resident workgroups per CU over the whole batch
-  const int64_t target = (int64_t)num_cus() * 2;
+int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather, int wg_per_cu) {
+  // aim at one wave of resident workgroups over the whole batch
+  const int64_t target = (int64_t)num_cus() * wg_per_cu;
   const int64_t unit = std::max<int64_t>(kTile * kWaves, gather ? 1 : page_size);
   int64_t chunk = ceil_div(num_req * max_items, target);
   chunk = ceil_div(std::max<int64_t>(chunk, 256), unit) * unit;
@@ -416,10 +733,14 @@ template <int KIND>
 hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   const bool gather = a.positions != nullptr;
   const int max_items = gather ? a.n_pos : a.max_seq_len;
-  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather);
+  const bool dma = KIND == KIND_FP8 && !gather;
+  constexpr int kRingTiles = 2;
+  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, dma ? (kRingTiles >= 4 ? 2 : 3) : 2);
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   const int ps = ilog2(a.page_size);
-  if (gather)
+  if (dma)
+    hipLaunchKernelGGL(scan_fp8_dma_kernel<kRingTiles>, grid, dim3(kThreads), 0, s, a, chunk, ps);
+  else if (gather)
     hipLaunchKernelGGL((scan_kernel<KIND, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   else
     hipLaunchKernelGGL((scan_kernel<KIND, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
