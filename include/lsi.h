@@ -138,7 +138,7 @@ int32_t lsi_topk(const float* scores, int64_t ld, const lsi_batch* batch,
  * Attention of every query head over the selected tokens only (MLI abstract:
  * the layer attends the selection).
  *   kv   LSI_BF16 latent cache with dim == dk == 576, dv == 512,
- *        n_heads a multiple of 64 (V = first dv entries of each row, v must
+ *        n_heads a multiple of 16 (V = first dv entries of each row, v must
  *        be NULL); or LSI_F32 key cache with dk <= 256 plus a separate LSI_F32
  *        value cache v with dim == dv <= 256 (any n_heads <= 1024).
  *   q    [num_req][n_heads][dk], same dtype as kv.

@@ -190,7 +190,7 @@ int32_t validate_attn(const lsi_paged_cache* kv, const lsi_paged_cache* v, const
   LSI_REQUIRE(dk == kv->dim, "dk must equal kv->dim");
   if (kv->dtype == LSI_BF16) {
     LSI_SUPPORT(dk == 576 && dv == 512, "bf16 latent attention needs dk = 576 and dv = 512");
-    LSI_SUPPORT(n_heads % 64 == 0, "bf16 latent attention needs n_heads a multiple of 64");
+    LSI_SUPPORT(n_heads % 16 == 0, "bf16 latent attention needs n_heads a multiple of 16");
     LSI_REQUIRE(v == nullptr, "bf16 latent attention reads V from kv; v must be NULL");
     LSI_REQUIRE(aligned(q, 16) && aligned(out, 16), "q and out must be 16-byte aligned");
   } else if (kv->dtype == LSI_F32) {
@@ -309,7 +309,7 @@ int32_t lsi_topk(const float* scores, int64_t ld, const lsi_batch* batch, int32_
 size_t lsi_sparse_mla_workspace_bytes(int32_t num_req, int32_t n_heads, int32_t dv, int32_t k) {
   if (num_req < 1 || n_heads < 1 || dv < 1 || k < 1) return 0;
   // the bf16 latent path is the only one with scratch
-  if (n_heads % 64 != 0 || dv != 512) return 0;
+  if (n_heads % 16 != 0 || dv != 512) return 0;
   return mla_ws_bytes(num_req, n_heads, dv, k);
 }
 
@@ -330,7 +330,7 @@ size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len, int
   const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
   const size_t tk = topk_ws_bytes(num_req, max_seq_len);
   const size_t ph = align_up((size_t)num_req * k * sizeof(int32_t), kWsAlign);
-  const size_t at = (n_heads % 64 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
+  const size_t at = (n_heads % 16 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
   return sc + tk + ph + at;
 }
 

@@ -2,19 +2,25 @@
 // abstract: the layer attends only the k tokens its indexer kept).
 //
 // bf16 latent MLA (dk = 576 = 512 latent + 64 rope, dv = 512, one latent row
-// shared by all heads): a workgroup owns 64 heads of one request and one slice
-// of the selection, with 8 waves: wave (g4, half) owns heads 16*g4 .. +15;
-// for the scores it takes tile rows 16*half .. +15, for the output it takes
-// value dims 256*half .. +255, so each wave holds a 16 x 256 fp32 output (64
-// registers) and two waves fit per SIMD.  Per 32-row tile the selected rows
-// are gathered through the page table into LDS twice: row-major (K) and
-// transposed for the first 512 columns (V^T).
-//   S^T = K Q^T       v_mfma_f32_16x16x32_bf16, rows on M, heads on N
-//   logits -> LDS     both waves of a head group then read all 32 rows,
-//                     so each computes the same max, probabilities and sum
-//   O^T += V^T P^T    16 M-tiles of 16 value dims, one K-step over 32 rows
-// Softmax runs online in the log2 domain with lazy rescaling.  Splits of the
-// selection are merged with their log-sum-exp by a small combine kernel.
+// shared by all heads).  A workgroup of 4 waves owns 16 heads of one request
+// and one slice of the selection, taken in blocks of 64 rows:
+//   gather    the block's rows go from the pool straight into LDS by DMA
+//             (global_load_lds_dwordx4): one 1 KB instruction per row for the
+//             512 latent dims, one per 8 rows for the 64 rope dims.  Chunk c
+//             (16 bytes) of row r is stored at position c ^ (r % 16) (rope:
+//             c ^ (r % 8)), so the MFMA-layout reads below hit distinct banks.
+//   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, wave w takes rows 16w..+15
+//                      (M), the 16 heads on N, the query in registers
+//   softmax            online over blocks in the log2 domain; block max and
+//                      sum per head are exchanged through LDS
+//   O = P V            wave w takes value dims 128w..+127: P (bf16) from LDS,
+//                      V read with ds_read_b64_tr_b16, which hands each lane
+//                      four rows of one value dim straight from the row-major
+//                      rows in LDS
+// The workgroups of one slice (all head groups) are given block ids that are
+// equal modulo 8, so they run on one XCD and share its L2 for the rows.
+// Splits of the selection are merged with their log-sum-exp by a small
+// combine kernel.
 #include "lsi_internal.hpp"
 
 namespace lsi {
@@ -22,73 +28,81 @@ namespace {
 
 constexpr int kD = 576;
 constexpr int kDV = 512;
-constexpr int kRows = 32;        // rows per tile
-constexpr int kKStride = 584;    // bf16 elements per LDS row of the K tile
-constexpr int kVStride = 40;     // bf16 per LDS row of the V^T tile (32 rows + pad)
-constexpr int kLStride = 36;     // floats per LDS row of the logits tile
-constexpr int kHeadsPerWg = 64;
-constexpr int kMlaThreads = 512;
-constexpr int kMaxSplitRows = 1024;  // selection rows one workgroup handles (k <= 65536 with <= 64 splits)
+constexpr int kMH = 16;                       // heads per workgroup
+constexpr int kMBlk = 64;                     // selection rows per block
+constexpr int kMThreads = 256;
+constexpr int kVRow = 1024;                   // LDS bytes of a row's 512 latent dims
+constexpr int kRopeOff = kMBlk * kVRow;       // rope dims: 8 rows per 1 KB
+constexpr int kKvBytes = kRopeOff + kMBlk * 128;
+constexpr int kPStride = 72;                  // bf16 per LDS row of P (64 rows + pad)
+constexpr int kMaxSplitRows = 1024;           // selection rows one workgroup handles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
-                                                                  int nsplit, float* part_o,
-                                                                  float* part_lse) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDV * kVStride];
-  __shared__ __attribute__((aligned(16))) float Lg[kHeadsPerWg * kLStride];
-  __shared__ int rowidx[kRows];
+template <int OFF>
+__device__ __forceinline__ void dma_row16(uint8_t* lds, const uint8_t* g) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, OFF, 0);
+}
+
+// LDS transpose read: within each 16-lane group, lane 4a + c receives element
+// c of the 8-byte chunks addressed by lanes a, a + 4, a + 8 and a + 12.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
+}
+
+__global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
+                                                                int nsplit, int units, float* part_o,
+                                                                float* part_lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs[kKvBytes];
+  __shared__ __attribute__((aligned(16))) __bf16 Pl[kMH * kPStride];
+  __shared__ float red_m[4][kMH];
+  __shared__ float red_l[4][kMH];
+  __shared__ float alpha_s[kMH];
   __shared__ int rows_all[kMaxSplitRows];
 
-  const int n_hg = a.n_heads / kHeadsPerWg;
+  const int n_hg = a.n_heads / kMH;
   const int bid = blockIdx.x;
-  const int split = bid % nsplit;
-  const int hg = (bid / nsplit) % n_hg;
-  const int b = bid / (nsplit * n_hg);
+  const int u = (bid / (8 * n_hg)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % n_hg;
+  if (u >= units) return;
+  const int b = u / nsplit;
+  const int split = u % nsplit;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g4 = wave >> 1;          // head group of 16 inside the workgroup
-  const int half = wave & 1;         // score rows / value dims half
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int hl = 16 * g4 + n;        // head inside the workgroup
-  const int head = hg * kHeadsPerWg + hl;
+  const int head = hg * kMH + n;               // this lane's head in the S layout
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int r0 = split * rows_per_split;
   const int r1 = min(r0 + rows_per_split, a.k);
+  const int nr = max(0, r1 - r0);
 
-  // query operand: lane holds Q[head][32u + 8g .. 32u + 8g + 7]
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32u + 8g .. +7]
   const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + head) * kD;
   bf16x8 qr[kD / 32];
 #pragma unroll
-  for (int u = 0; u < kD / 32; ++u) qr[u] = *reinterpret_cast<const bf16x8*>(qh + 32 * u + 8 * g);
+  for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
 
-  f32x4 o[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  const float c = a.sm_scale * kLog2e;
-  const __bf16* kvb = static_cast<const __bf16*>(a.kv);
-  const int32_t* idxb = a.idx + (int64_t)b * a.k;
-
-  // Physical rows of the whole slice, resolved once: given by the selection
-  // (phys) or looked up through the page table.
+  // physical rows of the slice, resolved once (given by the selection, or
+  // looked up through the page table); -1 = skip
   const int n_rows_pool = a.num_pages * a.page_size;
-  for (int e = tid; e < r1 - r0; e += kMlaThreads) {
+  for (int e = tid; e < nr; e += kMThreads) {
     int row = -1;
     if (a.phys) {
       row = a.phys[(int64_t)b * a.k + r0 + e];
       if (row >= n_rows_pool) row = -1;
     } else {
-      const int pos = idxb[r0 + e];
+      const int pos = a.idx[(int64_t)b * a.k + r0 + e];
       if (pos >= 0 && pos < L) {
         const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
         if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
@@ -98,148 +112,148 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_bf16_kernel(AttnArgs a, in
   }
   __syncthreads();
 
-  // Gather of one 32-row tile into registers: thread tid owns tile row
-  // tid % 32 and the 16-byte column chunks tid / 32 + 16*it (it = 0..4; the
-  // fifth exists for threads below 256), so the lanes of a half-wave hold 32
-  // different rows of one column and the transposed V writes spread over the
-  // LDS banks.
-  constexpr int kChunks = 5;
-  const int my_row = tid & (kRows - 1);
-  const int my_col0 = tid >> 5;                      // 0..15
-  struct Pre {
-    u32x4 v[kChunks];
-    int row;
-  };
-  auto row_of = [&](int e) -> int { return e < r1 ? rows_all[e - r0] : -1; };
-  auto prefetch = [&](int base) {
-    Pre p;
-    p.row = row_of(base + my_row);
-    const __bf16* src = kvb + (int64_t)(p.row < 0 ? 0 : p.row) * kD;
+  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv);
+  const float c = a.sm_scale * kLog2e;
+  f32x4 o[8];
 #pragma unroll
-    for (int it = 0; it < kChunks; ++it) {
-      const int col = my_col0 + 16 * it;
-      p.v[it] = (p.row >= 0 && col < kD / 8) ? *reinterpret_cast<const u32x4*>(src + col * 8)
-                                              : u32x4{0, 0, 0, 0};
-    }
-    return p;
-  };
-  // two tiles in flight: the current one and the next
-  Pre pa = prefetch(r0), pb = prefetch(r0 + kRows);
+  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // per head n (S layout), the same in every wave
+  float l_run = 0.f;
 
-  for (int base = r0; base < r1; base += kRows) {
-    const Pre cur = pa;
-    pa = pb;
-    if (tid < kRows) rowidx[tid] = cur.row;
+  for (int base = 0; base < nr; base += kMBlk) {
+    const int nb = min(kMBlk, nr - base);
+    // ---- gather: wave w moves rows 16w .. 16w+15 of the block
+    {
+      const int rl = 16 * w + (lane & 15);
+      const int myrow = rl < nb ? rows_all[base + rl] : -1;
 #pragma unroll
-    for (int it = 0; it < kChunks; ++it) {
-      const int col = my_col0 + 16 * it;
-      if (col < kD / 8) {
-        const u32x4 v = cur.v[it];
-        *reinterpret_cast<u32x4*>(&Ks[my_row * kKStride + col * 8]) = v;
-        if (col < kDV / 8) {
-          uint16_t* dst = Vt + (col * 8) * kVStride + my_row;
-          dst[0 * kVStride] = (uint16_t)(v.x & 0xFFFF);
-          dst[1 * kVStride] = (uint16_t)(v.x >> 16);
-          dst[2 * kVStride] = (uint16_t)(v.y & 0xFFFF);
-          dst[3 * kVStride] = (uint16_t)(v.y >> 16);
-          dst[4 * kVStride] = (uint16_t)(v.z & 0xFFFF);
-          dst[5 * kVStride] = (uint16_t)(v.z >> 16);
-          dst[6 * kVStride] = (uint16_t)(v.w & 0xFFFF);
-          dst[7 * kVStride] = (uint16_t)(v.w >> 16);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int rw = __builtin_amdgcn_readlane(myrow, i);
+        const uint8_t* src = kvb + (int64_t)(rw < 0 ? 0 : rw) * (kD * 2) + 16 * (lane ^ ((16 * w + i) & 15));
+        dma_row16<0>(kvs + (16 * w + i) * kVRow, src);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rr = 8 * t + (lane >> 3);                 // row inside the wave's 16
+        const int rw = __shfl(myrow, rr);
+        const int p = lane & 7;
+        const uint8_t* src = kvb + (int64_t)(rw < 0 ? 0 : rw) * (kD * 2) + 2 * kDV + 16 * (p ^ (rr & 7));
+        dma_row16<0>(kvs + kRopeOff + (2 * w + t) * 1024, src);
       }
     }
-    __syncthreads();
-    pb = prefetch(base + 2 * kRows);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // S^T for tile rows 16*half .. +15, this wave's 16 heads
+    // ---- S^T for rows 16w + (0..15): A = K rows from LDS, B = Q^T
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    const __bf16* krow = &Ks[(16 * half + n) * kKStride + 8 * g];
-#pragma unroll
-    for (int u = 0; u < kD / 32; ++u) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(krow + 32 * u);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qr[u], sacc, 0, 0, 0);
-    }
-    // logits of rows 16*half + 4g + r for head hl -> LDS
     {
-      f32x4 xl;
+      const int row = 16 * w + n;                  // A-operand row of this lane
+      const uint8_t* vrow = kvs + row * kVRow;
+      const uint8_t* rrow = kvs + kRopeOff + (row >> 3) * 1024 + (row & 7) * 128;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        xl[r] = rowidx[16 * half + 4 * g + r] >= 0 ? sacc[r] * c : -INFINITY;
-      *reinterpret_cast<f32x4*>(&Lg[hl * kLStride + 16 * half + 4 * g]) = xl;
-    }
-    __syncthreads();
-    // every wave of the head group reads rows 8g .. 8g+7 of its heads
-    float x[8];
-    {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(&Lg[hl * kLStride + 8 * g]);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(&Lg[hl * kLStride + 8 * g + 4]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = x0[r];
-        x[4 + r] = x1[r];
+      for (int t = 0; t < kD / 32; ++t) {
+        bf16x8 av;
+        if (t < 16) {
+          av = *reinterpret_cast<const bf16x8*>(vrow + 16 * ((4 * t + g) ^ (row & 15)));
+        } else {
+          av = *reinterpret_cast<const bf16x8*>(rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7)));
+        }
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qr[t], sacc, 0, 0, 0);
       }
     }
-    float tmax = x[0];
+    // lane (n, g) holds S^T[row 16w + 4g + r][head n]
+    float x[4];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // Lazy rescaling: the reference max only moves when the tile max exceeds
+    for (int r = 0; r < 4; ++r) {
+      const int rl = 16 * w + 4 * g + r;
+      const bool ok = rl < nb && rows_all[base + rl] >= 0;
+      x[r] = ok ? sacc[r] * c : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) red_m[w][n] = mx;
+    __syncthreads();
+    const float bmax = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
+    // Lazy rescaling: the reference max only moves when the block max exceeds
     // it by more than 8 (log2 units); probabilities then stay below 2^8.
     const bool first = m_run == -INFINITY;
-    const float m_new = (first || tmax > m_run + 8.f) ? fmaxf(m_run, tmax) : m_run;
-    float p[8];
-    float alpha = 1.f;
-    if (m_new == -INFINITY) {
+    const float m_new = (first || bmax > m_run + 8.f) ? fmaxf(m_run, bmax) : m_run;
+    const float alpha = (first || m_new == m_run) ? (first ? 0.f : 1.f) : exp2f(m_run - m_new);
+    float p[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    } else {
-      if (!first) alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = exp2f(x[i] - m_new);
+    for (int r = 0; r < 4; ++r) p[r] = m_new == -INFINITY ? 0.f : exp2f(x[r] - m_new);
+    float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    if (g == 0) red_l[w][n] = ps;
+    {
+      const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      *reinterpret_cast<u32x2*>(&Pl[n * kPStride + 16 * w + 4 * g]) = pw;
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) psum += p[i];
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[j] *= alpha;
-    }
-    const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-    // O^T[dims 256*half + 16j + ..][head] += V^T P^T over the 32 rows
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const bf16x8 av =
-          *reinterpret_cast<const bf16x8*>(&Vt[(256 * half + 16 * j + n) * kVStride + 8 * g]);
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[j], 0, 0, 0);
-    }
+    if (w == 0 && g == 0) alpha_s[n] = alpha;
     __syncthreads();
+    l_run = l_run * (first ? 0.f : alpha) + ((red_l[0][n] + red_l[1][n]) + (red_l[2][n] + red_l[3][n]));
+    m_run = m_new;
+
+    // ---- O[heads][dims 128w ..] += P V; lane (dim n, g) holds heads 4g + r
+    {
+      f32x4 al;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = alpha_s[4 * g + r];
+      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] *= al;
+      }
+    }
+    const int s16 = lane & 15;                 // source lane of the transpose reads
+    const int ja = s16 >> 2;                   // row offset within the group of 4
+    const int aa = s16 & 3;                    // 4-dim column group
+#pragma unroll 1
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pl[n * kPStride + 32 * kk + 8 * g]);
+      const int ra = 32 * kk + 8 * g + ja;     // rows ra and ra + 4
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ch = (128 * w + 16 * t + 4 * aa) >> 3;    // 16-byte chunk of the dim group
+        const int hb = 8 * (aa & 1);
+        const s16x4 v0 = lds_read_tr16(kvs + ra * kVRow + 16 * (ch ^ (ra & 15)) + hb);
+        const s16x4 v1 = lds_read_tr16(kvs + (ra + 4) * kVRow + 16 * (ch ^ ((ra + 4) & 15)) + hb);
+        const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        bf16x8 vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vb[e] = __builtin_bit_cast(__bf16, vv[e]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // the block's LDS is refilled next
   }
 
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse2 = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
-  const int64_t bh = (int64_t)b * a.n_heads + head;
-  // lane holds O[head][256*half + 16j + 4g + r]
-  if (nsplit == 1) {
-    __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV + 256 * half;
+  // ---- results: per-head statistics to the output layout through LDS
+  if (w == 0 && g == 0) {
+    red_m[0][n] = m_run;
+    red_l[0][n] = l_run;
+  }
+  __syncthreads();
+  const int dim0 = 128 * w + n;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      u32x2 w2 = {pack_bf16x2(o[j][0] * inv, o[j][1] * inv), pack_bf16x2(o[j][2] * inv, o[j][3] * inv)};
-      *reinterpret_cast<u32x2*>(ob + 16 * j + 4 * g) = w2;
+  for (int r = 0; r < 4; ++r) {
+    const int hl = 4 * g + r;
+    const float lr = red_l[0][hl];
+    const float mr = red_m[0][hl];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    const float lse2 = lr > 0.f ? mr + log2f(lr) : -INFINITY;
+    const int64_t bh = (int64_t)b * a.n_heads + hg * kMH + hl;
+    if (nsplit == 1) {
+      __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV + dim0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ob[16 * t] = (__bf16)(o[t][r] * inv);
+      if (w == 0 && n == 0) a.lse[bh] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    } else {
+      float* po = part_o + (bh * nsplit + split) * kDV + dim0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) po[16 * t] = o[t][r] * inv;
+      if (w == 0 && n == 0) part_lse[bh * nsplit + split] = lse2;
     }
-    if (g == 0 && half == 0) a.lse[bh] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
-  } else {
-    float* po = part_o + (bh * nsplit + split) * kDV + 256 * half;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) *reinterpret_cast<f32x4*>(po + 16 * j + 4 * g) = o[j] * inv;
-    if (g == 0 && half == 0) part_lse[bh * nsplit + split] = lse2;
   }
 }
 
@@ -354,12 +368,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 int pick_nsplit(int num_req, int n_heads, int k) {
-  const int groups = num_req * (n_heads / kHeadsPerWg);
-  const int tiles = (k + kRows - 1) / kRows;
-  // ~2 workgroups per CU, at least 4 tiles per split
+  const int groups = num_req * (n_heads / kMH);
+  const int blocks = (k + kMBlk - 1) / kMBlk;
+  // ~2 workgroups per CU, at least one block per split
   int ns = (int)ceil_div((int64_t)num_cus() * 2, std::max(groups, 1));
-  ns = std::min(ns, std::max(1, tiles / 2));
-  ns = std::max(ns, (int)ceil_div(tiles, kMaxSplitRows / kRows));
+  ns = std::min(ns, std::max(1, blocks));
+  ns = std::max(ns, (int)ceil_div(blocks, kMaxSplitRows / kMBlk));
   return std::min(std::max(ns, 1), 64);
 }
 
@@ -373,14 +387,15 @@ size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k) {
 
 hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
   const int ns = pick_nsplit(a.num_req, a.n_heads, a.k);
-  const int tiles = (a.k + kRows - 1) / kRows;
-  const int rows_per_split = (int)ceil_div(tiles, ns) * kRows;
+  const int blocks = (a.k + kMBlk - 1) / kMBlk;
+  const int rows_per_split = (int)ceil_div(blocks, ns) * kMBlk;
   const int nsplit = (int)ceil_div(a.k, rows_per_split);
   float* part_o = static_cast<float*>(a.ws);
   float* part_lse = part_o ? part_o + (size_t)a.num_req * a.n_heads * nsplit * kDV : nullptr;
-  const int grid = a.num_req * (a.n_heads / kHeadsPerWg) * nsplit;
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMlaThreads), 0, s, a, rows_per_split, nsplit,
-                     part_o, part_lse);
+  const int units = a.num_req * nsplit;
+  const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / kMH);
+  hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, a, rows_per_split, nsplit,
+                     units, part_o, part_lse);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_req * a.n_heads), dim3(kDV / 4), 0, s, a,
                        nsplit, part_o, part_lse);

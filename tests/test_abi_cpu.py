@@ -99,7 +99,7 @@ def test_attention_validation(L):
         return L.lsi_sparse_mla_decode(C.byref(kvc), None if v is None else C.byref(v),
                                        C.byref(b), q, H, dk, dv, 0x6000, 2048, sm,
                                        0x7000, 0x8000, 0x100000, 1 << 30, None)
-    assert call(kv, H=96) == lsi.ERR_UNSUPPORTED
+    assert call(kv, H=72) == lsi.ERR_UNSUPPORTED           # not a multiple of 16
     assert call(kv, dv=256) == lsi.ERR_UNSUPPORTED
     assert call(kv, sm=0.0) == lsi.ERR_INVALID_ARG
     assert call(kv, sm=float("nan")) == lsi.ERR_INVALID_ARG

@@ -206,6 +206,56 @@ def test_mla_single_row_and_empty_selection():
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
+def test_mla_head_counts_and_partial_blocks():
+    # 48 heads (three 16-head groups), k = 1000 (a partial 64-row block), -1 padding
+    lens = (3000, 900, 2500)
+    wl = synth.scaled(synth.DSA_128K, seed=13, seq_lens=lens, num_req=3, n_planted=32, k=1000,
+                      n_heads=48)
+    di = synth.make_decode_inputs(wl, device=DEV, with_attn=True)
+    ov = OracleView(di)
+    _, req, kv, _ = objs(di)
+    rng = np.random.default_rng(5)
+    k = 1000
+    idx = torch.full((3, k), -1, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        n = min(L, k) - 7 * b
+        idx[b, :n] = torch.from_numpy(rng.choice(L, size=n, replace=False).astype(np.int32))
+    out, lse = lsi.sparse_mla_decode(kv, None, req, di.q_attn, idx.to(DEV), di.wl.sm_scale, 512)
+    torch.cuda.synchronize()
+    for b in range(3):
+        sel = idx[b][idx[b] >= 0].numpy()
+        ro, rl = ov.attention(b, sel)
+        print(b, check_attention(out[b].float().cpu().numpy(), ro, f"mla48 {b}"))
+        assert np.allclose(lse[b].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
+
+
+def test_mla_late_dominant_rows_rescale_the_running_softmax():
+    # four requests: each workgroup takes two 64-row blocks of its slice; the
+    # rows in the second half of every 128-entry slice get 6x larger latent
+    # rows, so their logits exceed the first block's maximum by far
+    lens = (3000,) * 4
+    di = small_dsa(lens, seed=17, k=2048)
+    _, req, kv, _ = objs(di)
+    rng = np.random.default_rng(6)
+    k = 2048
+    idx = np.stack([rng.choice(3000, size=k, replace=False) for _ in lens]).astype(np.int32)
+    pt = di.page_table.cpu().numpy()
+    kvflat = di.kv.view(-1, di.kv.shape[-1])
+    for b in range(len(lens)):
+        late = idx[b][(np.arange(k) % 128) >= 96]
+        phys = torch.from_numpy(pt[b][late // synth.PAGE].astype(np.int64) * synth.PAGE
+                                + late % synth.PAGE).to(DEV)
+        kvflat[phys] = (kvflat[phys].float() * 6.0).to(kvflat.dtype)
+    ov = OracleView(di)
+    out, lse = lsi.sparse_mla_decode(kv, None, req, di.q_attn, torch.from_numpy(idx).to(DEV),
+                                     di.wl.sm_scale, 512)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        ro, rl = ov.attention(b, idx[b])
+        print(b, check_attention(out[b].float().cpu().numpy(), ro, f"mla rescale {b}"))
+        assert np.allclose(lse[b].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
+
+
 def test_attention_f32_tiny_case():
     di = synth.make_decode_inputs(synth.TINY_F32, device=DEV)
     ov = OracleView(di)
