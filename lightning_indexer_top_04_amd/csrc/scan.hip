@@ -410,6 +410,22 @@ __device__ __forceinline__ void lds_read_tile(u32x4 (&kr)[4], const uint8_t* slo
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// The tile reads plus one float at byte offset `so` of the slot (its scale),
+// all complete when the statement ends: the slot may be refilled right after.
+__device__ __forceinline__ void lds_read_tile_scale(u32x4 (&kr)[4], float& sc, const uint8_t* slot,
+                                                    const uint32_t (&rd)[4], uint32_t so) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)slot;
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %6\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %8\n\t"
+      "ds_read_b32 %4, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(sc)
+      : "v"(base + rd[0]), "v"(base + rd[1]), "v"(base + rd[2]), "v"(base + rd[3]), "v"(base + so)
+      : "memory");
+}
 __device__ __forceinline__ float lds_read_f32(const uint8_t* p) {
   const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
   float v;
@@ -478,19 +494,23 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   for (int i = 0; i < 4; ++i) rd[i] = m * 128 + 16 * ((4 * h + i) ^ (m & 7));
   const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
 
-  // Every refill is issued, clamped to the wave's last tile, so the count of
-  // vector-memory operations between a tile's DMA and its use is the same at
-  // every step: RING - 1 later tiles of 5 DMAs each (four 1 KB key moves and
-  // one for the 32 scales, which lanes 32..63 copy a second time).  vmcnt
-  // counts loads in issue order, so waiting until at most that many are
-  // outstanding means the tile has landed in LDS.  (A wave without tiles
-  // fetches the slice's first tile into its own slots, which keeps the waits
-  // of every wave the same.)
+  // Every refill is issued, so the count of vector-memory operations between
+  // a tile's DMA and its use is the same at every step: RING - 1 later tiles
+  // of 5 DMAs each (four 1 KB key moves and one for the 32 scales, which
+  // lanes 32..63 copy a second time).  vmcnt counts loads in issue order, so
+  // waiting until at most that many are outstanding means the tile has landed
+  // in LDS.  Refills past the wave's last tile (and every fill of a wave
+  // without tiles) read pool row 0, which all of them share in L2, into a
+  // slot that is never consumed.  A slot is refilled only after every read of
+  // it has completed (its reads end with their own wait).
   auto issue = [&](int j, uint8_t* slot) {
-    const int t0 = (myn > 0 ? my0 + min(j, myn - 1) : 0) * kTile;
-    const int page = __builtin_amdgcn_readfirstlane(pages[t0 >> page_shift]);
-    const bool ok = page >= 0 && page < a.num_pages;
-    const int64_t row0 = ok ? (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1)) : 0;
+    int64_t row0 = 0;
+    if (j < myn) {
+      const int t0 = (my0 + j) * kTile;
+      const int page = __builtin_amdgcn_readfirstlane(pages[t0 >> page_shift]);
+      if (page >= 0 && page < a.num_pages)
+        row0 = (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1));
+    }
     const uint8_t* g = keys + row0 * kDim + goff;
     asm volatile("" ::: "memory");
     lds_dma16<0>(slot, g);
@@ -607,8 +627,8 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   auto consume = [&](int j, uint8_t* slot) -> float {
     wait_ring_tile<RING>();
     u32x4 kr[4];
-    lds_read_tile(kr, slot, rd);
-    const float scale = *reinterpret_cast<const float*>(slot + kTileBytes + 4 * lane);
+    float scale;
+    lds_read_tile_scale(kr, scale, slot, rd, kTileBytes + 4 * lane);
     const int page = pages[((my0 + j) * kTile) >> page_shift];
     const bool ok = page >= 0 && page < a.num_pages;
     f32x16 acc0 = {};

@@ -97,6 +97,36 @@ def test_scan_is_bitwise_invariant_to_page_placement_and_repeatable():
     assert torch.equal(s1[:, :3000], s2[:, :3000])
 
 
+def test_scan_repeatable_over_many_launches_into_poisoned_outputs():
+    # every launch writes every score, and equal inputs give bitwise equal
+    # scores: the key ring in LDS is refilled only after each slot's reads
+    # (tiles and scales) are complete; NaN-filled outputs expose any score a
+    # launch leaves unwritten or computes from a refilled slot
+    di1 = small_dsa([131072], seed=19, attn=False)
+    di8 = small_dsa([131072] * 4 + [70000, 50001, 8192, 33], seed=23, attn=False)
+    cases = []
+    for di in (di1, di8):
+        ik, req, _, _ = objs(di)
+        B = di.seq_lens.numel()
+        ld = 131072
+        cases.append((ik, req, di, B, ld))
+    refs = []
+    for ik, req, di, B, ld in cases:
+        s = torch.full((B, ld), float("nan"), device=DEV)
+        lsi.index_scores(ik, req, di.q_idx, di.w, scores=s)
+        refs.append(s.cpu())
+    for it in range(60):
+        ik, req, di, B, ld = cases[it % 2]
+        s = torch.full((B, ld), float("nan"), device=DEV)
+        lsi.index_scores(ik, req, di.q_idx, di.w, scores=s)
+        got = s.cpu()
+        ref = refs[it % 2]
+        for b in range(B):
+            L = int(di.seq_lens[b])
+            assert not torch.isnan(got[b, :L]).any(), (it, b)
+            assert torch.equal(got[b, :L], ref[b, :L]), (it, b)
+
+
 def test_scan_out_of_range_page_scores_minus_inf():
     di = small_dsa([640], n_planted=0, attn=False)
     pt = di.page_table.clone()
