@@ -1,6 +1,6 @@
 """Benchmark of the DSA-style decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets R] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets R] [--no-cpu] [--no-extra]
 
 Workload: one request with 131072 cached tokens (64 indexer heads x 128,
 fp8 E4M3FN keys with per-token scales, bf16 queries; k = 2048; sparse MLA with
@@ -15,8 +15,10 @@ loop would run them; the timed region covers exactly K steps.
 Printed (one JSON line): tokens/s = 131072 * steps / time (whole step timed,
 inputs resident in HBM), decode steps/s, per-phase averages from HIP events on
 the launch stream, the scan's roofline (algorithmic 132 B per token against
-8 TB/s), a sustained scan of 32 x 128K tokens in one launch, and the CPU
-oracle's throughput on a bounded sample of the same step.
+8 TB/s), a sustained scan of 32 x 128K tokens in one launch, the CPU
+oracle's throughput on a bounded sample of the same step, and (unless
+--no-extra) the ragged 64-request decode step, the two-stage compact-key
+search at 512K and the prefill indexer chunk, each against its own roofline.
 """
 from __future__ import annotations
 
@@ -43,6 +45,8 @@ def parse():
     p.add_argument("--sets", type=int, default=32)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the ragged-batch, two-stage and prefill measurements")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 512 MiB device copy (known traffic) for counter scaling")
     return p.parse_args()
@@ -223,6 +227,18 @@ def main():
                           "frac": step_bytes / (HBM_PEAK_GBS * 1e3) / (ms_step * 1e3)},
     }
 
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(di, wl, L, args.cpu_seconds)
+
+    if not args.no_extra:
+        # the other workloads of the pages' configurations, measured on the
+        # same device after the 128K sets are released
+        del g_all, g_rem, g_scan, g_topk, g_mla, di, scores, scores_all, sc_rows, idx_sel
+        del q_idx, w, q_attn, reqs, ik, kv, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other_workloads(lsi, synth, torch, dev)
+
     if args.calib_copy:
         # a plain elementwise copy of known size (512 MiB read, 512 MiB
         # written per launch) for scaling the FETCH_SIZE / WRITE_SIZE counters
@@ -234,9 +250,122 @@ def main():
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = 512 << 20
 
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(di, wl, L, args.cpu_seconds)
     print(json.dumps(res))
+
+
+def other_workloads(lsi, synth, torch, dev):
+    """Throughput of the ragged 64-request decode step, the two-stage
+    compact-key search at 512K and the prefill indexer chunk, each against
+    its own roofline (HBM bytes, or bf16 MFMA flops for the prefill)."""
+    out = {}
+
+    def graph_ms(fn, n=8, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        e1.synchronize()
+        del g
+        return e0.elapsed_time(e1) / (reps * n)
+
+    # ragged batch: 64 requests, L ~ U{10000..195000}
+    wl = synth.BATCH_RAGGED
+    di = synth.make_decode_inputs(wl, device=dev)
+    seq = di.seq_lens
+    maxL = int(seq.max().item())
+    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    kv = lsi.Cache(di.kv, None, "bf16", 576)
+    req = lsi.Requests(seq, di.page_table, maxL)
+    B, k, H, dv = seq.numel(), 2048, 128, 512
+    idx = torch.empty(B, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, dtype=torch.int32, device=dev)
+    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(lsi.decode_step_workspace_bytes(B, maxL, k, H, dv), dtype=torch.uint8,
+                     device=dev)
+    t = graph_ms(lambda: lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k,
+                                         wl.sm_scale, dv, out=o, lse=lse, idx=idx, count=cnt,
+                                         ws=ws), n=2, reps=5)
+    tokens = int(seq.sum().item())
+    byts = tokens * BYTES_PER_TOKEN + B * (k * 576 * 2 + H * 576 * 2 + H * dv * 2)
+    out["ragged_decode_b64"] = {
+        "requests": B, "tokens": tokens, "us_per_step": t * 1e3,
+        "tokens_per_s": tokens / (t * 1e-3), "steps_per_s": 1e3 / t,
+        "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
+                     "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    del di, ik, kv, req, idx, cnt, o, lse, ws
+    torch.cuda.empty_cache()
+
+    # two-stage compact-key search at 524288 tokens: int4 scan, 8192
+    # candidates, exact fp8 rescoring, 2048 kept
+    wl = synth.TWO_STAGE_512K
+    di = synth.make_decode_inputs(wl, device=dev, with_int4=True, with_attn=False)
+    L = 524288
+    ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, L)
+    t = graph_ms(lambda: lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048), n=4)
+    byts = L * 68 + 8192 * BYTES_PER_TOKEN
+    out["two_stage_l524288"] = {
+        "tokens": L, "us_per_call": t * 1e3, "tokens_per_s": L / (t * 1e-3),
+        "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
+                     "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    del di, ik8, ik4, req
+    torch.cuda.empty_cache()
+
+    # prefill chunk: 4096 queries over 65536 history + the chunk, causal
+    wl = synth.PREFILL_CHUNK
+    pi = synth.make_prefill_inputs(wl, device=dev)
+    Hh = pi.hist_len
+    hist_k_host = pi.keys[:Hh].cpu().pin_memory()
+    hist_s_host = pi.scale[:Hh].cpu().pin_memory()
+    hist_k_dev = pi.keys[:Hh].contiguous()
+    hist_s_dev = pi.scale[:Hh].contiguous()
+    chunk_k = pi.keys[Hh:].contiguous()
+    chunk_s = pi.scale[Hh:].contiguous()
+    copy_stream = torch.cuda.Stream()
+    T = pi.T
+    pairs = T * Hh + T * (T + 1) // 2
+    flops = pairs * 64 * 128 * 2
+
+    def prefill_ms(hk, hs, reps=5):
+        lsi.prefill_index_topk(hk, hs, chunk_k, chunk_s, pi.q, pi.w, 2048, 8192,
+                               copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            lsi.prefill_index_topk(hk, hs, chunk_k, chunk_s, pi.q, pi.w, 2048, 8192,
+                                   copy_stream=copy_stream)
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_host = prefill_ms(hist_k_host, hist_s_host)
+    t_dev = prefill_ms(hist_k_dev, hist_s_dev)
+    out["prefill_t4096_h65536"] = {
+        "queries": T, "pairs": pairs, "ms_history_from_pinned_host": t_host,
+        "ms_history_on_device": t_dev,
+        "roofline": {"bound": "mfma", "useful_flops": flops, "dtype": "bf16",
+                     "achieved_TFLOP_s": flops / (t_dev * 1e-3) / 1e12, "peak": 2500.0,
+                     "frac": flops / (t_dev * 1e-3) / 1e12 / 2500.0,
+                     "note": "indexer scores of every (query, visible token) pair plus the "
+                             "per-query top-k, history on the device; the pinned-host "
+                             "figure includes the block copies over PCIe"}}
+    return out
 
 
 def measured_traffic():
