@@ -2,20 +2,26 @@
 // abstract: keep the k=2048 highest-scoring tokens of the whole cache).
 //
 // Radix select over the order-preserving 32-bit key of each score, never a
-// sort.  Three launches, handing over only at kernel boundaries (on this
-// GPU an agent-scope fence in hundreds of workgroups costs tens of
-// microseconds, so no workgroup waits for or signals another one):
+// sort.  Long rows take three launches, handing over only at kernel
+// boundaries (on this GPU an agent-scope fence in hundreds of workgroups
+// costs tens of microseconds, so no workgroup waits for or signals another):
 //   1. topk_hist: each workgroup builds an LDS histogram of the top 12 key
-//      bits of its slice and adds the non-empty bins to the row's global
-//      histogram (a few dozen atomics per hot bin).
+//      bits of its 4096-position chunk, stores the chunk's suffix counts
+//      (elements at or above each bin) and adds the non-empty bins to the
+//      row's global histogram.
 //   2. topk_select: each workgroup reads the row histogram, finds the bin
-//      that holds the k-th largest key, writes the keys above it straight to
-//      the output and collects the bin's members; slots come from a block
-//      scan and one atomic per workgroup and counter.
-//   3. topk_refine: one workgroup per row refines the candidates in LDS:
-//      12 more key bits, the last 8 key bits, then positions (ascending) for
-//      exact ties; each stage is a 4096-bin LDS histogram and an ordered
-//      in-place compaction.  It also writes the padding and the count.
+//      that holds the k-th largest key, and learns from the earlier chunks'
+//      suffix counts where its own winners (keys above that bin) and
+//      candidates (keys in it) start; it writes its winners straight to the
+//      output, with their physical rows, and its candidates (slot, key) to
+//      the row's candidate list.  No atomics, nothing to wait for.
+//   3. topk_refine: one workgroup per row finds the threshold bin again,
+//      loads the candidates into LDS and refines them: 12 more key bits,
+//      the last 8 key bits, then positions (ascending) for exact ties; each
+//      stage is a 4096-bin LDS histogram and an ordered compaction.  It also
+//      writes the padding and the count.
+// Batches of rows (as many as compute units) and short rows take one launch
+// of one workgroup per row instead (topk_row).
 #include "lsi_internal.hpp"
 #include "topk_common.hpp"
 
@@ -25,9 +31,8 @@ namespace {
 using namespace topk;
 
 constexpr int kBlock = 512;
-constexpr int kPer = 8;                  // elements per thread in topk_select
-constexpr int kSelChunk = kBlock * kPer;  // 4096
-constexpr int kLdsCand = 4096;           // candidates refined in LDS
+constexpr int kLdsCand = 16384;          // candidates refined in LDS
+constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   int L;
@@ -41,17 +46,61 @@ __device__ __forceinline__ int out_value(const TopkArgs& a, int r, int slot) {
   return a.map ? a.map[(int64_t)r * a.map_ld + slot] : slot;
 }
 
+// Page and in-page offset of position pos >= 0 (shifts for the usual
+// power-of-two page sizes: a 32-bit division is dozens of instructions).
+__device__ __forceinline__ void split_pos(int pos, int ps, int& page, int& off) {
+  if ((ps & (ps - 1)) == 0) {
+    page = pos >> (__ffs(ps) - 1);
+    off = pos & (ps - 1);
+  } else {
+    page = pos / ps;
+    off = pos - page * ps;
+  }
+}
+
+// Physical cache row of logical position pos of row r (-1 for none).
+__device__ __forceinline__ int phys_of(const TopkArgs& a, int r, int pos) {
+  if (pos < 0) return -1;
+  int pg, off;
+  split_pos(pos, a.page_size, pg, off);
+  const int page = a.page_table[(int64_t)r * a.max_pages + pg];
+  return (unsigned)page < (unsigned)a.num_pages ? page * a.page_size + off : -1;
+}
+
 // Write kept position `pos` at output slot `o` of row r (and its physical
 // cache row when requested).
 __device__ __forceinline__ void emit(const TopkArgs& a, int r, int o, int pos) {
   a.idx[(int64_t)r * a.k + o] = pos;
-  if (a.phys) {
-    int row = -1;
-    if (pos >= 0) {
-      const int page = a.page_table[(int64_t)r * a.max_pages + pos / a.page_size];
-      if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+  if (a.phys) a.phys[(int64_t)r * a.k + o] = phys_of(a, r, pos);
+}
+
+// Output slots o0 .. o0+n-1 of row r receive out_value(get(i)) (get returns
+// a slot index, or -1 for padding).  The loads of kGather slots per thread
+// are all issued before the first store, so a batch costs one round trip
+// per dependent load instead of one per element.
+constexpr int kGather = 4;
+template <int NT, class Get>
+__device__ void emit_range(const TopkArgs& a, int r, uint32_t o0, uint32_t n, Get get) {
+  for (uint32_t b = threadIdx.x; b < n; b += NT * kGather) {
+    int v[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const uint32_t i = b + u * NT;
+      v[u] = i < n ? get(i) : -1;
     }
-    a.phys[(int64_t)r * a.k + o] = row;
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) v[u] = v[u] >= 0 ? out_value(a, r, v[u]) : -1;
+    int pr[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) pr[u] = a.phys ? phys_of(a, r, v[u]) : -1;
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const uint32_t i = b + u * NT;
+      if (i < n && o0 + i < (uint32_t)a.k) {
+        a.idx[(int64_t)r * a.k + o0 + i] = v[u];
+        if (a.phys) a.phys[(int64_t)r * a.k + o0 + i] = pr[u];
+      }
+    }
   }
 }
 
@@ -61,68 +110,104 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a, int chunk) {
+static_assert(kBins == 8 * kBlock, "tiling");
+
+// PER positions per thread: chunks of PER * kBlock positions
+template <int PER>
+__global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
+  constexpr int kChunk = PER * kBlock;
   __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t tmp[32];
   const int r = blockIdx.y;
+  const int c = blockIdx.x;
   const int L = row_len(a, r);
   if (L <= a.k) return;
-  const int begin = blockIdx.x * chunk;
+  const int begin = c * kChunk;
   if (begin >= L) return;
-  const int end = min(begin + chunk, L);
+  const int end = min(begin + kChunk, L);
+  const float* row = a.scores + (int64_t)r * a.ld;
+  // the chunk's loads go out first (indexes past the end are clamped and not
+  // counted), so they cost one round trip
+  uint32_t d[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) d[j] = float_key(row[min(begin + j * kBlock + (int)threadIdx.x, end - 1)]) >> 20;
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
   __syncthreads();
-  const float* row = a.scores + (int64_t)r * a.ld;
-  for (int i = begin + threadIdx.x; i < end; i += kBlock)
-    atomicAdd(&hist[float_key(row[i]) >> 20], 1u);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) atomicAdd(&hist[d[j]], begin + j * kBlock + (int)threadIdx.x < end ? 1u : 0u);
   __syncthreads();
-  uint32_t* gh = carve(a.ws, a.num_req).hist + (size_t)r * kBins;
+  const Ws ws = carve(a.ws, a.num_req, a.max_len);
+  // the chunk's suffix counts: thread t owns bins 4095-8t down to 4088-8t
+  uint32_t v[8], run = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = hist[kBins - 1 - (8 * (int)threadIdx.x + i)];
+    run += v[i];
+  }
+  uint32_t tot;
+  uint32_t acc = block_excl_scan<kBlock>(run, tmp, &tot);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc += v[i];
+    v[i] = acc;
+  }
+  // bins 4088-8t .. 4095-8t ascending, 16-bit counts, one 16-byte store
+  uint4* suf = reinterpret_cast<uint4*>(ws.suf + ((size_t)r * ws.nchunk + c) * kBins + kBins - 8 - 8 * (int)threadIdx.x);
+  *suf = make_uint4(v[7] | (v[6] << 16), v[5] | (v[4] << 16), v[3] | (v[2] << 16), v[1] | (v[0] << 16));
+  // and the row's histogram: the non-empty bins
+  uint32_t* gh = ws.hist + (size_t)r * kBins;
   for (int i = threadIdx.x; i < kBins; i += kBlock)
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
-// The single-workgroup refinement of a row's candidate list.
-__device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st, uint32_t* hist,
-                           uint32_t* tmp, uint32_t* lkey, int32_t* lslot) {
+// The single-workgroup refinement of a row's candidate list: n candidates
+// (positions in `list`, or already in LDS as (key, position) pairs), of which
+// `need` are still to be taken, after out_pos winners already written.
+// The candidates share every key bit above the lowest key_bits of
+// (key - kbase); lkey holds (key - kbase) when they sit in LDS.
+template <int NT, int CAP>
+__device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need, uint32_t out_pos,
+                             int32_t* list, bool in_lds, uint32_t* hist, uint32_t* tmp,
+                             uint32_t* lkey, int32_t* lslot, int key_bits, uint32_t kbase) {
   const float* row = a.scores + (int64_t)r * a.ld;
-  int32_t* list = ws.cand + (size_t)r * a.max_len;
-  uint32_t n = st[ST_CAND];
-  uint32_t need = st[ST_NEED];
-  uint32_t out_pos = st[ST_OUT];
-  bool in_lds = false;
-  // stages: key bits [19:8], key bits [7:0], then position bits
-  // [31:20], [19:8], [7:0] ascending
+  // stages: the unresolved key bits, at most 12 at a time (two stages for up
+  // to 24 bits), then position bits [31:20], [19:8], [7:0] ascending
+  const int kb_hi = key_bits > 12 ? 12 : key_bits;
+  const int kb_lo = key_bits > 12 ? key_bits - 12 : 0;
   for (int stage = 0; stage < 5 && need > 0 && n > 0; ++stage) {
     if (n <= need) break;
-    if (!in_lds && n <= (uint32_t)kLdsCand) {
-      for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
+    const bool by_key = stage < 2;
+    const int nbits = stage == 0 ? kb_hi : stage == 1 ? kb_lo : stage == 4 ? 8 : 12;
+    if (nbits == 0) continue;
+    if (!in_lds && n <= (uint32_t)CAP) {
+      for (uint32_t i = threadIdx.x; i < n; i += NT) {
         const int slot = list[i];
         lslot[i] = slot;
-        lkey[i] = float_key(row[slot]);
+        lkey[i] = float_key(row[slot]) - kbase;
       }
       in_lds = true;
       __syncthreads();
     }
-    const bool by_key = stage < 2;
-    const int shift = stage == 0 ? 8 : stage == 1 ? 0 : stage == 2 ? 20 : stage == 3 ? 8 : 0;
-    const uint32_t mask = (stage == 1 || stage == 4) ? 0xFFu : 0xFFFu;
+    const int shift = stage == 0 ? kb_lo : stage == 1 ? 0 : stage == 2 ? 20 : stage == 3 ? 8 : 0;
+    const uint32_t mask = (1u << nbits) - 1u;
     auto value = [&](uint32_t i, int& slot) -> uint32_t {
       slot = in_lds ? lslot[i] : list[i];
       if (!by_key) return (uint32_t)out_value(a, r, slot);
-      return in_lds ? lkey[i] : float_key(row[slot]);
+      return in_lds ? lkey[i] : float_key(row[slot]) - kbase;
     };
-    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
+    for (uint32_t i = threadIdx.x; i < n; i += NT) {
       int slot;
       const uint32_t v = value(i, slot);
       atomicAdd(&hist[(v >> shift) & mask], 1u);
     }
     __syncthreads();
     uint32_t better;
-    const int bin = find_threshold<kBlock>(hist, need, by_key, tmp, &better);
+    const int bin = find_threshold<NT>(hist, need, by_key, tmp, &better);
     // ordered pass: winners (better than bin) go out, equal ones stay
     uint32_t keep = 0;
-    for (uint32_t base = 0; base < n; base += kBlock) {
+    for (uint32_t base = 0; base < n; base += NT) {
       const uint32_t i = base + threadIdx.x;
       int slot = -1;
       uint32_t v = 0, flag_win = 0, flag_eq = 0;
@@ -133,7 +218,7 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
         flag_win = by_key ? (d > bin) : (d < bin);
       }
       uint32_t tot;
-      const uint32_t pre = block_excl_scan<kBlock>(flag_win | (flag_eq << 16), tmp, &tot);
+      const uint32_t pre = block_excl_scan<NT>(flag_win | (flag_eq << 16), tmp, &tot);
       if (flag_win && out_pos + (pre & 0xFFFF) < (uint32_t)a.k)
         emit(a, r, out_pos + (pre & 0xFFFF), out_value(a, r, slot));
       if (flag_eq) {
@@ -154,73 +239,135 @@ __device__ void refine_row(const TopkArgs& a, int r, const Ws& ws, uint32_t* st,
   }
   // whatever remains is taken whole (n <= need here)
   const uint32_t take = min(n, need);
-  for (uint32_t i = threadIdx.x; i < take && out_pos + i < (uint32_t)a.k; i += kBlock)
-    emit(a, r, out_pos + i, out_value(a, r, in_lds ? lslot[i] : list[i]));
+  emit_range<NT>(a, r, out_pos, take, [&](uint32_t i) { return in_lds ? lslot[i] : list[i]; });
   out_pos += take;
   __syncthreads();
-  for (int i = (int)out_pos + threadIdx.x; i < a.k; i += kBlock) emit(a, r, i, -1);
+  if (out_pos < (uint32_t)a.k) emit_range<NT>(a, r, out_pos, (uint32_t)a.k - out_pos, [](uint32_t) { return -1; });
   if (threadIdx.x == 0) a.count[r] = (int32_t)min(out_pos, (uint32_t)a.k);
 }
 
+// MAPPED: outputs go through the slot map (their pages are looked up per
+// winner); otherwise the chunk's page-table entries are staged in LDS
+template <int PER, bool MAPPED>
 __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
+  constexpr int kChunk = PER * kBlock;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[32];
-  __shared__ uint32_t bases[2];
+  __shared__ uint32_t before[2];
+  __shared__ int pages[MAPPED ? 1 : kChunk + 1];
   const int r = blockIdx.y;
+  const int c = blockIdx.x;
   const int L = row_len(a, r);
-  const int begin = blockIdx.x * kSelChunk;
+  const int begin = c * kChunk;
   if (begin >= max(L, 1)) return;
-  const int end = min(begin + kSelChunk, L);
+  const int end = min(begin + kChunk, L);
   if (L <= a.k) {
     // every element is kept; workgroup 0 also pads and counts
-    for (int i = begin + threadIdx.x; i < end; i += kBlock) emit(a, r, i, out_value(a, r, i));
+    emit_range<kBlock>(a, r, begin, end - begin, [&](uint32_t i) { return begin + (int)i; });
     if (blockIdx.x == 0) {
-      for (int i = L + threadIdx.x; i < a.k; i += kBlock) emit(a, r, i, -1);
+      if (L < a.k) emit_range<kBlock>(a, r, L, a.k - L, [](uint32_t) { return -1; });
       if (threadIdx.x == 0) a.count[r] = L;
     }
     return;
   }
-  const Ws ws = carve(a.ws, a.num_req);
-  uint32_t* st = ws.state + (size_t)r * kState;
+  const Ws ws = carve(a.ws, a.num_req, a.max_len);
+  const float* row = a.scores + (int64_t)r * a.ld;
+  // one round trip for the chunk's keys (thread t owns elements
+  // begin + t + j*kBlock), the row histogram and the chunk's page-table
+  // entries (so winners leave with their physical rows; with a slot map the
+  // pages are only known per winner)
+  const int i0 = begin + threadIdx.x;
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) key[j] = float_key(row[min(i0 + j * kBlock, end - 1)]);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = gh[i];
+  const bool lds_pages = !MAPPED && a.phys;
+  int pg0 = 0, off;
+  if (lds_pages) {
+    int pg1;
+    split_pos(begin, a.page_size, pg0, off);
+    split_pos(end - 1, a.page_size, pg1, off);
+    const int npg = pg1 - pg0 + 1;
+    const int* pt = a.page_table + (int64_t)r * a.max_pages + pg0;
+    for (int i = threadIdx.x; i < npg; i += kBlock) pages[i] = pt[i];
+  }
+  if (threadIdx.x < 2) before[threadIdx.x] = 0u;
   __syncthreads();
   uint32_t better;
   const uint32_t digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
-  if (blockIdx.x == 0 && threadIdx.x == 0) st[ST_NEED] = (uint32_t)a.k - better;
-  const float* row = a.scores + (int64_t)r * a.ld;
-  int32_t* list = ws.cand + (size_t)r * a.max_len;
-  // thread t owns elements begin + t*kPer .. +kPer (contiguous, 32 bytes)
-  const int i0 = begin + threadIdx.x * kPer;
-  uint32_t win = 0, eq = 0;      // bit masks over the kPer elements
+  if (c == 0 && threadIdx.x == 0) {
+    uint32_t* rec = ws.rec + (size_t)r * 4;
+    rec[0] = digit;
+    rec[1] = better;
+    rec[2] = hist[digit];
+  }
+  // winners and threshold-bin members of the chunks before this one, from
+  // their suffix counts (one load pair per earlier chunk)
+  // (summed per wave first: LDS atomics on one address serialise per lane)
+  if ((int)(threadIdx.x & ~63u) < c) {
+    uint32_t nw = 0, ne = 0;
+    for (int c2 = threadIdx.x; c2 < c; c2 += kBlock) {
+      const uint16_t* sf = ws.suf + ((size_t)r * ws.nchunk + c2) * kBins;
+      const uint32_t ge = sf[digit];
+      const uint32_t gt = digit + 1 < (uint32_t)kBins ? sf[digit + 1] : 0u;
+      nw += gt;
+      ne += ge - gt;
+    }
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = i0 + j;
-    if (i < end) {
-      const uint32_t d = float_key(row[i]) >> 20;
-      win |= (uint32_t)(d > digit) << j;
-      eq |= (uint32_t)(d == digit) << j;
+    for (int o = 32; o >= 1; o >>= 1) {
+      nw += __shfl_xor(nw, o);
+      ne += __shfl_xor(ne, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicAdd(&before[0], nw);
+      atomicAdd(&before[1], ne);
+    }
+  }
+  uint32_t win = 0, eq = 0;      // bit masks over the PER elements
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (i0 + j * kBlock < end) {
+      const uint32_t dj = key[j] >> 20;
+      win |= (uint32_t)(dj > digit) << j;
+      eq |= (uint32_t)(dj == digit) << j;
     }
   }
   uint32_t tot;
-  const uint32_t pre = block_excl_scan<kBlock>(__popc(win) | (__popc(eq) << 16), tmp, &tot);
-  if (threadIdx.x == 0) {
-    bases[0] = (tot & 0xFFFF) ? atomicAdd(&st[ST_OUT], tot & 0xFFFF) : 0u;
-    bases[1] = (tot >> 16) ? atomicAdd(&st[ST_CAND], tot >> 16) : 0u;
-  }
-  __syncthreads();
-  uint32_t ow = bases[0] + (pre & 0xFFFF);
-  uint32_t oc = bases[1] + (pre >> 16);
+  const uint32_t pre = block_excl_scan<kBlock>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot);
+  uint32_t ow = before[0] + (pre & 0xFFFF);
+  uint32_t oc = before[1] + (pre >> 16);
+  int wv[PER], wp[PER];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < PER; ++j) {
+    const int i = i0 + j * kBlock;
+    wv[j] = ((win >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
+  }
+  if (lds_pages) {
+    // every page read first, then the rows (non-winners read a valid dummy)
+    int pg[PER], po[PER], page[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) split_pos(max(wv[j], begin), a.page_size, pg[j], po[j]);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) page[j] = pages[pg[j] - pg0];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      wp[j] = (wv[j] >= 0 && (unsigned)page[j] < (unsigned)a.num_pages) ? page[j] * a.page_size + po[j] : -1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
+  }
+  int2* cand = ws.cand + (size_t)r * a.max_len;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
     if ((win >> j) & 1u) {
-      if (ow < (uint32_t)a.k) emit(a, r, ow, out_value(a, r, i0 + j));
+      if (ow < (uint32_t)a.k) {
+        a.idx[(int64_t)r * a.k + ow] = wv[j];
+        if (a.phys) a.phys[(int64_t)r * a.k + ow] = wp[j];
+      }
       ++ow;
     }
-    if ((eq >> j) & 1u) {
-      if (oc < (uint32_t)a.max_len) list[oc] = i0 + j;
-      ++oc;
-    }
+    if ((eq >> j) & 1u) cand[oc++] = make_int2(i0 + j * kBlock, (int)key[j]);
   }
 }
 
@@ -232,28 +379,192 @@ __global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
   const int r = blockIdx.x;
   const int L = row_len(a, r);
   if (L <= a.k) return;
-  const Ws ws = carve(a.ws, a.num_req);
-  refine_row(a, r, ws, ws.state + (size_t)r * kState, hist, tmp, lkey, lslot);
+  const Ws ws = carve(a.ws, a.num_req, a.max_len);
+  // the threshold bin's members are the candidates (everything above it has
+  // been written already); the first kBlock*kGather of them are loaded
+  // along with the record that says how many there are
+  const uint32_t* rec = ws.rec + (size_t)r * 4;
+  const int2* cand = ws.cand + (size_t)r * a.max_len;
+  int2 e0[kGather];
+#pragma unroll
+  for (int u = 0; u < kGather; ++u) e0[u] = cand[min((int)threadIdx.x + u * kBlock, a.max_len - 1)];
+  const uint32_t better = rec[1];
+  const uint32_t n = rec[2];
+  int32_t* list = ws.list + (size_t)r * a.max_len;
+  const bool in_lds = n <= (uint32_t)kLdsCand;
+  for (uint32_t b = threadIdx.x; b < n; b += kBlock * kGather) {
+    int2 e[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) e[u] = b < (uint32_t)(kBlock * kGather) ? e0[u] : cand[min(b + u * kBlock, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const uint32_t i = b + u * kBlock;
+      if (i >= n) continue;
+      if (in_lds) {
+        lslot[i] = e[u].x;
+        lkey[i] = (uint32_t)e[u].y;
+      } else {
+        list[i] = e[u].x;
+      }
+    }
+  }
+  __syncthreads();
+  refine_cands<kBlock, kLdsCand>(a, r, n, (uint32_t)a.k - better, better, list, in_lds, hist, tmp, lkey,
+                                 lslot, 20, 0u);
 }
 
-// a few dozen workgroups per row at most, so a hot bin sees few atomics
-int pick_hist_chunk(int64_t rows, int64_t max_len) {
-  const int64_t target = (int64_t)num_cus() * 4;
-  int64_t c = ceil_div(rows * max_len, target);
-  c = std::max<int64_t>(c, ceil_div(max_len, 32));
-  c = ceil_div(c, kBlock) * kBlock;
-  if (c < 4096) c = 4096;
-  if (c > 65536) c = 65536;
-  return (int)c;
+// ---------------------------------------------------------------------------
+// One workgroup per row, for batches of rows and short rows.  Scores gather
+// in a few binades, so the top bits of the key would put most of a row into a
+// handful of histogram bins (and the LDS atomics on them in line); the first
+// digit is instead (key - row minimum) >> shift, with shift chosen so that the
+// row's key range fills the 4096 bins.  That is monotone in the key, so the
+// select stays exact; the refinement resolves the `shift` bits below it.
+//   pass 0: row minimum and maximum key (no atomics)
+//   pass 1: LDS histogram of the first digit
+//   pass 2: keys above the threshold bin go straight out, the bin's members
+//           are collected in LDS (slots from wave-aggregated LDS counters)
+//   then the refinement in LDS.  No global atomics, no state to clear.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 1024;
+constexpr int kRowCap = 8192;     // candidates held in LDS
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t lkey[kRowCap];
+  __shared__ int32_t lslot[kRowCap];
+  __shared__ uint32_t tmp[32];
+  __shared__ uint32_t cnt[2];
+  __shared__ uint32_t red[2][kRowThreads / 64];
+  const int r = blockIdx.x;
+  const int L = row_len(a, r);
+  const float* row = a.scores + (int64_t)r * a.ld;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (L <= a.k) {
+    emit_range<kRowThreads>(a, r, 0, L, [](uint32_t i) { return (int)i; });
+    if (L < a.k) emit_range<kRowThreads>(a, r, L, a.k - L, [](uint32_t) { return -1; });
+    if (tid == 0) a.count[r] = L;
+    return;
+  }
+  // pass 0: key range of the row
+  // (each streaming pass issues kBatch loads per thread before using any;
+  // indexes past the end are clamped to the last element, which is harmless
+  // for the minimum and maximum and not counted elsewhere)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int b = tid; b < L; b += kRowThreads * kBatch) {
+    uint32_t kk[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) kk[j] = float_key(row[min(b + j * kRowThreads, L - 1)]);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      kmin = min(kmin, kk[j]);
+      kmax = max(kmax, kk[j]);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  for (int i = tid; i < kBins; i += kRowThreads) hist[i] = 0u;
+  if (tid < 2) cnt[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int wv = 0; wv < kRowThreads / 64; ++wv) {
+    kmin = min(kmin, red[0][wv]);
+    kmax = max(kmax, red[1][wv]);
+  }
+  const uint32_t range = kmax - kmin;
+  const int span = range ? 32 - __clz(range) : 0;      // bits of the range
+  const int shift = span > 12 ? span - 12 : 0;
+  // pass 1
+  for (int b = tid; b < L; b += kRowThreads * kBatch) {
+    uint32_t d[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) d[j] = (float_key(row[min(b + j * kRowThreads, L - 1)]) - kmin) >> shift;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) atomicAdd(&hist[d[j]], b + j * kRowThreads < L ? 1u : 0u);
+  }
+  __syncthreads();
+  uint32_t better;
+  const uint32_t digit = (uint32_t)find_threshold<kRowThreads>(hist, (uint32_t)a.k, true, tmp, &better);
+  int32_t* list = carve(a.ws, a.num_req, a.max_len).list + (size_t)r * a.max_len;
+  // pass 2
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = tid; b < L; b += kRowThreads * kBatch) {
+    uint32_t rel[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) rel[j] = float_key(row[min(b + j * kRowThreads, L - 1)]) - kmin;
+    uint64_t bw[kBatch], be[kBatch];
+    uint32_t nw = 0, ne = 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool in = b + j * kRowThreads < L;
+      const uint32_t d = rel[j] >> shift;
+      bw[j] = __ballot(in && d > digit);
+      be[j] = __ballot(in && d == digit);
+      nw += (uint32_t)__popcll(bw[j]);
+      ne += (uint32_t)__popcll(be[j]);
+    }
+    // one LDS counter update per wave and batch
+    uint32_t wb = 0, eb = 0;
+    if (lane == 0) {
+      if (nw) wb = atomicAdd(&cnt[0], nw);
+      if (ne) eb = atomicAdd(&cnt[1], ne);
+    }
+    wb = __shfl(wb, 0);
+    eb = __shfl(eb, 0);
+    // winners: all value and page loads first, then the stores
+    int wv[kBatch], wp[kBatch];
+    uint32_t wo[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      wo[j] = wb + (uint32_t)__popcll(bw[j] & below);
+      wb += (uint32_t)__popcll(bw[j]);
+      wv[j] = ((bw[j] >> lane) & 1ull) ? out_value(a, r, b + j * kRowThreads) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if ((bw[j] >> lane) & 1ull) {
+        a.idx[(int64_t)r * a.k + wo[j]] = wv[j];
+        if (a.phys) a.phys[(int64_t)r * a.k + wo[j]] = wp[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = b + j * kRowThreads;
+      if ((be[j] >> lane) & 1ull) {
+        const uint32_t c = eb + (uint32_t)__popcll(be[j] & below);
+        if (c < (uint32_t)kRowCap) {
+          lkey[c] = rel[j];
+          lslot[c] = i;
+        }
+        if (c < (uint32_t)a.max_len) list[c] = i;
+      }
+      eb += (uint32_t)__popcll(be[j]);
+    }
+  }
+  __syncthreads();
+  const uint32_t n = cnt[1];
+  refine_cands<kRowThreads, kRowCap>(a, r, n, (uint32_t)a.k - better, better, list, n <= (uint32_t)kRowCap,
+                                     hist, tmp, lkey, lslot, shift, kmin);
 }
 
 }  // namespace
 
 size_t topk_ws_bytes(int num_req, int max_len) {
-  return align_up(((size_t)num_req * (kBins + kState) + (size_t)num_req * max_len) * 4, 256);
+  const size_t R = (size_t)num_req;
+  return align_up(R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (3 * R * max_len + 4 * R) * 4, 256);
 }
 
-int64_t topk_zero_words(int num_req) { return (int64_t)num_req * (kBins + kState); }
+int64_t topk_zero_words(int num_req) { return (int64_t)num_req * kBins; }
 
 hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t s) {
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, kBlock * 4), 1024));
@@ -262,12 +573,36 @@ hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
-  if (ws_state == 0) launch_zero(static_cast<uint32_t*>(a.ws), topk_zero_words(a.num_req), s);
-  const int chunk = pick_hist_chunk(a.num_req, a.max_len);
-  dim3 hgrid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, chunk)), (unsigned)a.num_req);
-  hipLaunchKernelGGL(topk_hist_kernel, hgrid, dim3(kBlock), 0, s, a, chunk);
-  dim3 sgrid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, kSelChunk)), (unsigned)a.num_req);
-  hipLaunchKernelGGL(topk_select_kernel, sgrid, dim3(kBlock), 0, s, a);
+  // rows enough to fill every compute unit, or short ones: one workgroup per
+  // row is enough parallelism and needs no hand-over between workgroups
+  if (a.num_req >= num_cus() || a.max_len <= 32768) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(a.num_req), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (ws_state == 0) {
+    const hipError_t e = launch_zero(static_cast<uint32_t*>(a.ws), topk_zero_words(a.num_req), s);
+    if (e != hipSuccess) return e;
+  }
+  // chunks sized for about two workgroups per compute unit
+  const int64_t want = ceil_div((int64_t)a.num_req * a.max_len, 2 * (int64_t)num_cus());
+  int per = kMinChunk / kBlock;
+  while (per * kBlock < kMaxChunk && per * kBlock < want) per *= 2;
+  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)), (unsigned)a.num_req);
+  const bool mapped = a.map != nullptr;
+  switch (per) {
+#define LSI_TOPK_PER(P)                                                                      \
+  case P:                                                                                    \
+    hipLaunchKernelGGL(topk_hist_kernel<P>, grid, dim3(kBlock), 0, s, a);                    \
+    if (mapped) hipLaunchKernelGGL((topk_select_kernel<P, true>), grid, dim3(kBlock), 0, s, a); \
+    else hipLaunchKernelGGL((topk_select_kernel<P, false>), grid, dim3(kBlock), 0, s, a);    \
+    break;
+    LSI_TOPK_PER(2)
+    LSI_TOPK_PER(4)
+    LSI_TOPK_PER(8)
+    LSI_TOPK_PER(16)
+#undef LSI_TOPK_PER
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

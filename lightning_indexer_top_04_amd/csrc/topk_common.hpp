@@ -8,46 +8,52 @@ namespace lsi {
 namespace topk {
 
 constexpr int kBins = 4096;      // 12-bit digits
-constexpr int kState = 16;       // state words per row
+constexpr int kMinChunk = 1024;  // smallest chunk of positions per workgroup
+constexpr int kMaxChunk = 8192;  // largest
 
-// state words per row
-enum {
-  ST_NEED = 0,        // how many of the threshold bin still need to be taken
-  ST_OUT = 1,         // winners written so far
-  ST_CAND = 2,        // candidates collected so far
-};
-
+// Per-row workspace of the multi-workgroup top-k.  Only hist must be zero
+// when a call starts; every other word is written before it is read.
 struct Ws {
-  uint32_t* hist;    // [R][kBins]
-  uint32_t* state;   // [R][kState]
-  int32_t* cand;     // [R][max_len]
+  uint32_t* hist;    // [R][kBins] histogram of the top 12 key bits
+  uint16_t* suf;     // [R][nchunk][kBins] per chunk: elements with digit >= bin
+  int2* cand;        // [R][max_len] threshold-bin members (slot, key), in chunk order
+  int32_t* list;     // [R][max_len] their slots, compacted (when too many for LDS)
+  uint32_t* rec;     // [R][4] threshold bin, count above it, count in it
+  int nchunk;        // chunks per row at the smallest chunk size
 };
 
-__host__ __device__ inline Ws carve(void* ws, int R) {
+__host__ __device__ inline int max_chunks(int max_len) { return (max_len + kMinChunk - 1) / kMinChunk; }
+
+__host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   Ws w;
+  w.nchunk = max_chunks(max_len);
   w.hist = static_cast<uint32_t*>(ws);
-  w.state = w.hist + (size_t)R * kBins;
-  w.cand = reinterpret_cast<int32_t*>(w.state + (size_t)R * kState);
+  w.suf = reinterpret_cast<uint16_t*>(w.hist + (size_t)R * kBins);
+  w.cand = reinterpret_cast<int2*>(w.suf + (size_t)R * w.nchunk * kBins);
+  w.list = reinterpret_cast<int32_t*>(w.cand + (size_t)R * max_len);
+  w.rec = reinterpret_cast<uint32_t*>(w.list + (size_t)R * max_len);
   return w;
 }
 
-// Block-wide exclusive scan of one uint32 per thread (NT threads).
-template <int NT>
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+// Block-wide exclusive scan of one value per thread (NT threads); T is
+// uint32_t or uint64_t (two 32-bit counts packed, each summed on its own as
+// long as neither overflows).  tmp needs NT/64 values of T.
+template <int NT, class T>
+__device__ T block_excl_scan(T v, T* tmp, T* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t inc = v;
+  T inc = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(inc, o);
+    const T t = __shfl_up(inc, o);
     if (lane >= o) inc += t;
   }
   if (lane == 63) tmp[wave] = inc;
   __syncthreads();
-  uint32_t base = 0, tot = 0;
+  T base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
-    const uint32_t t = tmp[i];
+    const T t = tmp[i];
     if (i < wave) base += t;
     tot += t;
   }

@@ -159,19 +159,23 @@ def _topk_case(scores_np, k, lens):
     return idx, cnt, out
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_topk_random_rows_against_full_sort(seed):
+# Batches of 16 rows or more, and rows of at most 32768 scores, run one
+# workgroup per row; fewer, longer rows run the multi-workgroup kernels.  The
+# cases below cover both.
+
+@pytest.mark.parametrize("seed,reps", [(0, 1), (1, 1), (2, 3)])
+def test_topk_random_rows_against_full_sort(seed, reps):
     rng = np.random.default_rng(seed)
-    lens = [131072, 5000, 2049, 2048, 100, 0, 1, 77777]
+    lens = [131072, 5000, 2049, 2048, 100, 0, 1, 77777] * reps
     sc = rng.standard_normal((len(lens), max(lens))) * 3
     _, _, st = _topk_case(sc, 2048, lens)
     # fp32 inputs: the oracle sees the same values, so the sets are equal
     assert all(s["diff"] == 0 for s in st), st
 
 
-def test_topk_exact_ties_keep_lowest_positions():
+@pytest.mark.parametrize("L", [20000, 70000])
+def test_topk_exact_ties_keep_lowest_positions(L):
     rng = np.random.default_rng(3)
-    L = 20000
     sc = np.round(rng.standard_normal((2, L)) * 2) / 2     # heavy ties
     sc[1] = 1.5                                            # every score equal
     sc[0, 123] = -0.0
@@ -181,17 +185,19 @@ def test_topk_exact_ties_keep_lowest_positions():
         assert set(idx[b][:cnt[b]].tolist()) == set(ref.tolist())
 
 
-def test_topk_negative_scores_signed_zero_and_infinities():
-    sc = np.array([[-3.0, -0.0, 0.0, -np.inf, np.inf, -1e-30, 2.0, -2.0] + [-5.0] * 56])
-    idx, cnt, _ = _topk_case(sc, 4, [64])
+@pytest.mark.parametrize("L", [64, 40000])
+def test_topk_negative_scores_signed_zero_and_infinities(L):
+    sc = np.array([[-3.0, -0.0, 0.0, -np.inf, np.inf, -1e-30, 2.0, -2.0] + [-5.0] * (L - 8)])
+    idx, cnt, _ = _topk_case(sc, 4, [L])
     assert sorted(idx[0][:4].tolist()) == [1, 2, 4, 6]
 
 
-def test_topk_small_k_and_large_k():
+@pytest.mark.parametrize("reps", [1, 6])
+def test_topk_small_k_and_large_k(reps):
     rng = np.random.default_rng(9)
-    sc = rng.standard_normal((3, 70000))
-    _topk_case(sc, 1, [70000, 10, 0])
-    _topk_case(sc, 65536, [70000, 65536, 65535])
+    sc = rng.standard_normal((3 * reps, 70000))
+    _topk_case(sc, 1, [70000, 10, 0] * reps)
+    _topk_case(sc, 65536, [70000, 65536, 65535] * reps)
 
 
 # ----------------------------------------------------------------------------
