@@ -87,30 +87,43 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
   const int r1 = min(r0 + rows_per_split, a.k);
   const int nr = max(0, r1 - r0);
 
-  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32u + 8g .. +7]
-  const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + head) * kD;
-  bf16x8 qr[kD / 32];
-#pragma unroll
-  for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
-
   // physical rows of the slice, resolved once (given by the selection, or
   // looked up through the page table); -1 = skip
+  constexpr int kRowsPerThread = kMaxSplitRows / kMThreads;
   const int n_rows_pool = a.num_pages * a.page_size;
-  for (int e = tid; e < nr; e += kMThreads) {
-    int row = -1;
-    if (a.phys) {
-      row = a.phys[(int64_t)b * a.k + r0 + e];
-      if (row >= n_rows_pool) row = -1;
-    } else {
-      const int pos = a.idx[(int64_t)b * a.k + r0 + e];
-      if (pos >= 0 && pos < L) {
-        const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-        if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+  int prow[kRowsPerThread];
+  if (a.phys) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int e = tid + i * kMThreads;
+      prow[i] = e < nr ? a.phys[(int64_t)b * a.k + r0 + e] : -1;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int e = tid + i * kMThreads;
+      prow[i] = -1;
+      if (e < nr) {
+        const int pos = a.idx[(int64_t)b * a.k + r0 + e];
+        if (pos >= 0 && pos < L) {
+          const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+          if ((unsigned)page < (unsigned)a.num_pages) prow[i] = page * a.page_size + pos % a.page_size;
+        }
       }
     }
-    rows_all[e] = row < 0 ? -1 : row;
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int e = tid + i * kMThreads;
+    if (e < nr) rows_all[e] = (prow[i] < 0 || prow[i] >= n_rows_pool) ? -1 : prow[i];
   }
   __syncthreads();
+
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32u + 8g .. +7];
+  // loaded once the first block's gather is in flight (an ordinary load
+  // issued before the gather would make it wait for the load)
+  const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + head) * kD;
+  bf16x8 qr[kD / 32];
 
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv);
   const float c = a.sm_scale * kLog2e;
@@ -140,6 +153,10 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
         const uint8_t* src = kvb + (int64_t)(rw < 0 ? 0 : rw) * (kD * 2) + 2 * kDV + 16 * (p ^ (rr & 7));
         dma_row16<0>(kvs + kRopeOff + (2 * w + t) * 1024, src);
       }
+    }
+    if (base == 0) {
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
