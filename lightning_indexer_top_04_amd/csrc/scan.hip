@@ -468,19 +468,48 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int h = lane >> 5;
-  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-  const int nprod = max(1, (L + chunk - 1) / chunk);
-  if ((int)blockIdx.x >= nprod) return;
+  // One round trip for the slice's page ids (as far as the longest request
+  // reaches; the request's own length only trims them), the request length
+  // and, further down, the query rows and head weights.
   const int begin = blockIdx.x * chunk;
+  const int npg_max = max(0, (min(begin + chunk, a.max_seq_len) - begin + a.page_size - 1) >> page_shift);
+  int page_in = -1;
+  if (tid < npg_max) page_in = a.page_table[(int64_t)b * a.max_pages + (begin >> page_shift) + tid];
+  const int Lraw = a.seq_lens[b];
+  uint8_t* slot[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) slot[r] = &ring[r][0] + wv * kSlotBytes;
+
+  // The query split is computed while the first key tiles are on their way.
+  // The query rows of the wave's 16 heads (4 KB) and the 64 head weights come
+  // in by DMA as well, into the last ring position: an ordinary load issued
+  // ahead of the tile DMAs would be waited for with every DMA behind it.
+  // (The page ids and the length above are such loads; their wait covers
+  // this DMA too, which is what the prologue wants: all of it is one round
+  // trip.)  Issue order after that wait: tiles 0 .. RING-2 (5 operations
+  // each); the last ring position gets its tile once the split is done.
+  {
+    uint8_t* qslot = slot[RING - 1];
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
+                                                        ((int64_t)b * kHeads + 16 * wv) * kDim) + 16 * lane;
+    asm volatile("" ::: "memory");
+    lds_dma16<0>(qslot, qg);
+    lds_dma16<1024>(qslot, qg);
+    lds_dma16<2048>(qslot, qg);
+    lds_dma16<3072>(qslot, qg);
+    lds_dma4(qslot + kTileBytes, a.w + (int64_t)b * kHeads + lane);
+  }
+  const int L = min(max(Lraw, 0), a.max_seq_len);
+  const int nprod = max(1, (L + chunk - 1) / chunk);
+  if ((int)blockIdx.x >= nprod) {
+    // nothing of this request here; no DMA may still be writing the LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+  if (tid < npg_max) pages[tid] = page_in;
+  __syncthreads();
   const int end = min(begin + chunk, L);
   const int ntile = max(0, (end - begin + kTile - 1) / kTile);
-  {
-    const int npg = (end - begin + a.page_size - 1) >> page_shift;
-    const int pg0 = begin >> page_shift;
-    for (int i = tid; i < npg; i += kThreads)
-      pages[i] = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
-  }
-  __syncthreads();
 
   // A wave takes a contiguous run of the slice's tiles, so its scores form
   // one contiguous range.
@@ -519,27 +548,7 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
     lds_dma16<3072>(slot, g);
     lds_dma4(slot + kTileBytes, a.kscale + row0 + m);
   };
-  uint8_t* slot[RING];
-#pragma unroll
-  for (int r = 0; r < RING; ++r) slot[r] = &ring[r][0] + wv * kSlotBytes;
 
-  // The query split is computed while the first key tiles are on their way.
-  // The query rows of the wave's 16 heads (4 KB) and the 64 head weights come
-  // in by DMA as well, into the last ring position: an ordinary load issued
-  // ahead of the tile DMAs would be waited for with every DMA behind it.
-  // Issue order: query + weights (5 operations), then tiles 0 .. RING-2
-  // (5 each); the last ring position gets its tile once the split is done.
-  {
-    uint8_t* qslot = slot[RING - 1];
-    const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
-                                                        ((int64_t)b * kHeads + 16 * wv) * kDim) + 16 * lane;
-    asm volatile("" ::: "memory");
-    lds_dma16<0>(qslot, qg);
-    lds_dma16<1024>(qslot, qg);
-    lds_dma16<2048>(qslot, qg);
-    lds_dma16<3072>(qslot, qg);
-    lds_dma4(qslot + kTileBytes, a.w + (int64_t)b * kHeads + lane);
-  }
 #pragma unroll
   for (int r = 0; r + 1 < RING; ++r) issue(r, slot[r]);
   wait_ring_tile<RING>();     // the query DMAs, RING - 1 tile groups ago
@@ -688,6 +697,17 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   };
 
   for (int j = 0; j < myn; j += RING) {
+    {
+      // Issue priority falls as the run nears its end.  Three workgroups
+      // share a CU and the oldest waves otherwise win every arbitration, so
+      // the first-dispatched finish far ahead of the last and the CU ends
+      // its work under-occupied; this keeps co-resident runs in step.
+      const int p = (6 * (myn - j)) / (myn + 1);
+      if (p >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (p == 2) __builtin_amdgcn_s_setprio(2);
+      else if (p == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       const int jr = j + r;
@@ -756,6 +776,8 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   const bool dma = KIND == KIND_FP8 && !gather;
   constexpr int kRingTiles = 2;
   const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, dma ? (kRingTiles >= 4 ? 2 : 3) : 2);
+  // the DMA scan stages a slice's page ids with one load per thread
+  if (dma && (chunk + a.page_size - 1) / a.page_size > std::min(kMaxChunkPages, kThreads)) return hipErrorInvalidValue;
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   const int ps = ilog2(a.page_size);
   if (dma)
