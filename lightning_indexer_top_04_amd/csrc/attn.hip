@@ -52,6 +52,73 @@ __device__ __forceinline__ void dma_row16(uint8_t* lds, const uint8_t* g) {
                                    (__attribute__((address_space(3))) void*)lds, 16, OFF, 0);
 }
 
+// Max and sum over the four 16-lane rows of the wave (lanes n, n+16, n+32,
+// n+48) with the row-swap permutes: two VALU swaps instead of two LDS
+// round trips of a shuffle.
+__device__ __forceinline__ float max4rows(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum4rows(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and
+// writes, not for its block DMAs still in flight (__syncthreads would).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+// Six 16-byte LDS reads, complete when the statement ends.  Written out so
+// that the compiler, which cannot tell these rows from a block DMA still in
+// flight into the other buffer, does not wait for that DMA first.
+__device__ __forceinline__ void lds_read_b128x6(u32x4 (&o)[6], const uint32_t (&ad)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5])
+      : "memory");
+}
+// One 8-byte LDS write (same reason); the next barrier waits for it.
+__device__ __forceinline__ void lds_write_b64(uint32_t a, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+// Two 16-byte and eight transposing 8-byte LDS reads, complete when the
+// statement ends (same reason as above).
+__device__ __forceinline__ void lds_read_p2_tr8(u32x4 (&p)[2], s16x4 (&o)[8], uint32_t pa0, uint32_t pa1,
+                                                const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %10\n\t"
+      "ds_read_b128 %1, %11\n\t"
+      "ds_read_b64_tr_b16 %2, %12\n\t"
+      "ds_read_b64_tr_b16 %3, %13\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %15\n\t"
+      "ds_read_b64_tr_b16 %6, %16\n\t"
+      "ds_read_b64_tr_b16 %7, %17\n\t"
+      "ds_read_b64_tr_b16 %8, %18\n\t"
+      "ds_read_b64_tr_b16 %9, %19\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p[0]), "=&v"(p[1]), "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]),
+        "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(pa0), "v"(pa1), "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]),
+        "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
 // LDS transpose read: within each 16-lane group, lane 4a + c receives element
 // c of the 8-byte chunks addressed by lanes a, a + 4, a + 8 and a + 12.
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
@@ -186,8 +253,7 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
       x[r] = ok ? sacc[r] * c : -INFINITY;
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max4rows(mx);
     if (g == 0) red_m[w][n] = mx;
     __syncthreads();
     const float bmax = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
@@ -200,8 +266,7 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = m_new == -INFINITY ? 0.f : exp2f(x[r] - m_new);
     float ps = (p[0] + p[1]) + (p[2] + p[3]);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = sum4rows(ps);
     if (g == 0) red_l[w][n] = ps;
     {
       const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
@@ -270,6 +335,256 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
 #pragma unroll
       for (int t = 0; t < 8; ++t) po[16 * t] = o[t][r] * inv;
       if (w == 0 && n == 0) part_lse[bh * nsplit + split] = lse2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batches: 32 heads per workgroup of 8 waves, one workgroup per CU, the next
+// 64-row block gathered while the current one is computed.  Half the head
+// groups of the 16-head kernel, so each selected row is moved into LDS half
+// as often, and the gather latency hides behind compute instead of behind a
+// second workgroup.  Wave w = (rt, ht) computes S^T for rows 16rt..+15 and
+// heads 16ht..+15 of the group (its query tile in registers); the softmax of
+// a head meets the four row tiles through LDS; for O = P V wave w owns value
+// dims 64w..+63 of all 32 heads.
+// ---------------------------------------------------------------------------
+constexpr int kWH = 32;                       // heads per workgroup
+constexpr int kWThreads = 512;
+constexpr int kWMaxRows = 2048;               // selection rows one workgroup handles
+constexpr int kWDmaPerBlock = 9;              // DMA instructions per wave per block
+                                              // (the vmcnt(9) waits below)
+
+__global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a, int rows_per_split,
+                                                                    int nsplit, int units, float* part_o,
+                                                                    float* part_lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs0[kKvBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs1[kKvBytes];
+  __shared__ __attribute__((aligned(16))) __bf16 Pl[kWH * kPStride];
+  __shared__ float red_m[4][kWH];
+  __shared__ float red_l[4][kWH];
+  __shared__ float alpha_s[kWH];
+  __shared__ int rows_all[kWMaxRows];
+
+  const int n_hg = a.n_heads / kWH;
+  const int bid = blockIdx.x;
+  const int u = (bid / (8 * n_hg)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % n_hg;
+  if (u >= units) return;
+  const int b = u / nsplit;
+  const int split = u % nsplit;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3;                        // row tile of S
+  const int ht = w >> 2;                       // head tile of S
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int hh = 16 * ht + n;                  // this lane's head (S layout) within the group
+  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int r0 = split * rows_per_split;
+  const int r1 = min(r0 + rows_per_split, a.k);
+  const int nr = max(0, r1 - r0);
+
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32t + 8g .. +7]
+  const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + hg * kWH + hh) * kD;
+  bf16x8 qr[kD / 32];
+#pragma unroll
+  for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
+  // physical rows of the slice (-1 = skip)
+  const int n_rows_pool = a.num_pages * a.page_size;
+  for (int e = tid; e < nr; e += kWThreads) {
+    int row = -1;
+    if (a.phys) {
+      row = a.phys[(int64_t)b * a.k + r0 + e];
+    } else {
+      const int pos = a.idx[(int64_t)b * a.k + r0 + e];
+      if (pos >= 0 && pos < L) {
+        const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+        if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+      }
+    }
+    rows_all[e] = (row < 0 || row >= n_rows_pool) ? -1 : row;
+  }
+  // the query and row loads are complete here (ordinary loads are not left
+  // in flight under the block DMAs, whose waits are counted by hand below)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv);
+  // wave w moves rows 8w..8w+7 of a block: one 1 KB DMA per row for the
+  // latent dims (chunk c of row r at c ^ (r % 16)), one for their rope dims
+  // (c ^ (r % 8)) -- kWDmaPerBlock instructions, every wave, every block
+  auto gather = [&](int blk, uint8_t* buf) {
+    const int base = blk * kMBlk;
+    const int nb = min(kMBlk, nr - base);
+    const int rl = 8 * w + (lane & 7);
+    const int myrow = rl < nb ? rows_all[base + rl] : -1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rw = __builtin_amdgcn_readlane(myrow, i);
+      const uint8_t* src = kvb + (int64_t)(rw < 0 ? 0 : rw) * (kD * 2) + 16 * (lane ^ ((8 * w + i) & 15));
+      dma_row16<0>(buf + (8 * w + i) * kVRow, src);
+    }
+    const int rr = lane >> 3;
+    const int rw = __shfl(myrow, rr);
+    const uint8_t* src = kvb + (int64_t)(rw < 0 ? 0 : rw) * (kD * 2) + 2 * kDV + 16 * ((lane & 7) ^ rr);
+    dma_row16<0>(buf + kRopeOff + w * 1024, src);
+  };
+
+  const float c = a.sm_scale * kLog2e;
+  f32x4 o[2][4];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[h2][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // per head hh, the same in the four row-tile waves
+  float l_run = 0.f;
+
+  const int nblk = (nr + kMBlk - 1) / kMBlk;
+  auto step = [&](int blk, const uint8_t* kv, uint8_t* next) {
+    const int base = blk * kMBlk;
+    const int nb = min(kMBlk, nr - base);
+    // the next block goes out first; then this block's DMAs (the ones before
+    // the last kWDmaPerBlock) must have landed, in every wave
+    if (blk + 1 < nblk) {
+      gather(blk + 1, next);
+      asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    // ---- S^T for rows 16rt + (0..15) and heads 16ht + (0..15)
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int row = 16 * rt + n;
+      const uint32_t vrow = lds_addr(kv) + row * kVRow;
+      const uint32_t rrow = lds_addr(kv) + kRopeOff + (row >> 3) * 1024 + (row & 7) * 128;
+#pragma unroll
+      for (int t0 = 0; t0 < kD / 32; t0 += 6) {
+        uint32_t ad[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const int t = t0 + i;
+          ad[i] = t < 16 ? vrow + 16 * ((4 * t + g) ^ (row & 15)) : rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7));
+        }
+        u32x4 av[6];
+        lds_read_b128x6(av, ad);
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]), qr[t0 + i], sacc, 0, 0, 0);
+      }
+    }
+    // lane (n, g) holds S^T[row 16rt + 4g + r][head hh]
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rl = 16 * rt + 4 * g + r;
+      const bool ok = rl < nb && rows_all[base + rl] >= 0;
+      x[r] = ok ? sacc[r] * c : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = max4rows(mx);
+    if (g == 0) red_m[rt][hh] = mx;
+    lds_barrier();
+    const float bmax = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
+    // lazy rescaling, as in the 16-head kernel
+    const bool first = m_run == -INFINITY;
+    const float m_new = (first || bmax > m_run + 8.f) ? fmaxf(m_run, bmax) : m_run;
+    const float alpha = (first || m_new == m_run) ? (first ? 0.f : 1.f) : exp2f(m_run - m_new);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = m_new == -INFINITY ? 0.f : exp2f(x[r] - m_new);
+    float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    ps = sum4rows(ps);
+    if (g == 0) red_l[rt][hh] = ps;
+    {
+      const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      lds_write_b64(lds_addr(&Pl[hh * kPStride + 16 * rt + 4 * g]), pw);
+    }
+    if (rt == 0 && g == 0) alpha_s[hh] = alpha;
+    lds_barrier();
+    l_run = l_run * (first ? 0.f : alpha) + ((red_l[0][hh] + red_l[1][hh]) + (red_l[2][hh] + red_l[3][hh]));
+    m_run = m_new;
+
+    // ---- O[32 heads][dims 64w ..] += P V; lane (dim n, g) holds heads 16h2 + 4g + r
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x4 al;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = alpha_s[16 * h2 + 4 * g + r];
+      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[h2][t] *= al;
+      }
+    }
+    const int s16 = lane & 15;
+    const int ja = s16 >> 2;
+    const int aa = s16 & 3;
+#pragma unroll 1
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ra = 32 * kk + 8 * g + ja;
+      uint32_t ad[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ch = (64 * w + 16 * t + 4 * aa) >> 3;
+        const int hb = 8 * (aa & 1);
+        ad[2 * t] = lds_addr(kv) + ra * kVRow + 16 * (ch ^ (ra & 15)) + hb;
+        ad[2 * t + 1] = lds_addr(kv) + (ra + 4) * kVRow + 16 * (ch ^ ((ra + 4) & 15)) + hb;
+      }
+      u32x4 pr[2];
+      s16x4 vt[8];
+      lds_read_p2_tr8(pr, vt, lds_addr(&Pl[n * kPStride + 32 * kk + 8 * g]),
+                      lds_addr(&Pl[(16 + n) * kPStride + 32 * kk + 8 * g]), ad);
+      const bf16x8 pa[2] = {__builtin_bit_cast(bf16x8, pr[0]), __builtin_bit_cast(bf16x8, pr[1])};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const s16x4 v0 = vt[2 * t];
+        const s16x4 v1 = vt[2 * t + 1];
+        const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        bf16x8 vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vb[e] = __builtin_bit_cast(__bf16, vv[e]);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) o[h2][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h2], vb, o[h2][t], 0, 0, 0);
+      }
+    }
+    lds_barrier();   // this block's buffer is refilled by the next step
+  };
+  if (nblk > 0) gather(0, kvs0);
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, kvs0, kvs1);
+    if (blk + 1 < nblk) step(blk + 1, kvs1, kvs0);
+  }
+
+  // ---- results
+  if (rt == 0 && g == 0) {
+    red_m[0][hh] = m_run;
+    red_l[0][hh] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hl = 16 * h2 + 4 * g + r;
+      const float lr = red_l[0][hl];
+      const float mr = red_m[0][hl];
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      const float lse2 = lr > 0.f ? mr + log2f(lr) : -INFINITY;
+      const int64_t bh = (int64_t)b * a.n_heads + hg * kWH + hl;
+      const int dim0 = 64 * w + n;
+      if (nsplit == 1) {
+        __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV + dim0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ob[16 * t] = (__bf16)(o[h2][t][r] * inv);
+        if (w == 0 && n == 0) a.lse[bh] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+      } else {
+        float* po = part_o + (bh * nsplit + split) * kDV + dim0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) po[16 * t] = o[h2][t][r] * inv;
+        if (w == 0 && n == 0) part_lse[bh * nsplit + split] = lse2;
+      }
     }
   }
 }
@@ -384,35 +699,54 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   if (tid == 0) a.lse[bh] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
-int pick_nsplit(int num_req, int n_heads, int k) {
-  const int groups = num_req * (n_heads / kMH);
+// Kernel and split of the selection for a launch.  The 32-head kernel takes
+// batches (enough workgroups to fill the chip at one per CU); the 16-head
+// kernel, with twice the workgroups per request, takes few requests.
+struct MlaPlan {
+  bool wide;
+  int nsplit;
+  int rows_per_split;
+};
+
+constexpr int kWideMinReq = 8;
+
+MlaPlan plan_mla(int num_req, int n_heads, int k) {
   const int blocks = (k + kMBlk - 1) / kMBlk;
-  // ~2 workgroups per CU, at least one block per split
-  int ns = (int)ceil_div((int64_t)num_cus() * 2, std::max(groups, 1));
+  const bool wide = n_heads % kWH == 0 && num_req >= kWideMinReq;
+  const int groups = num_req * (n_heads / (wide ? kWH : kMH));
+  const int max_rows = wide ? kWMaxRows : kMaxSplitRows;
+  // about one (wide) or two (narrow) workgroups per CU, at least one block
+  // per split, at most max_rows rows per workgroup
+  int ns = (int)ceil_div((int64_t)num_cus() * (wide ? 1 : 2), std::max(groups, 1));
   ns = std::min(ns, std::max(1, blocks));
-  ns = std::max(ns, (int)ceil_div(blocks, kMaxSplitRows / kMBlk));
-  return std::min(std::max(ns, 1), 64);
+  ns = std::max(ns, (int)ceil_div(blocks, max_rows / kMBlk));
+  ns = std::min(std::max(ns, 1), 64);
+  const int rows_per_split = (int)ceil_div(blocks, ns) * kMBlk;
+  return {wide, (int)ceil_div(std::max(k, 1), rows_per_split), rows_per_split};
 }
 
 }  // namespace
 
 size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k) {
-  const int ns = pick_nsplit(num_req, n_heads, k);
-  if (ns == 1) return 0;
-  return align_up((size_t)num_req * n_heads * ns * (dv + 1) * sizeof(float), 256);
+  const MlaPlan p = plan_mla(num_req, n_heads, k);
+  if (p.nsplit == 1) return 0;
+  return align_up((size_t)num_req * n_heads * p.nsplit * (dv + 1) * sizeof(float), 256);
 }
 
 hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
-  const int ns = pick_nsplit(a.num_req, a.n_heads, a.k);
-  const int blocks = (a.k + kMBlk - 1) / kMBlk;
-  const int rows_per_split = (int)ceil_div(blocks, ns) * kMBlk;
-  const int nsplit = (int)ceil_div(a.k, rows_per_split);
+  const MlaPlan p = plan_mla(a.num_req, a.n_heads, a.k);
+  const int nsplit = p.nsplit;
+  const int rows_per_split = p.rows_per_split;
   float* part_o = static_cast<float*>(a.ws);
   float* part_lse = part_o ? part_o + (size_t)a.num_req * a.n_heads * nsplit * kDV : nullptr;
   const int units = a.num_req * nsplit;
-  const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / kMH);
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, a, rows_per_split, nsplit,
-                     units, part_o, part_lse);
+  const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / (p.wide ? kWH : kMH));
+  if (p.wide)
+    hipLaunchKernelGGL(mla_bf16_wide_kernel, dim3(grid), dim3(kWThreads), 0, s, a, rows_per_split, nsplit,
+                       units, part_o, part_lse);
+  else
+    hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, a, rows_per_split, nsplit,
+                       units, part_o, part_lse);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_req * a.n_heads), dim3(kDV / 4), 0, s, a,
                        nsplit, part_o, part_lse);

@@ -204,20 +204,24 @@ def test_topk_small_k_and_large_k(reps):
 # Sparse attention
 # ----------------------------------------------------------------------------
 
-def test_mla_on_oracle_selection_with_padding_and_splits():
-    di = small_dsa([6000, 1500, 2048], k=2048)
+# batches of 8 or more requests take the 32-head, double-buffered kernel
+@pytest.mark.parametrize("reps", [1, 3])
+def test_mla_on_oracle_selection_with_padding_and_splits(reps):
+    lens = [6000, 1500, 2048] * reps
+    B = len(lens)
+    di = small_dsa(lens, k=2048)
     ov = OracleView(di)
     ik, req, kv, _ = objs(di)
     k = 2048
-    idx = torch.full((3, k), -1, dtype=torch.int32)
-    for b in range(3):
+    idx = torch.full((B, k), -1, dtype=torch.int32)
+    for b in range(B):
         I, _ = ov.scores(b)
         sel, _ = O.topk(I, k)
         idx[b, :len(sel)] = torch.from_numpy(sel.astype(np.int32))
     idx_d = idx.to(DEV)
     out, lse = lsi.sparse_mla_decode(kv, None, req, di.q_attn, idx_d, di.wl.sm_scale, 512)
     torch.cuda.synchronize()
-    for b in range(3):
+    for b in range(B):
         sel = idx[b][idx[b] >= 0].numpy()
         ro, rl = ov.attention(b, sel)
         print(b, check_attention(out[b].float().cpu().numpy(), ro, f"mla {b}"))
@@ -242,34 +246,41 @@ def test_mla_single_row_and_empty_selection():
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
-def test_mla_head_counts_and_partial_blocks():
-    # 48 heads (three 16-head groups), k = 1000 (a partial 64-row block), -1 padding
-    lens = (3000, 900, 2500)
-    wl = synth.scaled(synth.DSA_128K, seed=13, seq_lens=lens, num_req=3, n_planted=32, k=1000,
-                      n_heads=48)
+@pytest.mark.parametrize("heads,reps", [(48, 1), (64, 3), (96, 3)])
+def test_mla_head_counts_and_partial_blocks(heads, reps):
+    # 48 heads (three 16-head groups; the 16-head kernel at any batch), 64 and
+    # 96 heads over 9 requests (two and three 32-head groups); k = 1000 (a
+    # partial 64-row block), -1 padding
+    lens = (3000, 900, 2500) * reps
+    B = len(lens)
+    wl = synth.scaled(synth.DSA_128K, seed=13, seq_lens=lens, num_req=B, n_planted=32, k=1000,
+                      n_heads=heads)
     di = synth.make_decode_inputs(wl, device=DEV, with_attn=True)
     ov = OracleView(di)
     _, req, kv, _ = objs(di)
     rng = np.random.default_rng(5)
     k = 1000
-    idx = torch.full((3, k), -1, dtype=torch.int32)
+    idx = torch.full((B, k), -1, dtype=torch.int32)
     for b, L in enumerate(lens):
         n = min(L, k) - 7 * b
         idx[b, :n] = torch.from_numpy(rng.choice(L, size=n, replace=False).astype(np.int32))
     out, lse = lsi.sparse_mla_decode(kv, None, req, di.q_attn, idx.to(DEV), di.wl.sm_scale, 512)
     torch.cuda.synchronize()
-    for b in range(3):
+    for b in range(B):
         sel = idx[b][idx[b] >= 0].numpy()
         ro, rl = ov.attention(b, sel)
         print(b, check_attention(out[b].float().cpu().numpy(), ro, f"mla48 {b}"))
         assert np.allclose(lse[b].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
 
 
-def test_mla_late_dominant_rows_rescale_the_running_softmax():
-    # four requests: each workgroup takes two 64-row blocks of its slice; the
-    # rows in the second half of every 128-entry slice get 6x larger latent
-    # rows, so their logits exceed the first block's maximum by far
-    lens = (3000,) * 4
+@pytest.mark.parametrize("B", [4, 8])
+def test_mla_late_dominant_rows_rescale_the_running_softmax(B):
+    # 16-head kernel (4 requests): each workgroup takes two 64-row blocks of
+    # its slice; the rows in the second half of every 128-entry slice get 6x
+    # larger latent rows, so their logits exceed the first block's maximum by
+    # far.  32-head kernel (8 requests): slices of 256 rows, four blocks, the
+    # same rows scaled.
+    lens = (3000,) * B
     di = small_dsa(lens, seed=17, k=2048)
     _, req, kv, _ = objs(di)
     rng = np.random.default_rng(6)
@@ -333,8 +344,9 @@ def test_decode_step_tiny_f32_case():
     print(_check_step(di, 256))
 
 
-def test_decode_step_fp8_ragged():
-    di = small_dsa([9000, 2047, 2048, 130, 4500], k=2048)
+@pytest.mark.parametrize("reps", [1, 2])
+def test_decode_step_fp8_ragged(reps):
+    di = small_dsa([9000, 2047, 2048, 130, 4500] * reps, k=2048)
     print(_check_step(di, 2048))
 
 
