@@ -212,7 +212,7 @@ def main():
         "timing": "HIP graph replay (one step per input set); eager per-call figure below",
         "eager_ms_per_step": eager_ms,
         "phases_us": {"scan": t_scan * 1e3, "topk": t_topk * 1e3, "mla": t_mla * 1e3},
-        "roofline": {"kernel": "scan_fp8_dma_kernel", "bound": "hbm", "achieved": scan_gbs,
+        "roofline": {"kernel": "scan_dma_kernel<0, 2> (fp8 keys)", "bound": "hbm", "achieved": scan_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
                      "note": "131072 tokens x 132 B per launch / average launch time "

@@ -708,7 +708,7 @@ struct MlaPlan {
   int rows_per_split;
 };
 
-constexpr int kWideMinReq = 8;
+constexpr int kWideMinReq = 4;
 
 MlaPlan plan_mla(int num_req, int n_heads, int k) {
   const int blocks = (k + kMBlk - 1) / kMBlk;

@@ -375,8 +375,17 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
 // The query split (hi/lo fp8 per head, as above) is computed once per
 // workgroup, 16 heads per wave, and handed to every wave through LDS.
 // ---------------------------------------------------------------------------
-constexpr int kTileBytes = kTile * kDim;    // 4 KB of fp8 codes
-constexpr int kSlotBytes = kTileBytes + 256; // codes + the 32 scales, twice
+// Per key kind: bytes per token row, per tile, and the DMA operations that
+// fill one ring slot (1 KB code moves plus one move of the 32 scales).
+template <int KIND>
+struct DmaTile {
+  static constexpr int kRow = KIND == KIND_FP8 ? kDim : kDim / 2;
+  static constexpr int kBytes = kTile * kRow;           // fp8 4 KB, int4 2 KB
+  static constexpr int kSlot = kBytes + 256;            // codes + the 32 scales, twice
+  static constexpr int kMoves = kBytes / 1024;
+  static constexpr int kOps = kMoves + 1;
+};
+constexpr int kTileBytes = DmaTile<KIND_FP8>::kBytes;
 constexpr int kFlushTiles = 32;             // tiles of scores staged per wave (4 KB)
 
 // Key tiles are read once: the non-temporal hint keeps them from evicting the
@@ -437,20 +446,34 @@ __device__ __forceinline__ void lds_dma4(uint8_t* lds, const float* g) {
                                    (__attribute__((address_space(3))) void*)lds, 4, 0, kNonTemporal);
 }
 
-// Wait until the tile issued RING - 1 refills ago has landed: every refill
-// is 5 vector-memory operations.
-template <int RING>
-__device__ __forceinline__ void wait_ring_tile() {
-  static_assert(RING >= 2 && RING <= 4, "ring of 2 to 4 tiles");
-  if constexpr (RING == 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  if constexpr (RING == 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  if constexpr (RING == 4) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+// The lane's 32 bytes of an int4 key row (two 16-byte reads) and the tile's
+// scale word, complete when the statement ends.
+__device__ __forceinline__ void lds_read_tile2_scale(u32x4 (&kr)[2], float& sc, const uint8_t* slot,
+                                                     const uint32_t (&rd)[2], uint32_t so) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)slot;
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(sc)
+      : "v"(base + rd[0]), "v"(base + rd[1]), "v"(base + so)
+      : "memory");
 }
 
-template <int RING>
-__global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kernel(ScanArgs a, int chunk,
-                                                                                   int page_shift) {
-  static_assert(kTileBytes == 4 * 1024, "four 1 KB DMA instructions per tile");
+// Wait until the tile issued RING - 1 refills ago has landed: every refill
+// is OPS vector-memory operations.
+template <int RING, int OPS>
+__device__ __forceinline__ void wait_ring_tile() {
+  static_assert(RING == 2 && (OPS == 5 || OPS == 3), "two-slot ring of fp8 or int4 tiles");
+  if constexpr (OPS == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  if constexpr (OPS == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+}
+
+template <int KIND, int RING>
+__global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int chunk, int page_shift) {
+  using TL = DmaTile<KIND>;
+  constexpr int kSlotBytes = TL::kSlot;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING][kWaves * kSlotBytes];
   __shared__ int pages[kMaxChunkPages];
   __shared__ __attribute__((aligned(16))) float wl[kHeads];   // w_j * 2^-E_j
@@ -488,16 +511,21 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   // this DMA too, which is what the prologue wants: all of it is one round
   // trip.)  Issue order after that wait: tiles 0 .. RING-2 (5 operations
   // each); the last ring position gets its tile once the split is done.
+  // The wave's 16 query rows (4 KB) land in its part of the score staging
+  // buffer, where its query split is written over them once read; the 64
+  // head weights land at the start of its slot in the last ring position,
+  // which is filled with a tile only after the split.
+  uint8_t* qraw = reinterpret_cast<uint8_t*>(&sbuf[wv][0]);
+  static_assert(sizeof(sbuf[0]) == 16 * kDim * 2, "a wave's staging buffer holds its 16 query rows");
   {
-    uint8_t* qslot = slot[RING - 1];
     const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
                                                         ((int64_t)b * kHeads + 16 * wv) * kDim) + 16 * lane;
     asm volatile("" ::: "memory");
-    lds_dma16<0>(qslot, qg);
-    lds_dma16<1024>(qslot, qg);
-    lds_dma16<2048>(qslot, qg);
-    lds_dma16<3072>(qslot, qg);
-    lds_dma4(qslot + kTileBytes, a.w + (int64_t)b * kHeads + lane);
+    lds_dma16<0>(qraw, qg);
+    lds_dma16<1024>(qraw, qg);
+    lds_dma16<2048>(qraw, qg);
+    lds_dma16<3072>(qraw, qg);
+    lds_dma4(slot[RING - 1], a.w + (int64_t)b * kHeads + lane);
   }
   const int L = min(max(Lraw, 0), a.max_seq_len);
   const int nprod = max(1, (L + chunk - 1) / chunk);
@@ -516,17 +544,29 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
   const int per = (ntile + kWaves - 1) / kWaves;
   const int my0 = wv * per;
   const int myn = max(0, min(ntile - my0, per));
-  const int r8 = lane >> 3;
-  const uint32_t goff = 128 * r8 + 16 * ((lane & 7) ^ r8);
-  uint32_t rd[4];
+  // fp8: a 1 KB move covers 8 rows of 128 bytes, chunk j of row r stored at
+  // j ^ (r % 8); int4: 16 rows of 64 bytes, chunk j of row r at j ^ f(r),
+  // f(r) = (r ^ (r / 4)) % 4, which puts the 16-byte reads of 8 consecutive
+  // rows at one chunk into 8 different bank groups
+  uint32_t goff;
+  uint32_t rd[KIND == KIND_FP8 ? 4 : 2];
+  if constexpr (KIND == KIND_FP8) {
+    const int r8 = lane >> 3;
+    goff = 128 * r8 + 16 * ((lane & 7) ^ r8);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rd[i] = m * 128 + 16 * ((4 * h + i) ^ (m & 7));
+    for (int i = 0; i < 4; ++i) rd[i] = m * 128 + 16 * ((4 * h + i) ^ (m & 7));
+  } else {
+    const int r16 = lane >> 2;
+    goff = 64 * r16 + 16 * ((lane & 3) ^ ((r16 ^ (r16 >> 2)) & 3));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rd[i] = m * 64 + 16 * ((2 * h + i) ^ ((m ^ (m >> 2)) & 3));
+  }
   const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
 
   // Every refill is issued, so the count of vector-memory operations between
   // a tile's DMA and its use is the same at every step: RING - 1 later tiles
-  // of 5 DMAs each (four 1 KB key moves and one for the 32 scales, which
-  // lanes 32..63 copy a second time).  vmcnt counts loads in issue order, so
+  // of TL::kOps DMAs each (four (fp8) or two (int4) 1 KB key moves and one
+  // for the 32 scales, which lanes 32..63 copy a second time).  vmcnt counts loads in issue order, so
   // waiting until at most that many are outstanding means the tile has landed
   // in LDS.  Refills past the wave's last tile (and every fill of a wave
   // without tiles) read pool row 0, which all of them share in L2, into a
@@ -540,18 +580,20 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
       if (page >= 0 && page < a.num_pages)
         row0 = (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1));
     }
-    const uint8_t* g = keys + row0 * kDim + goff;
+    const uint8_t* g = keys + row0 * TL::kRow + goff;
     asm volatile("" ::: "memory");
     lds_dma16<0>(slot, g);
     lds_dma16<1024>(slot, g);
-    lds_dma16<2048>(slot, g);
-    lds_dma16<3072>(slot, g);
-    lds_dma4(slot + kTileBytes, a.kscale + row0 + m);
+    if constexpr (TL::kMoves == 4) {
+      lds_dma16<2048>(slot, g);
+      lds_dma16<3072>(slot, g);
+    }
+    lds_dma4(slot + TL::kBytes, a.kscale + row0 + m);
   };
 
 #pragma unroll
   for (int r = 0; r + 1 < RING; ++r) issue(r, slot[r]);
-  wait_ring_tile<RING>();     // the query DMAs, RING - 1 tile groups ago
+  wait_ring_tile<RING, TL::kOps>();   // the query DMAs, RING - 1 tile groups ago
   const int qhead = 16 * wv + (lane >> 2);
   const int d0 = 32 * (lane & 3);
   bf16x8 raw[4];
@@ -561,18 +603,21 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
     uint32_t qoff[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) qoff[t] = (lane >> 2) * 2 * kDim + 2 * d0 + 16 * t;
-    lds_read_tile(qr, slot[RING - 1], qoff);
+    lds_read_tile(qr, qraw, qoff);
 #pragma unroll
     for (int t = 0; t < 4; ++t) raw[t] = __builtin_bit_cast(bf16x8, qr[t]);
-    wq = lds_read_f32(slot[RING - 1] + kTileBytes + 4 * qhead);
+    wq = lds_read_f32(slot[RING - 1] + 4 * qhead);
   }
 
-  // Query split into the score staging buffer (free until the first tile is
-  // scored): row `head` holds 16 chunks of 16 bytes, hi dims then lo dims,
-  // chunk c stored at position c ^ (head % 16) so that the reads below, 16
-  // rows at a time at one logical chunk, spread over all banks.
+  // Query operand in the score staging buffer (free until the first tile is
+  // scored).  fp8: row `head` holds 16 chunks of 16 bytes, hi dims then lo
+  // dims; int4: 16 chunks of 8 fp16, dims 8c..8c+7 in the order
+  // (0,4,1,5,2,6,3,7) that the nibble conversion produces.  Chunk c is stored
+  // at position c ^ (head % 16) so that the reads below, 16 rows at a time at
+  // one logical chunk, spread over all banks.  A wave writes only the rows of
+  // its own 16 heads, over its own raw query rows, which it has read.
   uint8_t* qx = reinterpret_cast<uint8_t*>(&sbuf[0][0]);
-  static_assert(sizeof(sbuf) == kHeads * 2 * kDim, "query split fills the staging buffer");
+  static_assert(sizeof(sbuf) == kHeads * 2 * kDim, "query operand fills the staging buffer");
   {
     float amax = 0.f;
 #pragma unroll
@@ -583,79 +628,116 @@ __global__ __launch_bounds__(kThreads, RING >= 4 ? 2 : 3) void scan_fp8_dma_kern
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     int e2 = 0;
     if (amax > 0.f) (void)frexpf(amax, &e2);
-    const int E = (amax > 0.f) ? 8 - e2 : 0;
-    const float sc = ldexpf(1.0f, E);
-    if ((lane & 3) == 0) wl[qhead] = wq * ldexpf(1.0f, -E);
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {              // dword d: dims d0 + 4d .. +3
-      float x[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = (float)raw[d >> 1][(d & 1) * 4 + j] * sc;
-      int ph = 0;
-      ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], ph, false);
-      ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], ph, true);
-      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, false);
-      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, true);
-      int pl = 0;
-      pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], pl, false);
-      pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], pl, true);
-      hi[d] = (uint32_t)ph;
-      lo[d] = (uint32_t)pl;
-    }
     uint8_t* row = qx + qhead * 2 * kDim;
     const int sw = qhead & 15;
-    const int c0 = d0 / 16;
-    *reinterpret_cast<u32x4*>(row + 16 * (c0 ^ sw)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *reinterpret_cast<u32x4*>(row + 16 * ((c0 + 1) ^ sw)) = u32x4{hi[4], hi[5], hi[6], hi[7]};
-    *reinterpret_cast<u32x4*>(row + 16 * ((8 + c0) ^ sw)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    *reinterpret_cast<u32x4*>(row + 16 * ((9 + c0) ^ sw)) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    if constexpr (KIND == KIND_FP8) {
+      const int E = (amax > 0.f) ? 8 - e2 : 0;
+      const float sc = ldexpf(1.0f, E);
+      if ((lane & 3) == 0) wl[qhead] = wq * ldexpf(1.0f, -E);
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {              // dword d: dims d0 + 4d .. +3
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (float)raw[d >> 1][(d & 1) * 4 + j] * sc;
+        int ph = 0;
+        ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], ph, false);
+        ph = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], ph, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ph, true);
+        int pl = 0;
+        pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - h01[0], x[1] - h01[1], pl, false);
+        pl = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], pl, true);
+        hi[d] = (uint32_t)ph;
+        lo[d] = (uint32_t)pl;
+      }
+      const int c0 = d0 / 16;
+      *reinterpret_cast<u32x4*>(row + 16 * (c0 ^ sw)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(row + 16 * ((c0 + 1) ^ sw)) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+      *reinterpret_cast<u32x4*>(row + 16 * ((8 + c0) ^ sw)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      *reinterpret_cast<u32x4*>(row + 16 * ((9 + c0) ^ sw)) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    } else {
+      // the largest |q| of the head scaled into [2^14, 2^15): exact in fp16
+      const int E = (amax > 0.f) ? 15 - e2 : 0;
+      const float sc = ldexpf(1.0f, E);
+      if ((lane & 3) == 0) wl[qhead] = wq * ldexpf(1.0f, -E);
+      constexpr int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {            // chunk d0 / 8 + t: dims d0 + 8t .. +7
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)raw[t][order[e]] * sc);
+        *reinterpret_cast<f16x8*>(row + 16 * ((d0 / 8 + t) ^ sw)) = v;
+      }
+    }
   }
   lds_barrier();
-  // qs[mt][part*2 + sI]: 32 bytes (dims 64h + 32 sI ..) of part `part` of head 32 mt + m
+  // fp8: qs[mt][part*2 + sI] = 32 bytes (dims 64h + 32 sI ..) of part `part`
+  // of head 32 mt + m; int4: qa[mt][t] = fp16 dims 64h + 8t .. of that head
   i32x8 qs[2][4];
+  f16x8 qa[2][8];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt) {
+    const int head = 32 * mt + m;
+    const uint8_t* row = qx + head * 2 * kDim;
+    if constexpr (KIND == KIND_FP8) {
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
+      for (int part = 0; part < 2; ++part)
 #pragma unroll
-      for (int sI = 0; sI < 2; ++sI) {
-        const int head = 32 * mt + m;
-        const uint8_t* row = qx + head * 2 * kDim;
-        const int c = part * 8 + 4 * h + 2 * sI;
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(row + 16 * (c ^ (head & 15)));
-        const u32x4 v1 = *reinterpret_cast<const u32x4*>(row + 16 * ((c + 1) ^ (head & 15)));
-        qs[mt][part * 2 + sI] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      }
+        for (int sI = 0; sI < 2; ++sI) {
+          const int c = part * 8 + 4 * h + 2 * sI;
+          const u32x4 v0 = *reinterpret_cast<const u32x4*>(row + 16 * (c ^ (head & 15)));
+          const u32x4 v1 = *reinterpret_cast<const u32x4*>(row + 16 * ((c + 1) ^ (head & 15)));
+          qs[mt][part * 2 + sI] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        qa[mt][t] = *reinterpret_cast<const f16x8*>(row + 16 * ((8 * h + t) ^ (head & 15)));
+    }
+  }
   lds_barrier();   // the staging buffer takes scores from here on
   const f32x4* wl4 = reinterpret_cast<const f32x4*>(wl + 4 * h);
   issue(RING - 1, slot[RING - 1]);    // the query rows are no longer needed
 
   // Score of token m of the wave's j-th tile (the same in lanes m and m + 32).
   auto consume = [&](int j, uint8_t* slot) -> float {
-    wait_ring_tile<RING>();
-    u32x4 kr[4];
+    wait_ring_tile<RING, TL::kOps>();
     float scale;
-    lds_read_tile_scale(kr, scale, slot, rd, kTileBytes + 4 * lane);
-    const int page = pages[((my0 + j) * kTile) >> page_shift];
-    const bool ok = page >= 0 && page < a.num_pages;
     f32x16 acc0 = {};
     f32x16 acc1 = {};
+    if constexpr (KIND == KIND_FP8) {
+      u32x4 kr[4];
+      lds_read_tile_scale(kr, scale, slot, rd, TL::kBytes + 4 * lane);
 #pragma unroll
-    for (int sI = 0; sI < 2; ++sI) {
-      const u32x4 k0 = kr[2 * sI];
-      const u32x4 k1 = kr[2 * sI + 1];
-      const i32x8 kb = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
-                        (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+      for (int sI = 0; sI < 2; ++sI) {
+        const u32x4 k0 = kr[2 * sI];
+        const u32x4 k1 = kr[2 * sI + 1];
+        const i32x8 kb = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                          (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[0][part * 2 + sI], kb, acc0,
-                                                               0, 0, 0, 127, 0, 127);
-        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[1][part * 2 + sI], kb, acc1,
-                                                               0, 0, 0, 127, 0, 127);
+        for (int part = 0; part < 2; ++part) {
+          acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[0][part * 2 + sI], kb, acc0,
+                                                                 0, 0, 0, 127, 0, 127);
+          acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qs[1][part * 2 + sI], kb, acc1,
+                                                                 0, 0, 0, 127, 0, 127);
+        }
+      }
+    } else {
+      u32x4 kr[2];
+      lds_read_tile2_scale(kr, scale, slot, rd, TL::kBytes + 4 * lane);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 r4 = kr[t >> 2];
+        const uint32_t d = (t & 3) == 0 ? r4.x : (t & 3) == 1 ? r4.y : (t & 3) == 2 ? r4.z : r4.w;
+        const f16x8 kb = int4x8_to_f16x8(d);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][t], kb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][t], kb, acc1, 0, 0, 0);
       }
     }
+    const int page = pages[((my0 + j) * kTile) >> page_shift];
+    const bool ok = page >= 0 && page < a.num_pages;
     // the slot's reads are complete (the MFMAs consumed them): refill it
     issue(j + RING, slot);
     float part = 0.f;
@@ -773,19 +855,17 @@ template <int KIND>
 hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   const bool gather = a.positions != nullptr;
   const int max_items = gather ? a.n_pos : a.max_seq_len;
-  const bool dma = KIND == KIND_FP8 && !gather;
   constexpr int kRingTiles = 2;
-  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, dma ? (kRingTiles >= 4 ? 2 : 3) : 2);
+  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, gather ? 2 : 3);
   // the DMA scan stages a slice's page ids with one load per thread
-  if (dma && (chunk + a.page_size - 1) / a.page_size > std::min(kMaxChunkPages, kThreads)) return hipErrorInvalidValue;
+  if (!gather && (chunk + a.page_size - 1) / a.page_size > std::min(kMaxChunkPages, kThreads))
+    return hipErrorInvalidValue;
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   const int ps = ilog2(a.page_size);
-  if (dma)
-    hipLaunchKernelGGL(scan_fp8_dma_kernel<kRingTiles>, grid, dim3(kThreads), 0, s, a, chunk, ps);
-  else if (gather)
-    hipLaunchKernelGGL((scan_kernel<KIND, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+  if (!gather)
+    hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   else
-    hipLaunchKernelGGL((scan_kernel<KIND, false>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+    hipLaunchKernelGGL((scan_kernel<KIND, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   return hipGetLastError();
 }
 
