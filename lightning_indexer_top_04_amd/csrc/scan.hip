@@ -14,23 +14,14 @@
 // elements, below 2^-10 of their head's largest, keep an error under 2^-10
 // in scaled units.  acc += hi.k + lo.k, and the head weight absorbs 2^-E.
 // int4 keys (compact keys of the two-stage search) use v_mfma_f32_32x32x16_f16
-// (below).  Each lane owns one token of the
-// 32-token tile and half of its key row (64 contiguous bytes for fp8, 32 for
-// int4), so a tile is fetched with 16-byte loads straight from the page, with
-// no LDS staging.  The dot product does not depend on the order of the K index,
-// so the query rows are loaded in exactly the order the key bytes arrive.
-// ReLU, the head weights and the head sum stay in registers: a lane sums the
-// 32 heads it holds, one cross-half swap adds the other 32, and lanes 0..31
-// store 32 consecutive scores.
+// on an exact nibble-to-fp16 conversion (below).  ReLU, the head weights and
+// the head sum stay in registers: a lane sums the 32 heads it holds and one
+// cross-half swap adds the other 32.
 //
-// Memory path (contiguous mode): a 32-token tile is one contiguous block of a
-// page (4 KB of fp8 codes, 2 KB of int4), fetched with 16-byte loads in which
-// each instruction covers 1 KB contiguously; every wave keeps four tiles in
-// flight in registers while it computes one, and passes each tile
-// through its own padded LDS slot to reach the MFMA lane layout (row n of
-// the tile to lanes n and n+32).  The page ids of the workgroup's slice are
-// staged in LDS first, so no key load waits on the page table.  In gather
-// mode (scattered positions) each lane loads its own row directly.
+// Memory paths: a contiguous page walk (every cached token of a request)
+// streams 32-token tiles from the pages into an LDS ring by global->LDS DMA
+// (scan_dma_kernel); gathered positions (the exact rescoring of the two-stage
+// search) load each lane's own key row into registers (scan_gather_kernel).
 #include "lsi_internal.hpp"
 
 namespace lsi {
@@ -51,10 +42,8 @@ constexpr int KIND_INT4 = 1;
 constexpr uint32_t kAbsent = 0xFFFFFFFFu;
 
 struct TileFetch {
-  // contiguous mode: instruction i of the tile (1 KB each); gather mode: the
-  // lane's own key half (fp8: 64 bytes, int4: raw[0..1] = 32 bytes)
-  u32x4 raw[4];
-  float scale;    // gather mode: kAbsent when the position or page is invalid
+  u32x4 raw[4];   // the lane's key half (fp8: 64 bytes, int4: raw[0..1] = 32 bytes)
+  float scale;    // kAbsent when the position or page is invalid
 };
 
 // ---------------------------------------------------------------------------
@@ -82,17 +71,16 @@ struct QOp {
   using T = typename std::conditional<KIND == KIND_FP8, bf16x8, f16x8>::type;
 };
 
-template <int KIND, bool GATHER>
-__global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk, int page_shift) {
+// Gathered positions: lane (m, h) loads half h of the key row of position
+// m of its tile (64 bytes fp8, 32 int4) straight into registers; two tiles
+// per wave in flight.
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 2) void scan_gather_kernel(ScanArgs a, int chunk, int page_shift) {
   constexpr int ROW = KIND == KIND_FP8 ? kDim : kDim / 2;   // key bytes per token
   using QT = typename QOp<KIND>::T;
-  constexpr int NINS = (kTile * ROW) / 1024;                // load instructions per tile
-  constexpr int kRing = GATHER ? 2 : 4;                     // tiles in the prefetch ring
-  constexpr int LROW = ROW + 16;                            // padded LDS row (bytes)
-  __shared__ int pages[GATHER ? 1 : kMaxChunkPages];
+  constexpr int kRing = 2;                                  // tiles in the prefetch ring
   __shared__ float inv_scale[kWaves * kHeads];
   __shared__ __attribute__((aligned(16))) float wl[kWaves * kHeads];   // w_j * 2^-E_j
-  __shared__ __attribute__((aligned(16))) uint8_t stage[GATHER ? 16 : kWaves * kTile * LROW];
 
   if (a.zero_ptr) {
     const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * kThreads;
@@ -107,19 +95,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   const int m = lane & 31;
   const int h = lane >> 5;
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-  const int n_items = GATHER ? a.n_pos : L;
+  const int n_items = a.n_pos;
   const int nprod = max(1, (n_items + chunk - 1) / chunk);
   if ((int)blockIdx.x >= nprod) return;
   const int begin = blockIdx.x * chunk;
   const int end = min(begin + chunk, n_items);
   const int ntile = max(0, (end - begin + kTile - 1) / kTile);
-
-  if (!GATHER) {
-    const int npg = (end - begin + a.page_size - 1) >> page_shift;
-    const int pg0 = begin >> page_shift;
-    for (int i = tid; i < npg; i += kThreads)
-      pages[i] = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
-  }
 
   // query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7
   const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
@@ -228,69 +209,32 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   auto fetch = [&](int tile_in) {
     TileFetch f;
     const int tile = min(tile_in, ntile - 1);
-    if (GATHER) {
-      const int it = min(begin + tile * kTile + m, end - 1);
-      const int pos = a.positions[(int64_t)b * a.n_pos + it];
-      const bool in = pos >= 0 && pos < L;
-      const int page = a.page_table[(int64_t)b * a.max_pages + ((in ? pos : 0) >> page_shift)];
-      const bool ok = in && page >= 0 && page < a.num_pages;
-      const int64_t row = ok ? (int64_t)page * a.page_size + (pos & (a.page_size - 1)) : 0;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(
-          static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
+    const int it = min(begin + tile * kTile + m, end - 1);
+    const int pos = a.positions[(int64_t)b * a.n_pos + it];
+    const bool in = pos >= 0 && pos < L;
+    const int page = a.page_table[(int64_t)b * a.max_pages + ((in ? pos : 0) >> page_shift)];
+    const bool ok = in && page >= 0 && page < a.num_pages;
+    const int64_t row = ok ? (int64_t)page * a.page_size + (pos & (a.page_size - 1)) : 0;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(
+        static_cast<const uint8_t*>(a.keys) + row * ROW + h * (ROW / 2));
 #pragma unroll
-      for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
-      const float sc = a.kscale[row];
-      f.scale = ok ? sc : __uint_as_float(kAbsent);
-    } else {
-      // the whole tile lies in one page
-      const int t0 = tile * kTile;                              // offset in the slice
-      const int page = pages[t0 >> page_shift];
-      const bool ok = page >= 0 && page < a.num_pages;
-      const int64_t row0 = ok ? (int64_t)page * a.page_size + ((begin + t0) & (a.page_size - 1)) : 0;
-      const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.keys) + row0 * ROW);
-#pragma unroll
-      for (int i = 0; i < NINS; ++i) f.raw[i] = tb[i * 64 + lane];
-      f.scale = a.kscale[row0 + m];
-    }
+    for (int i = 0; i < ROW / 32; ++i) f.raw[i] = kp[i];
+    const float sc = a.kscale[row];
+    f.scale = ok ? sc : __uint_as_float(kAbsent);
     return f;
   };
-  // Contiguous mode: route a fetched tile through this wave's LDS slot and
-  // return the lane's key half (row m, bytes h*ROW/2 ..) as dwords.
-  uint8_t* my_stage = stage + (GATHER ? 0 : wave * kTile * LROW);
-  auto transpose = [&](const TileFetch& f, u32x4* out) {
-#pragma unroll
-    for (int i = 0; i < NINS; ++i) {
-      const int byte = (i * 64 + lane) * 16;
-      *reinterpret_cast<u32x4*>(my_stage + (byte / ROW) * LROW + (byte % ROW)) = f.raw[i];
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < ROW / 32; ++i)
-      out[i] = *reinterpret_cast<const u32x4*>(my_stage + m * LROW + h * (ROW / 2) + 16 * i);
-    __builtin_amdgcn_wave_barrier();
-  };
 
-  // Consume tile `tile` held in f, refill f with the tile four wave-steps
-  // ahead, then compute and store.  Four TileFetch registers form a ring that
-  // the loop below walks with static names, so four tiles stay in flight.
+  // Consume tile `tile` held in f, refill f with the tile two wave-steps
+  // ahead, then compute and store.  Two TileFetch registers form a ring that
+  // the loop below walks with static names, so two tiles stay in flight.
   auto consume = [&](TileFetch& f, int tile) {
     u32x4 kr[ROW / 32];
-    if (GATHER) {
 #pragma unroll
-      for (int i = 0; i < ROW / 32; ++i) kr[i] = f.raw[i];
-    } else {
-      transpose(f, kr);
-    }
+    for (int i = 0; i < ROW / 32; ++i) kr[i] = f.raw[i];
     const float scale = f.scale;
     const int item = begin + tile * kTile + m;
     const bool valid = item < end;
-    bool ok;
-    if (GATHER) {
-      ok = __float_as_uint(scale) != kAbsent;
-    } else {
-      const int page = pages[(tile * kTile) >> page_shift];
-      ok = page >= 0 && page < a.num_pages;
-    }
+    const bool ok = __float_as_uint(scale) != kAbsent;
     f = fetch(tile + kRing * kWaves);   // clamped at the end of the slice
     f32x16 acc0 = {};
     f32x16 acc1 = {};
@@ -337,43 +281,27 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a, int chunk
   };
 
   if (wave < ntile) {
-    if constexpr (kRing == 4) {
-      TileFetch f0 = fetch(wave);
-      TileFetch f1 = fetch(wave + kWaves);
-      TileFetch f2 = fetch(wave + 2 * kWaves);
-      TileFetch f3 = fetch(wave + 3 * kWaves);
-      for (int tile = wave; tile < ntile; tile += 4 * kWaves) {
-        consume(f0, tile);
-        if (tile + kWaves >= ntile) break;
-        consume(f1, tile + kWaves);
-        if (tile + 2 * kWaves >= ntile) break;
-        consume(f2, tile + 2 * kWaves);
-        if (tile + 3 * kWaves >= ntile) break;
-        consume(f3, tile + 3 * kWaves);
-      }
-    } else {
-      TileFetch f0 = fetch(wave);
-      TileFetch f1 = fetch(wave + kWaves);
-      for (int tile = wave; tile < ntile; tile += 2 * kWaves) {
-        consume(f0, tile);
-        if (tile + kWaves >= ntile) break;
-        consume(f1, tile + kWaves);
-      }
+    TileFetch f0 = fetch(wave);
+    TileFetch f1 = fetch(wave + kWaves);
+    for (int tile = wave; tile < ntile; tile += 2 * kWaves) {
+      consume(f0, tile);
+      if (tile + kWaves >= ntile) break;
+      consume(f1, tile + kWaves);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// fp8 keys, contiguous page walk: the prefetch ring lives in LDS and is filled
-// by global->LDS DMA (global_load_lds_dwordx4), so no VGPRs hold tiles in
-// flight and no instruction copies them into LDS.  Each DMA instruction moves
-// 1 KB (8 token rows) contiguously; a lane's 16 bytes land at base + 16*lane,
-// so the lane fetches the chunk that belongs at that LDS position: row r of
-// the 8, chunk c ^ r.  Stored this way (16-byte chunk j of row m at chunk
-// j ^ (m & 7)), the per-lane 16-byte reads of the MFMA layout hit eight
-// different bank groups in every group of eight lanes.
-// The query split (hi/lo fp8 per head, as above) is computed once per
-// workgroup, 16 heads per wave, and handed to every wave through LDS.
+// Contiguous page walk (fp8 or int4 keys): the prefetch ring lives in LDS and
+// is filled by global->LDS DMA (global_load_lds_dwordx4), so no VGPRs hold
+// tiles in flight and no instruction copies them into LDS.  Each DMA
+// instruction moves 1 KB (8 fp8 or 16 int4 token rows) contiguously; a
+// lane's 16 bytes land at base + 16*lane, so the lane fetches the chunk that
+// belongs at that LDS position (the chunk order within a row is permuted per
+// row, see goff/rd below), which spreads the per-lane 16-byte reads of the
+// MFMA layout over all bank groups.  The query operand (hi/lo fp8 split, or
+// exact fp16) is computed once per workgroup, 16 heads per wave, and handed
+// to every wave through LDS.
 // ---------------------------------------------------------------------------
 // Per key kind: bytes per token row, per tile, and the DMA operations that
 // fill one ring slot (1 KB code moves plus one move of the 32 scales).
@@ -865,7 +793,7 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   if (!gather)
     hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, a, chunk, ps);
   else
-    hipLaunchKernelGGL((scan_kernel<KIND, true>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+    hipLaunchKernelGGL(scan_gather_kernel<KIND>, grid, dim3(kThreads), 0, s, a, chunk, ps);
   return hipGetLastError();
 }
 
