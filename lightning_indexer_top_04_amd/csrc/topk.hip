@@ -33,6 +33,7 @@ using namespace topk;
 constexpr int kBlock = 512;
 constexpr int kLdsCand = 16384;          // candidates refined in LDS
 constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
+constexpr int kRefPer = 8;               // candidates per thread in a refinement pass
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   int L;
@@ -186,7 +187,7 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
         lkey[i] = float_key(row[slot]) - kbase;
       }
       in_lds = true;
-      __syncthreads();
+      __syncthreads();   // (the list was written by other threads)
     }
     const int shift = stage == 0 ? kb_lo : stage == 1 ? 0 : stage == 2 ? 20 : stage == 3 ? 8 : 0;
     const uint32_t mask = (1u << nbits) - 1u;
@@ -195,44 +196,61 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
       if (!by_key) return (uint32_t)out_value(a, r, slot);
       return in_lds ? lkey[i] : float_key(row[slot]) - kbase;
     };
+    // with the candidates in LDS only LDS traffic needs ordering: the winners
+    // written to the output are never read back here
     for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
-    __syncthreads();
+    wg_sync(in_lds);
     for (uint32_t i = threadIdx.x; i < n; i += NT) {
       int slot;
       const uint32_t v = value(i, slot);
       atomicAdd(&hist[(v >> shift) & mask], 1u);
     }
-    __syncthreads();
+    wg_sync(in_lds);
     uint32_t better;
-    const int bin = find_threshold<NT>(hist, need, by_key, tmp, &better);
-    // ordered pass: winners (better than bin) go out, equal ones stay
+    const int bin = find_threshold<NT>(hist, need, by_key, tmp, &better, in_lds);
+    // ordered pass: winners (better than bin) go out, equal ones stay; a
+    // thread takes kRefPer consecutive candidates, so one block scan orders
+    // NT * kRefPer of them (all reads of a batch precede its writes, which
+    // land at or below the positions read)
     uint32_t keep = 0;
-    for (uint32_t base = 0; base < n; base += NT) {
-      const uint32_t i = base + threadIdx.x;
-      int slot = -1;
-      uint32_t v = 0, flag_win = 0, flag_eq = 0;
-      if (i < n) {
-        v = value(i, slot);
-        const int d = (int)((v >> shift) & mask);
-        flag_eq = d == bin;
-        flag_win = by_key ? (d > bin) : (d < bin);
+    for (uint32_t base = 0; base < n; base += NT * kRefPer) {
+      const uint32_t i0 = base + threadIdx.x * kRefPer;
+      int slot[kRefPer];
+      uint32_t v[kRefPer], win = 0, eq = 0;
+#pragma unroll
+      for (int j = 0; j < kRefPer; ++j) {
+        slot[j] = -1;
+        v[j] = 0;
+        if (i0 + j < n) {
+          v[j] = value(i0 + j, slot[j]);
+          const int d = (int)((v[j] >> shift) & mask);
+          eq |= (uint32_t)(d == bin) << j;
+          win |= (uint32_t)(by_key ? (d > bin) : (d < bin)) << j;
+        }
       }
       uint32_t tot;
-      const uint32_t pre = block_excl_scan<NT>(flag_win | (flag_eq << 16), tmp, &tot);
-      if (flag_win && out_pos + (pre & 0xFFFF) < (uint32_t)a.k)
-        emit(a, r, out_pos + (pre & 0xFFFF), out_value(a, r, slot));
-      if (flag_eq) {
-        const uint32_t j = keep + (pre >> 16);
-        if (in_lds) {
-          lslot[j] = slot;
-          if (by_key) lkey[j] = v;
-        } else {
-          list[j] = slot;
+      const uint32_t pre = block_excl_scan<NT>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot, in_lds);
+      uint32_t ow = out_pos + (pre & 0xFFFF);
+      uint32_t oe = keep + (pre >> 16);
+#pragma unroll
+      for (int j = 0; j < kRefPer; ++j) {
+        if ((win >> j) & 1u) {
+          if (ow < (uint32_t)a.k) emit(a, r, ow, out_value(a, r, slot[j]));
+          ++ow;
+        }
+        if ((eq >> j) & 1u) {
+          if (in_lds) {
+            lslot[oe] = slot[j];
+            if (by_key) lkey[oe] = v[j];
+          } else {
+            list[oe] = slot[j];
+          }
+          ++oe;
         }
       }
       out_pos += tot & 0xFFFF;
       keep += tot >> 16;
-      __syncthreads();
+      wg_sync(in_lds);
     }
     need -= better;
     n = keep;
@@ -241,7 +259,6 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
   const uint32_t take = min(n, need);
   emit_range<NT>(a, r, out_pos, take, [&](uint32_t i) { return in_lds ? lslot[i] : list[i]; });
   out_pos += take;
-  __syncthreads();
   if (out_pos < (uint32_t)a.k) emit_range<NT>(a, r, out_pos, (uint32_t)a.k - out_pos, [](uint32_t) { return -1; });
   if (threadIdx.x == 0) a.count[r] = (int32_t)min(out_pos, (uint32_t)a.k);
 }
@@ -392,21 +409,34 @@ __global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
   const uint32_t n = rec[2];
   int32_t* list = ws.list + (size_t)r * a.max_len;
   const bool in_lds = n <= (uint32_t)kLdsCand;
-  for (uint32_t b = threadIdx.x; b < n; b += kBlock * kGather) {
-    int2 e[kGather];
-#pragma unroll
-    for (int u = 0; u < kGather; ++u) e[u] = b < (uint32_t)(kBlock * kGather) ? e0[u] : cand[min(b + u * kBlock, n - 1)];
+  if (in_lds) {
 #pragma unroll
     for (int u = 0; u < kGather; ++u) {
-      const uint32_t i = b + u * kBlock;
-      if (i >= n) continue;
-      if (in_lds) {
-        lslot[i] = e[u].x;
-        lkey[i] = (uint32_t)e[u].y;
-      } else {
-        list[i] = e[u].x;
+      const uint32_t i = threadIdx.x + u * kBlock;
+      if (i < n) {
+        lslot[i] = e0[u].x;
+        lkey[i] = (uint32_t)e0[u].y;
       }
     }
+    if (n > (uint32_t)(kBlock * kGather)) {
+      // the rest in one batch of loads (a loop of smaller batches would
+      // cost a round trip each)
+      constexpr int kRest = kLdsCand / kBlock - kGather;
+      int2 e[kRest];
+#pragma unroll
+      for (int u = 0; u < kRest; ++u)
+        e[u] = cand[min(threadIdx.x + (u + kGather) * kBlock, n - 1)];
+#pragma unroll
+      for (int u = 0; u < kRest; ++u) {
+        const uint32_t i = threadIdx.x + (u + kGather) * kBlock;
+        if (i < n) {
+          lslot[i] = e[u].x;
+          lkey[i] = (uint32_t)e[u].y;
+        }
+      }
+    }
+  } else {
+    for (uint32_t i = threadIdx.x; i < n; i += kBlock) list[i] = cand[i].x;
   }
   __syncthreads();
   refine_cands<kBlock, kLdsCand>(a, r, n, (uint32_t)a.k - better, better, list, in_lds, hist, tmp, lkey,
@@ -451,12 +481,26 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   // pass 0: key range of the row
   // (each streaming pass issues kBatch loads per thread before using any;
   // indexes past the end are clamped to the last element, which is harmless
-  // for the minimum and maximum and not counted elsewhere)
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int b = tid; b < L; b += kRowThreads * kBatch) {
-    uint32_t kk[kBatch];
+  // for the minimum and maximum and not counted elsewhere.  The first batch
+  // stays in registers for the later passes: rows of up to 8192 are read
+  // from memory once.)
+  constexpr int kStride = kRowThreads * kBatch;
+  uint32_t k0[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) kk[j] = float_key(row[min(b + j * kRowThreads, L - 1)]);
+  for (int j = 0; j < kBatch; ++j) k0[j] = float_key(row[min(tid + j * kRowThreads, L - 1)]);
+  auto keys_of = [&](int b, uint32_t (&kk)[kBatch]) {
+    if (b == tid) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) kk[j] = k0[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) kk[j] = float_key(row[min(b + j * kRowThreads, L - 1)]);
+    }
+  };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int b = tid; b < L; b += kStride) {
+    uint32_t kk[kBatch];
+    keys_of(b, kk);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       kmin = min(kmin, kk[j]);
@@ -483,12 +527,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   const int span = range ? 32 - __clz(range) : 0;      // bits of the range
   const int shift = span > 12 ? span - 12 : 0;
   // pass 1
-  for (int b = tid; b < L; b += kRowThreads * kBatch) {
-    uint32_t d[kBatch];
+  for (int b = tid; b < L; b += kStride) {
+    uint32_t kk[kBatch];
+    keys_of(b, kk);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) d[j] = (float_key(row[min(b + j * kRowThreads, L - 1)]) - kmin) >> shift;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) atomicAdd(&hist[d[j]], b + j * kRowThreads < L ? 1u : 0u);
+    for (int j = 0; j < kBatch; ++j) atomicAdd(&hist[(kk[j] - kmin) >> shift], b + j * kRowThreads < L ? 1u : 0u);
   }
   __syncthreads();
   uint32_t better;
@@ -496,10 +539,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   int32_t* list = carve(a.ws, a.num_req, a.max_len).list + (size_t)r * a.max_len;
   // pass 2
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = tid; b < L; b += kRowThreads * kBatch) {
+  for (int b = tid; b < L; b += kStride) {
     uint32_t rel[kBatch];
+    keys_of(b, rel);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) rel[j] = float_key(row[min(b + j * kRowThreads, L - 1)]) - kmin;
+    for (int j = 0; j < kBatch; ++j) rel[j] -= kmin;
     uint64_t bw[kBatch], be[kBatch];
     uint32_t nw = 0, ne = 0;
 #pragma unroll

@@ -35,11 +35,20 @@ __host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   return w;
 }
 
+// Workgroup barrier.  With lds_only it orders LDS traffic only: a plain
+// __syncthreads also waits for this wave's global stores to complete, which
+// in a loop that writes results as it goes costs a memory round trip per
+// iteration.
+__device__ __forceinline__ void wg_sync(bool lds_only) {
+  if (lds_only) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __syncthreads();
+}
+
 // Block-wide exclusive scan of one value per thread (NT threads); T is
 // uint32_t or uint64_t (two 32-bit counts packed, each summed on its own as
 // long as neither overflows).  tmp needs NT/64 values of T.
 template <int NT, class T>
-__device__ T block_excl_scan(T v, T* tmp, T* total) {
+__device__ T block_excl_scan(T v, T* tmp, T* total, bool lds_only = false) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   T inc = v;
@@ -49,7 +58,7 @@ __device__ T block_excl_scan(T v, T* tmp, T* total) {
     if (lane >= o) inc += t;
   }
   if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
+  wg_sync(lds_only);
   T base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
@@ -57,7 +66,7 @@ __device__ T block_excl_scan(T v, T* tmp, T* total) {
     if (i < wave) base += t;
     tot += t;
   }
-  __syncthreads();
+  wg_sync(lds_only);
   *total = tot;
   return base + inc - v;
 }
@@ -67,7 +76,7 @@ __device__ T block_excl_scan(T v, T* tmp, T* total) {
 // receives the count of all bins before it.  tmp needs 32 words.
 template <int NT>
 __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uint32_t* tmp,
-                              uint32_t* better) {
+                              uint32_t* better, bool lds_only = false) {
   constexpr int per = kBins / NT;
   const int t = threadIdx.x;
   uint32_t local = 0;
@@ -77,7 +86,7 @@ __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uin
     local += cnt[desc ? kBins - 1 - q : q];
   }
   uint32_t tot;
-  const uint32_t excl = block_excl_scan<NT>(local, tmp, &tot);
+  const uint32_t excl = block_excl_scan<NT>(local, tmp, &tot, lds_only);
   if (excl < need && excl + local >= need) {
     uint32_t acc = excl;
     for (int i = 0; i < per; ++i) {
@@ -91,10 +100,10 @@ __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uin
       acc += cnt[bin];
     }
   }
-  __syncthreads();
+  wg_sync(lds_only);
   const int bin = (int)tmp[24];
   *better = tmp[25];
-  __syncthreads();
+  wg_sync(lds_only);
   return bin;
 }
 
