@@ -14,8 +14,9 @@ loop would run them; the timed region covers exactly K steps.
 
 Printed (one JSON line): tokens/s = 131072 * steps / time (whole step timed,
 inputs resident in HBM), decode steps/s, per-phase averages from HIP events on
-the launch stream, the scan's roofline (algorithmic 132 B per token against
-8 TB/s), a sustained scan of 32 x 128K tokens in one launch, the CPU
+the launch stream, the scan's roofline (algorithmic 136 B per token: 128 key
+bytes, a 4-byte scale and a 4-byte score written, against 8 TB/s), a
+sustained scan of 32 x 128K tokens in one launch, the CPU
 oracle's throughput on a bounded sample of the same step, and (unless
 --no-extra) the ragged 64-request decode step, the two-stage compact-key
 search at 512K and the prefill indexer chunk, each against its own roofline.
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer-scanned tokens/s and decode steps/s (index+top-k+sparse attn) @128K ctx"
 HBM_PEAK_GBS = 8000.0
 BYTES_PER_TOKEN = 132          # 128 fp8 key bytes + 4-byte scale
+SCAN_BYTES_PER_TOKEN = BYTES_PER_TOKEN + 4   # ... and the fp32 score the scan writes
 
 
 def parse():
@@ -177,7 +179,7 @@ def main():
     t_scan = per_launch_ms(g_scan)
     t_topk = per_launch_ms(g_topk)
     t_mla = per_launch_ms(g_mla)
-    scan_gbs = L * BYTES_PER_TOKEN / (t_scan * 1e-3) / 1e9
+    scan_gbs = L * SCAN_BYTES_PER_TOKEN / (t_scan * 1e-3) / 1e9
 
     # ---- sustained scan: all R requests in one launch ---------------------
     req_all = lsi.Requests(di.seq_lens, di.page_table, L)
@@ -186,10 +188,19 @@ def main():
     stream = torch.cuda.current_stream()
     for _ in range(3):
         lsi.index_scores(ik, req_all, di.q_idx, di.w, scores=scores_all, stream=stream)
+    torch.cuda.synchronize()
+    # back-to-back launches on the stream (the figure reported) and the same
+    # launches replayed from one graph (for comparison: graph replays insert
+    # their own inter-node synchronisation, which is slower here)
     t_sus = event_loop(lambda i: lsi.index_scores(ik, req_all, di.q_idx, di.w,
                                                   scores=scores_all, stream=stream),
                        n_sus, stream)
-    sus_gbs = R * L * BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
+    g_sus = capture([lambda: lsi.index_scores(ik, req_all, di.q_idx, di.w, scores=scores_all)
+                     for _ in range(n_sus)])
+    g_sus.replay()
+    torch.cuda.synchronize()
+    t_sus_graph = event_loop(lambda i: g_sus.replay(), 3, torch.cuda.current_stream()) / n_sus
+    sus_gbs = R * L * SCAN_BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
 
     step_bytes = L * BYTES_PER_TOKEN + k * 576 * 2 + H * 576 * 2 + H * dv * 2
     res = {
@@ -215,11 +226,14 @@ def main():
         "roofline": {"kernel": "scan_dma_kernel<0, 2> (fp8 keys)", "bound": "hbm", "achieved": scan_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "note": "131072 tokens x 132 B per launch / average launch time "
+                     "note": "131072 tokens x 136 B per launch / average launch time "
                              "(HIP events around graph replays of the scan)"},
         "scan_sustained": {"tokens": R * L, "us": t_sus * 1e3,
                            "tokens_per_s": R * L / (t_sus * 1e-3), "GB_s": sus_gbs,
-                           "frac": sus_gbs / HBM_PEAK_GBS},
+                           "frac": sus_gbs / HBM_PEAK_GBS,
+                           "bytes_per_token": SCAN_BYTES_PER_TOKEN,
+                           "timing": "HIP events around 20 back-to-back launches on one stream",
+                           "us_graph_replay": t_sus_graph * 1e3},
         # the whole step against its algorithmic HBM time: the scan's keys and
         # scales, the gathered latent rows, the query and the output
         "step_roofline": {"algorithmic_bytes": step_bytes,
@@ -233,7 +247,7 @@ def main():
     if not args.no_extra:
         # the other workloads of the pages' configurations, measured on the
         # same device after the 128K sets are released
-        del g_all, g_rem, g_scan, g_topk, g_mla, di, scores, scores_all, sc_rows, idx_sel
+        del g_all, g_rem, g_scan, g_topk, g_mla, g_sus, di, scores, scores_all, sc_rows, idx_sel
         del q_idx, w, q_attn, reqs, ik, kv, ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -33,7 +33,8 @@ using namespace topk;
 constexpr int kBlock = 512;
 constexpr int kLdsCand = 16384;          // candidates refined in LDS
 constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
-constexpr int kRefPer = 8;               // candidates per thread in a refinement pass
+constexpr int kRefPer = 8;
+constexpr int kRefThreads = 1024;      // threads of the one-workgroup refinement               // candidates per thread in a refinement pass
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   int L;
@@ -191,6 +192,94 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
     }
     const int shift = stage == 0 ? kb_lo : stage == 1 ? 0 : stage == 2 ? 20 : stage == 3 ? 8 : 0;
     const uint32_t mask = (1u << nbits) - 1u;
+    if (in_lds) {
+      // Candidates in LDS: each thread holds up to CAP / NT of them in
+      // registers for the whole stage (wave w takes a contiguous run, its
+      // lanes interleaved), so the stage needs two count exchanges instead of
+      // a block scan per NT candidates.  The kept ones are written back in
+      // wave order, not position order: later stages select by value and by
+      // position bits, never by list order.
+      constexpr int kPer = CAP / NT;
+      constexpr int kNW = NT / 64;
+      static_assert(kNW <= 16, "per-wave counts fit the 32-word scratch");
+      const int lane = threadIdx.x & 63;
+      const int w = threadIdx.x >> 6;
+      uint32_t v[kPer];
+      int sl[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t i = (uint32_t)(w * 64 * kPer + j * 64 + lane);
+        sl[j] = -1;
+        v[j] = 0;
+        if (i < n) {
+          sl[j] = lslot[i];
+          v[j] = by_key ? lkey[i] : (uint32_t)out_value(a, r, sl[j]);
+        }
+      }
+      for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
+      wg_sync(true);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (sl[j] >= 0) atomicAdd(&hist[(v[j] >> shift) & mask], 1u);
+      wg_sync(true);
+      uint32_t better;
+      const int bin = find_threshold<NT>(hist, need, by_key, tmp, &better, true);
+      // this thread's winners and kept ones as bit masks over j; the wave's
+      // counts by a lane sum (ballots here would be kept live, per j, into
+      // the write pass below)
+      uint32_t winm = 0, eqm = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int d = (int)((v[j] >> shift) & mask);
+        if (sl[j] >= 0) {
+          winm |= (uint32_t)(by_key ? d > bin : d < bin) << j;
+          eqm |= (uint32_t)(d == bin) << j;
+        }
+      }
+      uint32_t cnt = (uint32_t)__popc(winm) | ((uint32_t)__popc(eqm) << 16);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+      if (lane == 0) {
+        tmp[w] = cnt & 0xFFFFu;
+        tmp[16 + w] = cnt >> 16;
+      }
+      wg_sync(true);
+      uint32_t ow = out_pos, oe = 0, tw = 0, te = 0;
+#pragma unroll
+      for (int x = 0; x < kNW; ++x) {
+        const uint32_t a0 = tmp[x], a1 = tmp[16 + x];
+        if (x < w) {
+          ow += a0;
+          oe += a1;
+        }
+        tw += a0;
+        te += a1;
+      }
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const bool win = (winm >> j) & 1u;
+        const bool eq = (eqm >> j) & 1u;
+        const uint64_t bw = __ballot(win);
+        const uint64_t be = __ballot(eq);
+        if (win) {
+          const uint32_t o = ow + (uint32_t)__popcll(bw & below);
+          if (o < (uint32_t)a.k) emit(a, r, o, out_value(a, r, sl[j]));
+        }
+        if (eq) {
+          const uint32_t o = oe + (uint32_t)__popcll(be & below);
+          lslot[o] = sl[j];
+          if (by_key) lkey[o] = v[j];
+        }
+        ow += (uint32_t)__popcll(bw);
+        oe += (uint32_t)__popcll(be);
+      }
+      wg_sync(true);
+      out_pos += tw;
+      need -= better;
+      n = te;
+      continue;
+    }
     auto value = [&](uint32_t i, int& slot) -> uint32_t {
       slot = in_lds ? lslot[i] : list[i];
       if (!by_key) return (uint32_t)out_value(a, r, slot);
@@ -388,7 +477,7 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t lkey[kLdsCand];
   __shared__ int32_t lslot[kLdsCand];
@@ -398,13 +487,13 @@ __global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
   if (L <= a.k) return;
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
   // the threshold bin's members are the candidates (everything above it has
-  // been written already); the first kBlock*kGather of them are loaded
+  // been written already); the first kRefThreads*kGather of them are loaded
   // along with the record that says how many there are
   const uint32_t* rec = ws.rec + (size_t)r * 4;
   const int2* cand = ws.cand + (size_t)r * a.max_len;
   int2 e0[kGather];
 #pragma unroll
-  for (int u = 0; u < kGather; ++u) e0[u] = cand[min((int)threadIdx.x + u * kBlock, a.max_len - 1)];
+  for (int u = 0; u < kGather; ++u) e0[u] = cand[min((int)threadIdx.x + u * kRefThreads, a.max_len - 1)];
   const uint32_t better = rec[1];
   const uint32_t n = rec[2];
   int32_t* list = ws.list + (size_t)r * a.max_len;
@@ -412,23 +501,23 @@ __global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
   if (in_lds) {
 #pragma unroll
     for (int u = 0; u < kGather; ++u) {
-      const uint32_t i = threadIdx.x + u * kBlock;
+      const uint32_t i = threadIdx.x + u * kRefThreads;
       if (i < n) {
         lslot[i] = e0[u].x;
         lkey[i] = (uint32_t)e0[u].y;
       }
     }
-    if (n > (uint32_t)(kBlock * kGather)) {
+    if (n > (uint32_t)(kRefThreads * kGather)) {
       // the rest in one batch of loads (a loop of smaller batches would
       // cost a round trip each)
-      constexpr int kRest = kLdsCand / kBlock - kGather;
+      constexpr int kRest = kLdsCand / kRefThreads - kGather;
       int2 e[kRest];
 #pragma unroll
       for (int u = 0; u < kRest; ++u)
-        e[u] = cand[min(threadIdx.x + (u + kGather) * kBlock, n - 1)];
+        e[u] = cand[min(threadIdx.x + (u + kGather) * kRefThreads, n - 1)];
 #pragma unroll
       for (int u = 0; u < kRest; ++u) {
-        const uint32_t i = threadIdx.x + (u + kGather) * kBlock;
+        const uint32_t i = threadIdx.x + (u + kGather) * kRefThreads;
         if (i < n) {
           lslot[i] = e[u].x;
           lkey[i] = (uint32_t)e[u].y;
@@ -436,10 +525,10 @@ __global__ __launch_bounds__(kBlock) void topk_refine_kernel(TopkArgs a) {
       }
     }
   } else {
-    for (uint32_t i = threadIdx.x; i < n; i += kBlock) list[i] = cand[i].x;
+    for (uint32_t i = threadIdx.x; i < n; i += kRefThreads) list[i] = cand[i].x;
   }
   __syncthreads();
-  refine_cands<kBlock, kLdsCand>(a, r, n, (uint32_t)a.k - better, better, list, in_lds, hist, tmp, lkey,
+  refine_cands<kRefThreads, kLdsCand>(a, r, n, (uint32_t)a.k - better, better, list, in_lds, hist, tmp, lkey,
                                  lslot, 20, 0u);
 }
 
@@ -647,7 +736,7 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
 #undef LSI_TOPK_PER
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kRefThreads), 0, s, a);
   return hipGetLastError();
 }
 
