@@ -32,8 +32,10 @@ constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
-constexpr int kMaxChunk = 8192;  // tokens per workgroup (contiguous mode)
-constexpr int kMaxChunkPages = kMaxChunk / 32;
+constexpr int kMaxChunk = 8192;  // tokens per workgroup (contiguous mode, one request per grid row)
+constexpr int kMaxBalChunk = 32768;   // tokens per workgroup (contiguous mode, balanced slices)
+constexpr int kMaxChunkPages = 512;   // page ids a workgroup stages (two per thread)
+static_assert(kMaxChunkPages <= 2 * 256, "two page ids per thread");
 constexpr int KIND_FP8 = 0;
 constexpr int KIND_INT4 = 1;
 
@@ -399,7 +401,7 @@ __device__ __forceinline__ void wait_ring_tile() {
 }
 
 template <int KIND, int RING>
-__global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int chunk, int page_shift) {
+__global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int chunk, int page_shift, int bal_n, int bal_sp) {
   using TL = DmaTile<KIND>;
   constexpr int kSlotBytes = TL::kSlot;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING][kWaves * kSlotBytes];
@@ -413,39 +415,39 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
          i < a.zero_words; i += nthreads)
       a.zero_ptr[i] = 0u;
   }
-  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int h = lane >> 5;
-  // One round trip for the slice's page ids (as far as the longest request
-  // reaches; the request's own length only trims them), the request length
-  // and, further down, the query rows and head weights.
-  const int begin = blockIdx.x * chunk;
-  const int npg_max = max(0, (min(begin + chunk, a.max_seq_len) - begin + a.page_size - 1) >> page_shift);
-  int page_in = -1;
-  if (tid < npg_max) page_in = a.page_table[(int64_t)b * a.max_pages + (begin >> page_shift) + tid];
-  const int Lraw = a.seq_lens[b];
   uint8_t* slot[RING];
 #pragma unroll
   for (int r = 0; r < RING; ++r) slot[r] = &ring[r][0] + wv * kSlotBytes;
-
-  // The query split is computed while the first key tiles are on their way.
-  // The query rows of the wave's 16 heads (4 KB) and the 64 head weights come
-  // in by DMA as well, into the last ring position: an ordinary load issued
-  // ahead of the tile DMAs would be waited for with every DMA behind it.
-  // (The page ids and the length above are such loads; their wait covers
-  // this DMA too, which is what the prologue wants: all of it is one round
-  // trip.)  Issue order after that wait: tiles 0 .. RING-2 (5 operations
-  // each); the last ring position gets its tile once the split is done.
-  // The wave's 16 query rows (4 KB) land in its part of the score staging
-  // buffer, where its query split is written over them once read; the 64
-  // head weights land at the start of its slot in the last ring position,
-  // which is filled with a tile only after the split.
   uint8_t* qraw = reinterpret_cast<uint8_t*>(&sbuf[wv][0]);
   static_assert(sizeof(sbuf[0]) == 16 * kDim * 2, "a wave's staging buffer holds its 16 query rows");
-  {
+
+  // The workgroup's slice: request b, positions [begin, begin + span).
+  int b = 0, begin = 0, span = 0, Lraw = 0;
+  int npg_max = 0, page_in0 = -1, page_in1 = -1;
+  // One round trip for the slice's page ids (as far as the longest request
+  // reaches; the request's own length only trims them), the request length
+  // (with_len) and the query rows and head weights.  The query split is
+  // computed while the first key tiles are on their way.  The query rows of
+  // the wave's 16 heads (4 KB) and the 64 head weights come in by DMA, into
+  // the wave's part of the score staging buffer (its query split is written
+  // over them once read) and the start of its slot in the last ring
+  // position (filled with a tile only after the split): an ordinary load
+  // issued ahead of the tile DMAs would be waited for with every DMA behind
+  // it.  (The page ids and the length are such loads; their wait covers
+  // these DMAs too, which is what the prologue wants.)  Issue order after
+  // that wait: tiles 0 .. RING-2; the last ring position gets its tile once
+  // the split is done.
+  auto prologue = [&](bool with_len) {
+    npg_max = max(0, (min(begin + span, a.max_seq_len) - begin + a.page_size - 1) >> page_shift);
+    const int32_t* pt = a.page_table + (int64_t)b * a.max_pages + (begin >> page_shift);
+    page_in0 = tid < npg_max ? pt[tid] : -1;
+    page_in1 = tid + kThreads < npg_max ? pt[tid + kThreads] : -1;
+    if (with_len) Lraw = a.seq_lens[b];
     const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
                                                         ((int64_t)b * kHeads + 16 * wv) * kDim) + 16 * lane;
     asm volatile("" ::: "memory");
@@ -454,17 +456,152 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     lds_dma16<2048>(qraw, qg);
     lds_dma16<3072>(qraw, qg);
     lds_dma4(slot[RING - 1], a.w + (int64_t)b * kHeads + lane);
+  };
+  if (bal_n > 0) {
+    // The slice the grid would have if every request had the longest
+    // length (bal_n slices of bal_sp positions per request) is loaded
+    // while the real one is worked out, and loaded again only if it differs.
+    const int gb = (int)blockIdx.x / bal_n;
+    const int gbegin = ((int)blockIdx.x % bal_n) * bal_sp;
+    b = gb;
+    begin = gbegin;
+    span = bal_sp;
+    if (gb < a.num_req) prologue(false);
+    // Balanced slices over a one-dimensional grid of G workgroups (at most
+    // kThreads requests): request r of length L_r gets slices of
+    // ceil(L_r / n_r) positions rounded up to a multiple of `chunk`, with
+    // n_r = ceil(L_r * G' / T) for T the batch's tokens and G' the largest
+    // of eight values from G down to G - R whose slices fit in the grid (at
+    // G - R they always do).  Workgroups take the slices in request order;
+    // the rest retire here.
+    constexpr int kCand = 8;
+    __shared__ int64_t bal_sum[kWaves];
+    __shared__ int bal_cnt[kWaves][kCand];
+    __shared__ int bal_scan[kWaves];
+    __shared__ int bal_own[4];
+    const int R = a.num_req;
+    const int64_t G = gridDim.x;
+    const int Lr = tid < R ? min(max(a.seq_lens[tid], 0), a.max_seq_len) : 0;
+    int64_t t = Lr;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int lo = __shfl_xor((int)(uint32_t)t, o);
+      const int hi = __shfl_xor((int)(t >> 32), o);
+      t += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    }
+    if (lane == 0) bal_sum[wv] = t;
+    if (tid == 0) bal_own[0] = -1;
+    __syncthreads();
+    int64_t T = 0;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) T += bal_sum[x];
+    const bool uniform = T == (int64_t)R * a.max_seq_len;   // every request at the longest length
+    // x / y rounded up for 0 <= x < 2^53, y > 0: a double quotient, then
+    // corrected (a 64-bit integer division is a long software sequence)
+    auto cdiv = [](int64_t x, int64_t y) -> int64_t {
+      int64_t q = (int64_t)__builtin_ceil((double)x / (double)y);
+      if (q * y < x) ++q;
+      else if (q > 0 && (q - 1) * y >= x) --q;
+      return q;
+    };
+    auto slices = [&](int i, int& sp) -> int {   // slices of this thread's request at G'_i
+      sp = 0;
+      if (Lr == 0) return 0;
+      const int64_t Gi = G - ((int64_t)R * i + kCand - 2) / (kCand - 1);
+      const int nr = (int)max((int64_t)1, cdiv((int64_t)Lr * Gi, T));
+      sp = (int)(cdiv(cdiv(Lr, nr), chunk) * chunk);
+      return (int)cdiv(Lr, sp);
+    };
+    if (!uniform) {
+      // G' = G first; the seven smaller values only when that does not fit
+      int pick = 0;
+      {
+        int sp;
+        int c = slices(0, sp);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+        if (lane == 0) bal_cnt[wv][0] = c;
+      }
+      __syncthreads();
+      {
+        int c = 0;
+#pragma unroll
+        for (int x = 0; x < kWaves; ++x) c += bal_cnt[x][0];
+        if (c > G) pick = -1;
+      }
+      if (pick < 0) {
+        for (int i = 1; i < kCand; ++i) {
+          int sp;
+          int c = slices(i, sp);
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+          if (lane == 0) bal_cnt[wv][i] = c;
+        }
+        __syncthreads();
+        pick = kCand - 1;
+        for (int i = kCand - 1; i >= 1; --i) {
+          int c = 0;
+#pragma unroll
+          for (int x = 0; x < kWaves; ++x) c += bal_cnt[x][i];
+          if (c <= G) pick = i;
+        }
+      }
+      int sp;
+      const int used = slices(pick, sp);
+      int inc = used;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      if (lane == 63) bal_scan[wv] = inc;
+      __syncthreads();
+      int pre = inc - used;
+#pragma unroll
+      for (int x = 0; x < kWaves; ++x)
+        if (x < wv) pre += bal_scan[x];
+      const int me = (int)blockIdx.x;
+      if (used > 0 && me >= pre && me < pre + used) {
+        bal_own[0] = tid;
+        bal_own[1] = (me - pre) * sp;
+        bal_own[2] = sp;
+        bal_own[3] = Lr;
+      }
+      __syncthreads();
+      b = bal_own[0];
+      begin = bal_own[1];
+      span = bal_own[2];
+      Lraw = bal_own[3];
+    } else {
+      // every request has the longest length: the slicing is the one
+      // loaded above
+      b = gb < R ? gb : -1;
+      Lraw = a.max_seq_len;
+    }
+    if (b < 0) {             // no slice for this workgroup
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+    if (b != gb || begin != gbegin || span != bal_sp) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      prologue(false);
+    }
+  } else {
+    b = blockIdx.y;
+    begin = blockIdx.x * chunk;
+    span = chunk;
+    prologue(true);
   }
   const int L = min(max(Lraw, 0), a.max_seq_len);
-  const int nprod = max(1, (L + chunk - 1) / chunk);
-  if ((int)blockIdx.x >= nprod) {
+  if (begin > 0 && begin >= L) {
     // nothing of this request here; no DMA may still be writing the LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
-  if (tid < npg_max) pages[tid] = page_in;
+  if (tid < npg_max) pages[tid] = page_in0;
+  if (tid + kThreads < npg_max) pages[tid + kThreads] = page_in1;
   __syncthreads();
-  const int end = min(begin + chunk, L);
+  const int end = min(begin + span, L);
   const int ntile = max(0, (end - begin + kTile - 1) / kTile);
 
   // A wave takes a contiguous run of the slice's tiles, so its scores form
@@ -784,14 +921,45 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   const bool gather = a.positions != nullptr;
   const int max_items = gather ? a.n_pos : a.max_seq_len;
   constexpr int kRingTiles = 2;
-  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, gather ? 2 : 3);
-  // the DMA scan stages a slice's page ids with one load per thread
-  if (!gather && (chunk + a.page_size - 1) / a.page_size > std::min(kMaxChunkPages, kThreads))
-    return hipErrorInvalidValue;
-  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   const int ps = ilog2(a.page_size);
+  if (!gather) {
+    // Batches: one wave of resident workgroups over balanced slices, sized
+    // on the device from the request lengths (a grid of one row per request
+    // would leave the slices of ragged requests to a partial second wave).
+    const int64_t G = (int64_t)num_cus() * 3;
+    const int64_t unit = std::max<int64_t>(kTile * kWaves, a.page_size);
+    const int64_t work = (int64_t)a.num_req * a.max_seq_len;
+    if (a.num_req >= 2 && a.num_req <= kThreads && 4 * (int64_t)a.num_req <= G &&
+        a.max_seq_len <= (1 << 30) && work >= G * unit) {
+      const int64_t span = ceil_div(ceil_div(work, G - a.num_req), unit) * unit;
+      if (span <= kMaxBalChunk && ceil_div(span, (int64_t)a.page_size) <= kMaxChunkPages) {
+        // the device's slicing when every request has the longest length:
+        // the workgroups load that slice while they work out their own
+        const int64_t R = a.num_req, Lm = a.max_seq_len, T = R * Lm;
+        int64_t n_u = 0, sp_u = 0;
+        for (int i = 0; i < 8; ++i) {
+          const int64_t Gi = G - (R * i + 6) / 7;
+          const int64_t nr = std::max<int64_t>(1, (Lm * Gi + T - 1) / T);
+          const int64_t sp = ceil_div(ceil_div(Lm, nr), unit) * unit;
+          const int64_t used = ceil_div(Lm, sp);
+          if (R * used <= G || i == 7) {
+            n_u = used;
+            sp_u = sp;
+            break;
+          }
+        }
+        hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), dim3((unsigned)G), dim3(kThreads), 0, s, a,
+                           (int)unit, ps, (int)n_u, (int)sp_u);
+        return hipGetLastError();
+      }
+    }
+  }
+  const int chunk = pick_chunk(a.num_req, max_items, a.page_size, gather, gather ? 2 : 3);
+  // the DMA scan stages a slice's page ids, two per thread
+  if (!gather && (chunk + a.page_size - 1) / a.page_size > kMaxChunkPages) return hipErrorInvalidValue;
+  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
   if (!gather)
-    hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, a, chunk, ps);
+    hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, a, chunk, ps, 0, 0);
   else
     hipLaunchKernelGGL(scan_gather_kernel<KIND>, grid, dim3(kThreads), 0, s, a, chunk, ps);
   return hipGetLastError();

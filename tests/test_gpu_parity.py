@@ -65,6 +65,29 @@ def test_scan_fp8_ragged_batch():
         print(f"req {b} L={L} {st}")
 
 
+@pytest.mark.parametrize("lens", [
+    [60000, 0, 1, 40000, 777, 65, 12345, 30000],      # ragged, empty and one-token requests
+    [50000, 50000, 50000],                            # uniform
+    [0, 0, 131072, 0],                                # one request holds every token
+])
+def test_scan_fp8_balanced_slices(lens):
+    """Batches large enough for the one-wave grid of balanced slices sized on
+    the device: every score of every request, nothing past a request's end."""
+    di = small_dsa(lens, n_planted=16, attn=False)
+    ov = OracleView(di)
+    ik, req, _, _ = objs(di)
+    s = torch.full((len(lens), max(lens) + 64), float("nan"), device=DEV)
+    lsi.index_scores(ik, req, di.q_idx, di.w, scores=s)
+    torch.cuda.synchronize()
+    sc = s.cpu().numpy()
+    for b in range(len(lens)):
+        L = ov.L(b)
+        assert np.isnan(sc[b, L:]).all(), f"req {b}: written past its length"
+        if L:
+            ref, mag = ov.scores(b)
+            check_scores(sc[b, :L], ref, mag, f"req {b}")
+
+
 def test_scan_f32_tiny_case():
     di = synth.make_decode_inputs(synth.TINY_F32, device=DEV, with_attn=False)
     ov = OracleView(di)
