@@ -57,6 +57,14 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
     const int32_t _st = (expr);                                  \
     if (_st != LSI_OK) return _st;                               \
   } while (0)
+// A launcher's status (it returns hipGetLastError(), which also clears the
+// error): the first failure ends the call before anything else is enqueued.
+#define LSI_LAUNCH(expr, what)                                                         \
+  do {                                                                                 \
+    const hipError_t _le = (expr);                                                     \
+    if (_le != hipSuccess)                                                             \
+      return fail(LSI_ERR_HIP, std::string(what) + ": " + hipGetErrorString(_le));     \
+  } while (0)
 
 int32_t check_batch(const lsi_batch* b, bool need_pages) {
   LSI_REQUIRE(b != nullptr, "batch is NULL");
@@ -278,7 +286,7 @@ int32_t lsi_index_scores(const lsi_paged_cache* ikeys, const lsi_batch* batch, c
                          hipStream_t stream) {
   LSI_TRY(validate_index(ikeys, batch, q, n_heads, dim, w, scores, ld));
   const ScanArgs a = scan_args(ikeys, batch, q, n_heads, dim, w, scores, ld);
-  run_scan(ikeys->dtype, a, stream);
+  LSI_LAUNCH(run_scan(ikeys->dtype, a, stream), "lsi_index_scores");
   return check_launch("lsi_index_scores");
 }
 
@@ -302,7 +310,7 @@ int32_t lsi_topk(const float* scores, int64_t ld, const lsi_batch* batch, int32_
   t.idx = idx;
   t.count = count;
   t.ws = workspace;
-  launch_topk(t, 0, stream);
+  LSI_LAUNCH(launch_topk(t, 0, stream), "lsi_topk");
   return check_launch("lsi_topk");
 }
 
@@ -320,7 +328,7 @@ int32_t lsi_sparse_mla_decode(const lsi_paged_cache* kv, const lsi_paged_cache* 
   LSI_TRY(validate_attn(kv, v, batch, q, n_heads, dk, dv, idx, k, sm_scale, out, lse));
   LSI_TRY(check_ws(workspace, ws_bytes, attn_ws(kv->dtype, batch->num_req, n_heads, dv, k)));
   const AttnArgs a = attn_args(kv, v, batch, q, n_heads, dk, dv, idx, k, sm_scale, out, lse, workspace);
-  run_attn(kv->dtype, a, stream);
+  LSI_LAUNCH(run_attn(kv->dtype, a, stream), "lsi_sparse_mla_decode");
   return check_launch("lsi_sparse_mla_decode");
 }
 
@@ -363,7 +371,7 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
   sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
   sa.zero_words = topk_zero_words(batch->num_req);
-  run_scan(ikeys->dtype, sa, stream);
+  LSI_LAUNCH(run_scan(ikeys->dtype, sa, stream), "lsi_decode_step (scan)");
 
   TopkArgs t;
   t.scores = scores;
@@ -380,11 +388,11 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.max_pages = batch->max_pages;
   t.page_size = kv->page_size;
   t.num_pages = kv->num_pages;
-  launch_topk(t, 1, stream);
+  LSI_LAUNCH(launch_topk(t, 1, stream), "lsi_decode_step (top-k)");
 
   AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
   a.phys = phys;
-  run_attn(kv->dtype, a, stream);
+  LSI_LAUNCH(run_attn(kv->dtype, a, stream), "lsi_decode_step (attention)");
   return check_launch("lsi_decode_step");
 }
 
@@ -436,7 +444,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
   a4.zero_ptr = static_cast<uint32_t*>(t1);
   a4.zero_words = topk_zero_words(B);
-  launch_scan_int4(a4, stream);
+  LSI_LAUNCH(launch_scan_int4(a4, stream), "lsi_two_stage_topk (compact scan)");
   TopkArgs ta;
   ta.scores = s4;
   ta.ld = ld;
@@ -447,7 +455,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ta.idx = cl;
   ta.count = cc;
   ta.ws = t1;
-  launch_topk(ta, 1, stream);
+  LSI_LAUNCH(launch_topk(ta, 1, stream), "lsi_two_stage_topk (first top-k)");
 
   // stage 2: exact fp8 scores of the candidates only, keep k
   ScanArgs a8 = scan_args(ikeys8, batch, q, n_heads, dim, w, s8, n_cand);
@@ -455,7 +463,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   a8.n_pos = n_cand;
   a8.zero_ptr = static_cast<uint32_t*>(t2);
   a8.zero_words = topk_zero_words(B);
-  launch_scan_fp8(a8, stream);
+  LSI_LAUNCH(launch_scan_fp8(a8, stream), "lsi_two_stage_topk (exact scan)");
   TopkArgs tb;
   tb.scores = s8;
   tb.ld = n_cand;
@@ -468,7 +476,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   tb.idx = idx;
   tb.count = count;
   tb.ws = t2;
-  launch_topk(tb, 1, stream);
+  LSI_LAUNCH(launch_topk(tb, 1, stream), "lsi_two_stage_topk (second top-k)");
   if (cand) {
     const hipError_t e = hipMemcpyAsync(cand, cl, (size_t)B * n_cand * 4, hipMemcpyDeviceToDevice, stream);
     if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("lsi_two_stage_topk: ") + hipGetErrorString(e));
@@ -571,14 +579,14 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
     pa.kscale = bufs[j];
     pa.tok0 = tok0;
     pa.n_tok = n;
-    launch_prefill_scan(pa, s_compute);
+    LSI_HIP(launch_prefill_scan(pa, s_compute));
     LSI_HIP(hipEventRecord(ev.done[j], s_compute));
   }
   pa.keys = chunk_keys;
   pa.kscale = chunk_scale;
   pa.tok0 = hist_len;
   pa.n_tok = T;
-  launch_prefill_scan(pa, s_compute);
+  LSI_HIP(launch_prefill_scan(pa, s_compute));
 
   TopkArgs t;
   t.scores = sc;
@@ -590,7 +598,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   t.idx = idx;
   t.count = count;
   t.ws = tws;
-  launch_topk(t, 0, s_compute);
+  LSI_HIP(launch_topk(t, 0, s_compute));
 #undef LSI_HIP
   return check_launch("lsi_prefill_index_topk");
 }

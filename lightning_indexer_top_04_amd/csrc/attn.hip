@@ -354,6 +354,7 @@ constexpr int kWThreads = 512;
 constexpr int kWMaxRows = 2048;               // selection rows one workgroup handles
 constexpr int kWDmaPerBlock = 9;              // DMA instructions per wave per block
                                               // (the vmcnt(9) waits below)
+static_assert(kWDmaPerBlock == kMBlk / (kWThreads / 64) + 1, "a DMA per row of the wave, one for their rope dims");
 
 __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a, int rows_per_split,
                                                                     int nsplit, int units, float* part_o,
