@@ -77,20 +77,26 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-// Six 16-byte LDS reads, complete when the statement ends.  Written out so
-// that the compiler, which cannot tell these rows from a block DMA still in
-// flight into the other buffer, does not wait for that DMA first.
-__device__ __forceinline__ void lds_read_b128x6(u32x4 (&o)[6], const uint32_t (&ad)[6]) {
+// Nine 16-byte LDS reads (half a row tile of S), complete when the statement
+// ends.  Written out so that the compiler, which cannot tell these rows from
+// a block DMA still in flight into the other buffer, does not wait for that
+// DMA first.
+__device__ __forceinline__ void lds_read_b128x9(u32x4* o, const uint32_t* ad) {
   asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %7\n\t"
-      "ds_read_b128 %2, %8\n\t"
-      "ds_read_b128 %3, %9\n\t"
-      "ds_read_b128 %4, %10\n\t"
-      "ds_read_b128 %5, %11\n\t"
+      "ds_read_b128 %0, %9\n\t"
+      "ds_read_b128 %1, %10\n\t"
+      "ds_read_b128 %2, %11\n\t"
+      "ds_read_b128 %3, %12\n\t"
+      "ds_read_b128 %4, %13\n\t"
+      "ds_read_b128 %5, %14\n\t"
+      "ds_read_b128 %6, %15\n\t"
+      "ds_read_b128 %7, %16\n\t"
+      "ds_read_b128 %8, %17\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5])
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7]), "=&v"(o[8])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(ad[8])
       : "memory");
 }
 // One 8-byte LDS write (same reason); the next barrier waits for it.
@@ -362,10 +368,9 @@ __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a,
   __shared__ __attribute__((aligned(1024))) uint8_t kvs0[kKvBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t kvs1[kKvBytes];
   __shared__ __attribute__((aligned(16))) __bf16 Pl[kWH * kPStride];
-  __shared__ float red_m[4][kWH];
-  __shared__ float red_l[4][kWH];
-  __shared__ float alpha_s[kWH];
-  __shared__ int rows_all[kWMaxRows];
+  __shared__ __attribute__((aligned(16))) float red_m[kWH][4];   // [head][row tile]
+  __shared__ __attribute__((aligned(16))) float red_l[kWH][4];
+  __shared__ __attribute__((aligned(16))) int rows_all[kWMaxRows];
 
   const int n_hg = a.n_heads / kWH;
   const int bid = blockIdx.x;
@@ -439,8 +444,25 @@ __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a,
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[h2][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // per head hh, the same in the four row-tile waves
-  float l_run = 0.f;
+  // Running maxima (log2 units).  Every wave holds the same values: for head
+  // hh (its S tile), for head lane % 32 (the vote below) and for the heads
+  // 16 h2 + 4 g + r of its O rows.  A head's running maximum moves only when
+  // a block's maximum passes it by more than 8 (the first finite score
+  // always does); until then the block's P is taken against the old value,
+  // at most 2^8, so most blocks need no exchange of maxima before P.
+  float m_s = -INFINITY;
+  float m_v = -INFINITY;
+  float m_o[2][4];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m_o[h2][r] = -INFINITY;
+  float l_w = 0.f;   // this wave's rows' share of the softmax sum of head hh
+  auto bump = [](float m, float bm) { return bm > m + 8.f ? fmaxf(m, bm) : m; };
+  auto hmax = [&](int head) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&red_m[head][0]);
+    return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  };
 
   const int nblk = (nr + kMBlk - 1) / kMBlk;
   auto step = [&](int blk, const uint8_t* kv, uint8_t* next) {
@@ -455,70 +477,75 @@ __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a,
       asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
-    // ---- S^T for rows 16rt + (0..15) and heads 16ht + (0..15)
+    // ---- S^T for rows 16rt + (0..15) and heads 16ht + (0..15), nine reads
+    // at a time
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     {
       const int row = 16 * rt + n;
       const uint32_t vrow = lds_addr(kv) + row * kVRow;
       const uint32_t rrow = lds_addr(kv) + kRopeOff + (row >> 3) * 1024 + (row & 7) * 128;
+      uint32_t ad[kD / 32];
 #pragma unroll
-      for (int t0 = 0; t0 < kD / 32; t0 += 6) {
-        uint32_t ad[6];
+      for (int t = 0; t < kD / 32; ++t)
+        ad[t] = t < 16 ? vrow + 16 * ((4 * t + g) ^ (row & 15)) : rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7));
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-          const int t = t0 + i;
-          ad[i] = t < 16 ? vrow + 16 * ((4 * t + g) ^ (row & 15)) : rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7));
-        }
-        u32x4 av[6];
-        lds_read_b128x6(av, ad);
+      for (int t0 = 0; t0 < kD / 32; t0 += 9) {
+        u32x4 av[9];
+        lds_read_b128x9(av, ad + t0);
 #pragma unroll
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 9; ++i)
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]), qr[t0 + i], sacc, 0, 0, 0);
       }
     }
-    // lane (n, g) holds S^T[row 16rt + 4g + r][head hh]
+    // lane (n, g) holds S^T[row 16rt + 4g + r][head hh]; the four rows'
+    // physical ids in one read
+    const int4 rv = *reinterpret_cast<const int4*>(&rows_all[base + 16 * rt + 4 * g]);
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = 16 * rt + 4 * g + r;
-      const bool ok = rl < nb && rows_all[base + rl] >= 0;
-      x[r] = ok ? sacc[r] * c : -INFINITY;
+      const int id = r == 0 ? rv.x : r == 1 ? rv.y : r == 2 ? rv.z : rv.w;
+      x[r] = rl < nb && id >= 0 ? sacc[r] * c : -INFINITY;
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max4rows(mx);
-    if (g == 0) red_m[rt][hh] = mx;
-    lds_barrier();
-    const float bmax = fmaxf(fmaxf(red_m[0][hh], red_m[1][hh]), fmaxf(red_m[2][hh], red_m[3][hh]));
-    // lazy rescaling, as in the 16-head kernel
-    const bool first = m_run == -INFINITY;
-    const float m_new = (first || bmax > m_run + 8.f) ? fmaxf(m_run, bmax) : m_run;
-    const float alpha = (first || m_new == m_run) ? (first ? 0.f : 1.f) : exp2f(m_run - m_new);
-    float p[4];
+    auto write_p = [&](float m, float (&p)[4]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = m_new == -INFINITY ? 0.f : exp2f(x[r] - m_new);
-    float ps = (p[0] + p[1]) + (p[2] + p[3]);
-    ps = sum4rows(ps);
-    if (g == 0) red_l[rt][hh] = ps;
-    {
+      for (int r = 0; r < 4; ++r) p[r] = m == -INFINITY ? 0.f : exp2f(x[r] - m);
       const u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       lds_write_b64(lds_addr(&Pl[hh * kPStride + 16 * rt + 4 * g]), pw);
-    }
-    if (rt == 0 && g == 0) alpha_s[hh] = alpha;
+    };
+    float p[4];
+    write_p(m_s, p);
+    if (g == 0) red_m[hh][rt] = mx;
     lds_barrier();
-    l_run = l_run * (first ? 0.f : alpha) + ((red_l[0][hh] + red_l[1][hh]) + (red_l[2][hh] + red_l[3][hh]));
-    m_run = m_new;
-
-    // ---- O[32 heads][dims 64w ..] += P V; lane (dim n, g) holds heads 16h2 + 4g + r
+    // Vote (the same in every wave): does any head's block maximum pass its
+    // running maximum by more than 8?
+    if (__ballot(hmax(lane & 31) > m_v + 8.f) != 0) {
+      const float ms_new = bump(m_s, hmax(hh));
+      const float a_s = ms_new == m_s ? 1.f : (m_s == -INFINITY ? 0.f : exp2f(m_s - ms_new));
+      write_p(ms_new, p);
+      l_w = l_w * a_s + sum4rows((p[0] + p[1]) + (p[2] + p[3]));
+      m_s = ms_new;
+      m_v = bump(m_v, hmax(lane & 31));
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f32x4 al;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x4 al;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = alpha_s[16 * h2 + 4 * g + r];
-      if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
+        for (int r = 0; r < 4; ++r) {
+          const float mn = bump(m_o[h2][r], hmax(16 * h2 + 4 * g + r));
+          al[r] = mn == m_o[h2][r] ? 1.f : (m_o[h2][r] == -INFINITY ? 0.f : exp2f(m_o[h2][r] - mn));
+          m_o[h2][r] = mn;
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) o[h2][t] *= al;
       }
+      lds_barrier();   // the rewritten P
+    } else {
+      l_w += sum4rows((p[0] + p[1]) + (p[2] + p[3]));
     }
+
+    // ---- O[32 heads][dims 64w ..] += P V; lane (dim n, g) holds heads 16h2 + 4g + r
     const int s16 = lane & 15;
     const int ja = s16 >> 2;
     const int aa = s16 & 3;
@@ -558,19 +585,17 @@ __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a,
     if (blk + 1 < nblk) step(blk + 1, kvs1, kvs0);
   }
 
-  // ---- results
-  if (rt == 0 && g == 0) {
-    red_m[0][hh] = m_run;
-    red_l[0][hh] = l_run;
-  }
+  // ---- results: the four row tiles' shares of each head's sum
+  if (g == 0) red_l[hh][rt] = l_w;
   __syncthreads();
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hl = 16 * h2 + 4 * g + r;
-      const float lr = red_l[0][hl];
-      const float mr = red_m[0][hl];
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&red_l[hl][0]);
+      const float lr = (lv[0] + lv[1]) + (lv[2] + lv[3]);
+      const float mr = m_o[h2][r];
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       const float lse2 = lr > 0.f ? mr + log2f(lr) : -INFINITY;
       const int64_t bh = (int64_t)b * a.n_heads + hg * kWH + hl;
