@@ -33,8 +33,8 @@ using namespace topk;
 constexpr int kBlock = 512;
 constexpr int kLdsCand = 16384;          // candidates refined in LDS
 constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
-constexpr int kRefPer = 8;
-constexpr int kRefThreads = 1024;      // threads of the one-workgroup refinement               // candidates per thread in a refinement pass
+constexpr int kRefPer = 8;               // candidates per thread in a refinement pass
+constexpr int kRefThreads = 1024;        // threads of the one-workgroup refinement
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   int L;
@@ -115,7 +115,44 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint32_t* p, int64_t n) {
 static_assert(kBins == 8 * kBlock, "tiling");
 
 // PER positions per thread: chunks of PER * kBlock positions
-template <int PER>
+// Element j of this thread in a chunk of PER * kBlock scores: thread t
+// takes runs of VW consecutive scores, VW * kBlock apart, so that a load is
+// VW scores wide (VW = 1 where rows are not 16-byte aligned).
+template <int VW>
+__device__ __forceinline__ int chunk_pos(int begin, int j) {
+  return begin + VW * ((int)threadIdx.x + (j / VW) * kBlock) + j % VW;
+}
+// The chunk's PER keys of this thread, every load issued before the first
+// use; positions past `end` read the last score (and are not counted).
+template <int PER, int VW>
+__device__ __forceinline__ void load_keys(const float* row, int begin, int end, uint32_t (&key)[PER]) {
+  static_assert(PER % VW == 0, "runs tile the chunk");
+#pragma unroll
+  for (int q = 0; q < PER / VW; ++q) {
+    const int p = chunk_pos<VW>(begin, q * VW);
+    if constexpr (VW == 4) {
+      if (p + 4 <= end) {
+        const float4 v = *reinterpret_cast<const float4*>(row + p);
+        key[4 * q] = float_key(v.x);
+        key[4 * q + 1] = float_key(v.y);
+        key[4 * q + 2] = float_key(v.z);
+        key[4 * q + 3] = float_key(v.w);
+        continue;
+      }
+    } else if constexpr (VW == 2) {
+      if (p + 2 <= end) {
+        const float2 v = *reinterpret_cast<const float2*>(row + p);
+        key[2 * q] = float_key(v.x);
+        key[2 * q + 1] = float_key(v.y);
+        continue;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VW; ++e) key[q * VW + e] = float_key(row[min(p + e, end - 1)]);
+  }
+}
+
+template <int PER, int VW>
 __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
   __shared__ uint32_t hist[kBins];
@@ -128,15 +165,13 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   if (begin >= L) return;
   const int end = min(begin + kChunk, L);
   const float* row = a.scores + (int64_t)r * a.ld;
-  // the chunk's loads go out first (indexes past the end are clamped and not
-  // counted), so they cost one round trip
+  // the chunk's loads go out first, so they cost one round trip
   uint32_t d[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) d[j] = float_key(row[min(begin + j * kBlock + (int)threadIdx.x, end - 1)]) >> 20;
+  load_keys<PER, VW>(row, begin, end, d);
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < PER; ++j) atomicAdd(&hist[d[j]], begin + j * kBlock + (int)threadIdx.x < end ? 1u : 0u);
+  for (int j = 0; j < PER; ++j) atomicAdd(&hist[d[j] >> 20], chunk_pos<VW>(begin, j) < end ? 1u : 0u);
   __syncthreads();
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
   // the chunk's suffix counts: thread t owns bins 4095-8t down to 4088-8t
@@ -354,7 +389,7 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
 
 // MAPPED: outputs go through the slot map (their pages are looked up per
 // winner); otherwise the chunk's page-table entries are staged in LDS
-template <int PER, bool MAPPED>
+template <int PER, bool MAPPED, int VW>
 __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
   __shared__ uint32_t hist[kBins];
@@ -378,14 +413,12 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   }
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
   const float* row = a.scores + (int64_t)r * a.ld;
-  // one round trip for the chunk's keys (thread t owns elements
-  // begin + t + j*kBlock), the row histogram and the chunk's page-table
+  // one round trip for the chunk's keys (the same elements per thread as in
+  // the histogram pass), the row histogram and the chunk's page-table
   // entries (so winners leave with their physical rows; with a slot map the
   // pages are only known per winner)
-  const int i0 = begin + threadIdx.x;
   uint32_t key[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) key[j] = float_key(row[min(i0 + j * kBlock, end - 1)]);
+  load_keys<PER, VW>(row, begin, end, key);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = gh[i];
   const bool lds_pages = !MAPPED && a.phys;
@@ -433,7 +466,7 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   uint32_t win = 0, eq = 0;      // bit masks over the PER elements
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    if (i0 + j * kBlock < end) {
+    if (chunk_pos<VW>(begin, j) < end) {
       const uint32_t dj = key[j] >> 20;
       win |= (uint32_t)(dj > digit) << j;
       eq |= (uint32_t)(dj == digit) << j;
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   int wv[PER], wp[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = i0 + j * kBlock;
+    const int i = chunk_pos<VW>(begin, j);
     wv[j] = ((win >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
   }
   if (lds_pages) {
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
       }
       ++ow;
     }
-    if ((eq >> j) & 1u) cand[oc++] = make_int2(i0 + j * kBlock, (int)key[j]);
+    if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
   }
 }
 
@@ -722,17 +755,23 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   while (per * kBlock < kMaxChunk && per * kBlock < want) per *= 2;
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)), (unsigned)a.num_req);
   const bool mapped = a.map != nullptr;
-  switch (per) {
-#define LSI_TOPK_PER(P)                                                                      \
-  case P:                                                                                    \
-    hipLaunchKernelGGL(topk_hist_kernel<P>, grid, dim3(kBlock), 0, s, a);                    \
-    if (mapped) hipLaunchKernelGGL((topk_select_kernel<P, true>), grid, dim3(kBlock), 0, s, a); \
-    else hipLaunchKernelGGL((topk_select_kernel<P, false>), grid, dim3(kBlock), 0, s, a);    \
+  // rows that start on 16-byte boundaries are read 4 (or 2) scores per load
+  const bool vec = reinterpret_cast<uintptr_t>(a.scores) % 16 == 0 && a.ld % 4 == 0;
+  switch (per * (vec ? 1 : -1)) {
+#define LSI_TOPK_PER(P, VW)                                                                           \
+  case (VW == 1 ? -P : P):                                                                            \
+    hipLaunchKernelGGL((topk_hist_kernel<P, VW>), grid, dim3(kBlock), 0, s, a);                       \
+    if (mapped) hipLaunchKernelGGL((topk_select_kernel<P, true, VW>), grid, dim3(kBlock), 0, s, a);   \
+    else hipLaunchKernelGGL((topk_select_kernel<P, false, VW>), grid, dim3(kBlock), 0, s, a);         \
     break;
-    LSI_TOPK_PER(2)
-    LSI_TOPK_PER(4)
-    LSI_TOPK_PER(8)
-    LSI_TOPK_PER(16)
+    LSI_TOPK_PER(2, 2)
+    LSI_TOPK_PER(4, 4)
+    LSI_TOPK_PER(8, 4)
+    LSI_TOPK_PER(16, 4)
+    LSI_TOPK_PER(2, 1)
+    LSI_TOPK_PER(4, 1)
+    LSI_TOPK_PER(8, 1)
+    LSI_TOPK_PER(16, 1)
 #undef LSI_TOPK_PER
     default: return hipErrorInvalidValue;
   }

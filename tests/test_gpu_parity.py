@@ -196,6 +196,25 @@ def test_topk_random_rows_against_full_sort(seed, reps):
     assert all(s["diff"] == 0 for s in st), st
 
 
+@pytest.mark.parametrize("ld,offset", [(50001, 0), (50004, 1), (50004, 0)])
+def test_topk_row_alignment_and_ragged_tails(ld, offset):
+    """Rows that do not start on 16-byte boundaries (odd leading dimension or
+    a pointer one score in) take one score per load; aligned rows take four.
+    Lengths end mid-run so that the last loads are partial."""
+    rng = np.random.default_rng(17)
+    lens = [50001 - offset, 45003, 33333, 40000]
+    base = torch.from_numpy(rng.standard_normal((len(lens), ld)).astype(np.float32)).to(DEV)
+    sc = base[:, offset:offset + max(lens)]
+    req = lsi.Requests(torch.tensor(lens, dtype=torch.int32, device=DEV), None, max(lens))
+    idx, cnt = lsi.topk(sc, req, 2048)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    host = sc.cpu().numpy().astype(np.float64)
+    for b, L in enumerate(lens):
+        st = check_topk(idx[b], cnt[b], host[b, :L], 2048, f"row {b}")
+        assert st["diff"] == 0, st
+
+
 @pytest.mark.parametrize("L", [20000, 70000])
 def test_topk_exact_ties_keep_lowest_positions(L):
     rng = np.random.default_rng(3)
