@@ -35,6 +35,8 @@ constexpr int kLdsCand = 16384;          // candidates refined in LDS
 constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
 constexpr int kRefPer = 8;               // candidates per thread in a refinement pass
 constexpr int kRefThreads = 1024;        // threads of the one-workgroup refinement
+constexpr int kSelPages = 520;           // page ids a select workgroup stages (8192 positions
+                                         // over pages of 16 or more tokens)
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   int L;
@@ -152,10 +154,24 @@ __device__ __forceinline__ void load_keys(const float* row, int begin, int end, 
   }
 }
 
+// Histogram counters: four replicas of each bin (lane % 4 picks one), so
+// that the lanes of a wave that hit one bin, as most do when the scores
+// crowd into a few bins, serialise four times less on the LDS atomic.  Bins
+// b and b + 2048 (a positive and a negative score bin) share the 32-bit
+// words of replica set b % 2048 as low and high halves; a replica counts at
+// most kBlock / 4 * PER < 2^16 elements.
+constexpr int kHistReps = 4;
+__device__ __forceinline__ uint32_t hist_count(const uint32_t* h, int bin) {
+  const uint4 v = *reinterpret_cast<const uint4*>(h + kHistReps * (bin & 2047));
+  const int sh = 16 * (bin >> 11);
+  return ((v.x >> sh) & 0xFFFFu) + ((v.y >> sh) & 0xFFFFu) + ((v.z >> sh) & 0xFFFFu) + ((v.w >> sh) & 0xFFFFu);
+}
+
 template <int PER, int VW>
 __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
+  static_assert(kBlock / kHistReps * PER < 65536, "16-bit replica counters");
   constexpr int kChunk = PER * kBlock;
-  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistReps * kBins / 2];
   __shared__ uint32_t tmp[32];
   const int r = blockIdx.y;
   const int c = blockIdx.x;
@@ -168,21 +184,31 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   // the chunk's loads go out first, so they cost one round trip
   uint32_t d[PER];
   load_keys<PER, VW>(row, begin, end, d);
-  for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+  for (int i = threadIdx.x; i < kHistReps * kBins / 2; i += kBlock) hist[i] = 0u;
   __syncthreads();
+  const int rep = threadIdx.x & (kHistReps - 1);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) atomicAdd(&hist[d[j] >> 20], chunk_pos<VW>(begin, j) < end ? 1u : 0u);
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t bin = d[j] >> 20;
+    const uint32_t one = chunk_pos<VW>(begin, j) < end ? 1u : 0u;
+    atomicAdd(&hist[kHistReps * (bin & 2047) + rep], one << (16 * (bin >> 11)));
+  }
   __syncthreads();
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
   // the chunk's suffix counts: thread t owns bins 4095-8t down to 4088-8t
   uint32_t v[8], run = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v[i] = hist[kBins - 1 - (8 * (int)threadIdx.x + i)];
+    v[i] = hist_count(hist, kBins - 1 - (8 * (int)threadIdx.x + i));
     run += v[i];
   }
   uint32_t tot;
   uint32_t acc = block_excl_scan<kBlock>(run, tmp, &tot);
+  // and the row's histogram: the non-empty bins (the counts are in hand)
+  uint32_t* gh = ws.hist + (size_t)r * kBins;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (v[i]) atomicAdd(&gh[kBins - 1 - (8 * (int)threadIdx.x + i)], v[i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     acc += v[i];
@@ -191,10 +217,6 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   // bins 4088-8t .. 4095-8t ascending, 16-bit counts, one 16-byte store
   uint4* suf = reinterpret_cast<uint4*>(ws.suf + ((size_t)r * ws.nchunk + c) * kBins + kBins - 8 - 8 * (int)threadIdx.x);
   *suf = make_uint4(v[7] | (v[6] << 16), v[5] | (v[4] << 16), v[3] | (v[2] << 16), v[1] | (v[0] << 16));
-  // and the row's histogram: the non-empty bins
-  uint32_t* gh = ws.hist + (size_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kBlock)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
 // The single-workgroup refinement of a row's candidate list: n candidates
@@ -390,12 +412,12 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
 // MAPPED: outputs go through the slot map (their pages are looked up per
 // winner); otherwise the chunk's page-table entries are staged in LDS
 template <int PER, bool MAPPED, int VW>
-__global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[32];
   __shared__ uint32_t before[2];
-  __shared__ int pages[MAPPED ? 1 : kChunk + 1];
+  __shared__ int pages[MAPPED ? 1 : kSelPages];
   const int r = blockIdx.y;
   const int c = blockIdx.x;
   const int L = row_len(a, r);
@@ -421,15 +443,18 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   load_keys<PER, VW>(row, begin, end, key);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
   for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = gh[i];
-  const bool lds_pages = !MAPPED && a.phys;
+  bool lds_pages = !MAPPED && a.phys;
   int pg0 = 0, off;
   if (lds_pages) {
     int pg1;
     split_pos(begin, a.page_size, pg0, off);
     split_pos(end - 1, a.page_size, pg1, off);
     const int npg = pg1 - pg0 + 1;
-    const int* pt = a.page_table + (int64_t)r * a.max_pages + pg0;
-    for (int i = threadIdx.x; i < npg; i += kBlock) pages[i] = pt[i];
+    lds_pages = npg <= kSelPages;   // else (tiny pages) each winner looks its page up
+    if (lds_pages) {
+      const int* pt = a.page_table + (int64_t)r * a.max_pages + pg0;
+      for (int i = threadIdx.x; i < npg; i += kBlock) pages[i] = pt[i];
+    }
   }
   if (threadIdx.x < 2) before[threadIdx.x] = 0u;
   __syncthreads();
@@ -476,37 +501,47 @@ __global__ __launch_bounds__(kBlock) void topk_select_kernel(TopkArgs a) {
   const uint32_t pre = block_excl_scan<kBlock>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot);
   uint32_t ow = before[0] + (pre & 0xFFFF);
   uint32_t oc = before[1] + (pre >> 16);
-  int wv[PER], wp[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = chunk_pos<VW>(begin, j);
-    wv[j] = ((win >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
-  }
-  if (lds_pages) {
-    // every page read first, then the rows (non-winners read a valid dummy)
-    int pg[PER], po[PER], page[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) split_pos(max(wv[j], begin), a.page_size, pg[j], po[j]);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) page[j] = pages[pg[j] - pg0];
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      wp[j] = (wv[j] >= 0 && (unsigned)page[j] < (unsigned)a.num_pages) ? page[j] * a.page_size + po[j] : -1;
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
-  }
+  // threshold-bin members first (their keys are then dead), then the
+  // winners in groups of eight (fewer live registers: four workgroups fit
+  // per compute unit)
   int2* cand = ws.cand + (size_t)r * a.max_len;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if ((win >> j) & 1u) {
-      if (ow < (uint32_t)a.k) {
-        a.idx[(int64_t)r * a.k + ow] = wv[j];
-        if (a.phys) a.phys[(int64_t)r * a.k + ow] = wp[j];
-      }
-      ++ow;
-    }
+  for (int j = 0; j < PER; ++j)
     if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
+  constexpr int G = PER < 8 ? PER : 8;
+#pragma unroll
+  for (int g0 = 0; g0 < PER; g0 += G) {
+    int wv[G], wp[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = g0 + u;
+      const int i = chunk_pos<VW>(begin, j);
+      wv[u] = ((win >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
+    }
+    if (lds_pages) {
+      // every page read first, then the rows (non-winners read a valid dummy)
+      int pg[G], po[G], page[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) split_pos(max(wv[u], begin), a.page_size, pg[u], po[u]);
+#pragma unroll
+      for (int u = 0; u < G; ++u) page[u] = pages[pg[u] - pg0];
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        wp[u] = (wv[u] >= 0 && (unsigned)page[u] < (unsigned)a.num_pages) ? page[u] * a.page_size + po[u] : -1;
+    } else {
+#pragma unroll
+      for (int u = 0; u < G; ++u) wp[u] = a.phys ? phys_of(a, r, wv[u]) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if ((win >> (g0 + u)) & 1u) {
+        if (ow < (uint32_t)a.k) {
+          a.idx[(int64_t)r * a.k + ow] = wv[u];
+          if (a.phys) a.phys[(int64_t)r * a.k + ow] = wp[u];
+        }
+        ++ow;
+      }
+    }
   }
 }
 
