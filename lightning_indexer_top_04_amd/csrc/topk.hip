@@ -173,8 +173,8 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
   __shared__ __attribute__((aligned(16))) uint32_t hist[kHistReps * kBins / 2];
   __shared__ uint32_t tmp[32];
-  const int r = blockIdx.y;
-  const int c = blockIdx.x;
+  const int r = blockIdx.x;   // rows fastest: every row's early (full) chunks
+  const int c = blockIdx.y;   // are dispatched before the empty tails
   const int L = row_len(a, r);
   if (L <= a.k) return;
   const int begin = c * kChunk;
@@ -418,8 +418,8 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t tmp[32];
   __shared__ uint32_t before[2];
   __shared__ int pages[MAPPED ? 1 : kSelPages];
-  const int r = blockIdx.y;
-  const int c = blockIdx.x;
+  const int r = blockIdx.x;   // rows fastest: every row's early (full) chunks
+  const int c = blockIdx.y;   // are dispatched before the empty tails
   const int L = row_len(a, r);
   const int begin = c * kChunk;
   if (begin >= max(L, 1)) return;
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   if (L <= a.k) {
     // every element is kept; workgroup 0 also pads and counts
     emit_range<kBlock>(a, r, begin, end - begin, [&](uint32_t i) { return begin + (int)i; });
-    if (blockIdx.x == 0) {
+    if (c == 0) {
       if (L < a.k) emit_range<kBlock>(a, r, L, a.k - L, [](uint32_t) { return -1; });
       if (threadIdx.x == 0) a.count[r] = L;
     }
@@ -788,7 +788,7 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   const int64_t want = ceil_div((int64_t)a.num_req * a.max_len, 2 * (int64_t)num_cus());
   int per = kMinChunk / kBlock;
   while (per * kBlock < kMaxChunk && per * kBlock < want) per *= 2;
-  dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)), (unsigned)a.num_req);
+  dim3 grid((unsigned)a.num_req, (unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)));
   const bool mapped = a.map != nullptr;
   // rows that start on 16-byte boundaries are read 4 (or 2) scores per load
   const bool vec = reinterpret_cast<uintptr_t>(a.scores) % 16 == 0 && a.ld % 4 == 0;
