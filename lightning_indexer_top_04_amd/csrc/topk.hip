@@ -154,24 +154,32 @@ __device__ __forceinline__ void load_keys(const float* row, int begin, int end, 
   }
 }
 
-// Histogram counters: four replicas of each bin (lane % 4 picks one), so
-// that the lanes of a wave that hit one bin, as most do when the scores
-// crowd into a few bins, serialise four times less on the LDS atomic.  Bins
-// b and b + 2048 (a positive and a negative score bin) share the 32-bit
-// words of replica set b % 2048 as low and high halves; a replica counts at
-// most kBlock / 4 * PER < 2^16 elements.
-constexpr int kHistReps = 4;
+// Histogram counters in REPS replicas of each bin (lane % REPS picks one):
+// with several scores per thread, the lanes of a wave that hit one bin, as
+// most do when the scores crowd into a few bins, serialise REPS times less
+// on the LDS atomic.  Bins b and b + 2048 (a positive and a negative score
+// bin) share the 32-bit words of replica set b % 2048 as low and high
+// halves; a replica counts at most kBlock / REPS * PER < 2^16 elements.
+template <int PER>
+constexpr int hist_reps() { return PER >= 8 ? 4 : 1; }
+template <int REPS>
 __device__ __forceinline__ uint32_t hist_count(const uint32_t* h, int bin) {
-  const uint4 v = *reinterpret_cast<const uint4*>(h + kHistReps * (bin & 2047));
   const int sh = 16 * (bin >> 11);
-  return ((v.x >> sh) & 0xFFFFu) + ((v.y >> sh) & 0xFFFFu) + ((v.z >> sh) & 0xFFFFu) + ((v.w >> sh) & 0xFFFFu);
+  if constexpr (REPS == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(h + 4 * (bin & 2047));
+    return ((v.x >> sh) & 0xFFFFu) + ((v.y >> sh) & 0xFFFFu) + ((v.z >> sh) & 0xFFFFu) + ((v.w >> sh) & 0xFFFFu);
+  } else {
+    static_assert(REPS == 1, "one or four replicas");
+    return (h[bin & 2047] >> sh) & 0xFFFFu;
+  }
 }
 
 template <int PER, int VW>
 __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
-  static_assert(kBlock / kHistReps * PER < 65536, "16-bit replica counters");
+  constexpr int kReps = hist_reps<PER>();
+  static_assert(kBlock / kReps * PER < 65536, "16-bit replica counters");
   constexpr int kChunk = PER * kBlock;
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistReps * kBins / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kReps * kBins / 2];
   __shared__ uint32_t tmp[32];
   const int r = blockIdx.x;   // rows fastest: every row's early (full) chunks
   const int c = blockIdx.y;   // are dispatched before the empty tails
@@ -184,14 +192,14 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   // the chunk's loads go out first, so they cost one round trip
   uint32_t d[PER];
   load_keys<PER, VW>(row, begin, end, d);
-  for (int i = threadIdx.x; i < kHistReps * kBins / 2; i += kBlock) hist[i] = 0u;
+  for (int i = threadIdx.x; i < kReps * kBins / 2; i += kBlock) hist[i] = 0u;
   __syncthreads();
-  const int rep = threadIdx.x & (kHistReps - 1);
+  const int rep = threadIdx.x & (kReps - 1);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const uint32_t bin = d[j] >> 20;
     const uint32_t one = chunk_pos<VW>(begin, j) < end ? 1u : 0u;
-    atomicAdd(&hist[kHistReps * (bin & 2047) + rep], one << (16 * (bin >> 11)));
+    atomicAdd(&hist[kReps * (bin & 2047) + rep], one << (16 * (bin >> 11)));
   }
   __syncthreads();
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
@@ -199,16 +207,11 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   uint32_t v[8], run = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v[i] = hist_count(hist, kBins - 1 - (8 * (int)threadIdx.x + i));
+    v[i] = hist_count<kReps>(hist, kBins - 1 - (8 * (int)threadIdx.x + i));
     run += v[i];
   }
   uint32_t tot;
   uint32_t acc = block_excl_scan<kBlock>(run, tmp, &tot);
-  // and the row's histogram: the non-empty bins (the counts are in hand)
-  uint32_t* gh = ws.hist + (size_t)r * kBins;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (v[i]) atomicAdd(&gh[kBins - 1 - (8 * (int)threadIdx.x + i)], v[i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     acc += v[i];
@@ -217,6 +220,14 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   // bins 4088-8t .. 4095-8t ascending, 16-bit counts, one 16-byte store
   uint4* suf = reinterpret_cast<uint4*>(ws.suf + ((size_t)r * ws.nchunk + c) * kBins + kBins - 8 - 8 * (int)threadIdx.x);
   *suf = make_uint4(v[7] | (v[6] << 16), v[5] | (v[4] << 16), v[3] | (v[2] << 16), v[1] | (v[0] << 16));
+  // and the row's histogram: the non-empty bins, consecutive bins in
+  // consecutive lanes (the few hot bins share a cache line, which then takes
+  // one atomic request per wave instead of one per lane group)
+  uint32_t* gh = ws.hist + (size_t)r * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kBlock) {
+    const uint32_t n = hist_count<kReps>(hist, i);
+    if (n) atomicAdd(&gh[i], n);
+  }
 }
 
 // The single-workgroup refinement of a row's candidate list: n candidates
