@@ -126,32 +126,42 @@ __device__ __forceinline__ int chunk_pos(int begin, int j) {
 }
 // The chunk's PER keys of this thread, every load issued before the first
 // use; positions past `end` read the last score (and are not counted).
+// Keeps the scheduler from moving anything across this point.  Loads are
+// issued above it and their values used below it: without it the compiler,
+// short of registers, pairs each load with its use, and a batch of loads
+// becomes a chain of round trips.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 template <int PER, int VW>
 __device__ __forceinline__ void load_keys(const float* row, int begin, int end, uint32_t (&key)[PER]) {
   static_assert(PER % VW == 0, "runs tile the chunk");
+  float x[PER];
 #pragma unroll
   for (int q = 0; q < PER / VW; ++q) {
     const int p = chunk_pos<VW>(begin, q * VW);
     if constexpr (VW == 4) {
       if (p + 4 <= end) {
         const float4 v = *reinterpret_cast<const float4*>(row + p);
-        key[4 * q] = float_key(v.x);
-        key[4 * q + 1] = float_key(v.y);
-        key[4 * q + 2] = float_key(v.z);
-        key[4 * q + 3] = float_key(v.w);
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
         continue;
       }
     } else if constexpr (VW == 2) {
       if (p + 2 <= end) {
         const float2 v = *reinterpret_cast<const float2*>(row + p);
-        key[2 * q] = float_key(v.x);
-        key[2 * q + 1] = float_key(v.y);
+        x[2 * q] = v.x;
+        x[2 * q + 1] = v.y;
         continue;
       }
     }
 #pragma unroll
-    for (int e = 0; e < VW; ++e) key[q * VW + e] = float_key(row[min(p + e, end - 1)]);
+    for (int e = 0; e < VW; ++e) x[q * VW + e] = row[min(p + e, end - 1)];
   }
+  issue_fence();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) key[j] = float_key(x[j]);
 }
 
 // Histogram counters in REPS replicas of each bin (lane % REPS picks one):
@@ -453,7 +463,14 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   uint32_t key[PER];
   load_keys<PER, VW>(row, begin, end, key);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = gh[i];
+  {
+    uint32_t hv[kBins / kBlock];
+#pragma unroll
+    for (int m = 0; m < kBins / kBlock; ++m) hv[m] = gh[threadIdx.x + m * kBlock];
+    issue_fence();
+#pragma unroll
+    for (int m = 0; m < kBins / kBlock; ++m) hist[threadIdx.x + m * kBlock] = hv[m];
+  }
   bool lds_pages = !MAPPED && a.phys;
   int pg0 = 0, off;
   if (lds_pages) {
@@ -464,7 +481,12 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
     lds_pages = npg <= kSelPages;   // else (tiny pages) each winner looks its page up
     if (lds_pages) {
       const int* pt = a.page_table + (int64_t)r * a.max_pages + pg0;
-      for (int i = threadIdx.x; i < npg; i += kBlock) pages[i] = pt[i];
+      static_assert(kSelPages <= 2 * kBlock, "two page ids per thread");
+      const int p0 = threadIdx.x < npg ? pt[threadIdx.x] : 0;
+      const int p1 = threadIdx.x + kBlock < npg ? pt[threadIdx.x + kBlock] : 0;
+      issue_fence();
+      if (threadIdx.x < npg) pages[threadIdx.x] = p0;
+      if (threadIdx.x + kBlock < npg) pages[threadIdx.x + kBlock] = p1;
     }
   }
   if (threadIdx.x < 2) before[threadIdx.x] = 0u;
@@ -627,6 +649,15 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
 constexpr int kRowThreads = 1024;
 constexpr int kRowCap = 8192;     // candidates held in LDS
 
+// NB batches of kRowThreads * kBatch scores stay in registers for all three
+// passes (a row of up to NB batches is read from memory once); batches past
+// them are streamed again by every pass.  One resident batch: holding whole
+// 64K-score rows (NB = 9, 72 registers of keys) spills at 128 VGPRs and ran
+// slower than streaming them three times.
+// LOOKUP: the row has a slot map or physical rows to look up per winner.
+// Without it the select pass loads nothing: a load there is waited for with
+// vmcnt(0), which also waits for every earlier batch's winner stores.
+template <int NB, bool LOOKUP>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t lkey[kRowCap];
@@ -647,34 +678,49 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     return;
   }
   // pass 0: key range of the row
-  // (each streaming pass issues kBatch loads per thread before using any;
+  // (each streaming batch issues kBatch loads per thread before using any;
   // indexes past the end are clamped to the last element, which is harmless
-  // for the minimum and maximum and not counted elsewhere.  The first batch
-  // stays in registers for the later passes: rows of up to 8192 are read
-  // from memory once.)
+  // for the minimum and maximum and not counted elsewhere)
   constexpr int kStride = kRowThreads * kBatch;
-  uint32_t k0[kBatch];
+  const int nbat = (L + kStride - 1) / kStride;
+  uint32_t kr[NB][kBatch];
+  {
+    float x[NB][kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) k0[j] = float_key(row[min(tid + j * kRowThreads, L - 1)]);
-  auto keys_of = [&](int b, uint32_t (&kk)[kBatch]) {
-    if (b == tid) {
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) kk[j] = k0[j];
-    } else {
+      for (int j = 0; j < kBatch; ++j)
+        x[bi][j] = bi < nbat ? row[min(tid + bi * kStride + j * kRowThreads, L - 1)] : 0.f;
+    issue_fence();
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) kk[j] = float_key(row[min(b + j * kRowThreads, L - 1)]);
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) kr[bi][j] = bi < nbat ? float_key(x[bi][j]) : 0u;
+  }
+  // f(b, keys) for every batch b of this thread, the resident ones first
+  auto for_batches = [&](auto&& f) {
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+      if (bi < nbat) f(tid + bi * kStride, kr[bi]);
+    for (int b = tid + NB * kStride; b < L; b += kStride) {
+      float x[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) x[j] = row[min(b + j * kRowThreads, L - 1)];
+      issue_fence();
+      uint32_t kk[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) kk[j] = float_key(x[j]);
+      f(b, kk);
     }
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int b = tid; b < L; b += kStride) {
-    uint32_t kk[kBatch];
-    keys_of(b, kk);
+  for_batches([&](int, const uint32_t (&kk)[kBatch]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       kmin = min(kmin, kk[j]);
       kmax = max(kmax, kk[j]);
     }
-  }
+  });
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
@@ -695,23 +741,20 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   const int span = range ? 32 - __clz(range) : 0;      // bits of the range
   const int shift = span > 12 ? span - 12 : 0;
   // pass 1
-  for (int b = tid; b < L; b += kStride) {
-    uint32_t kk[kBatch];
-    keys_of(b, kk);
+  for_batches([&](int b, const uint32_t (&kk)[kBatch]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) atomicAdd(&hist[(kk[j] - kmin) >> shift], b + j * kRowThreads < L ? 1u : 0u);
-  }
+  });
   __syncthreads();
   uint32_t better;
   const uint32_t digit = (uint32_t)find_threshold<kRowThreads>(hist, (uint32_t)a.k, true, tmp, &better);
   int32_t* list = carve(a.ws, a.num_req, a.max_len).list + (size_t)r * a.max_len;
   // pass 2
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = tid; b < L; b += kStride) {
+  for_batches([&](int b, const uint32_t (&kk)[kBatch]) {
     uint32_t rel[kBatch];
-    keys_of(b, rel);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) rel[j] -= kmin;
+    for (int j = 0; j < kBatch; ++j) rel[j] = kk[j] - kmin;
     uint64_t bw[kBatch], be[kBatch];
     uint32_t nw = 0, ne = 0;
 #pragma unroll
@@ -738,15 +781,18 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     for (int j = 0; j < kBatch; ++j) {
       wo[j] = wb + (uint32_t)__popcll(bw[j] & below);
       wb += (uint32_t)__popcll(bw[j]);
-      wv[j] = ((bw[j] >> lane) & 1ull) ? out_value(a, r, b + j * kRowThreads) : -1;
+      const int i = b + j * kRowThreads;
+      wv[j] = ((bw[j] >> lane) & 1ull) ? (LOOKUP ? out_value(a, r, i) : i) : -1;
     }
+    if constexpr (LOOKUP) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
+      for (int j = 0; j < kBatch; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if ((bw[j] >> lane) & 1ull) {
         a.idx[(int64_t)r * a.k + wo[j]] = wv[j];
-        if (a.phys) a.phys[(int64_t)r * a.k + wo[j]] = wp[j];
+        if (LOOKUP && a.phys) a.phys[(int64_t)r * a.k + wo[j]] = wp[j];
       }
     }
 #pragma unroll
@@ -762,7 +808,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
       }
       eb += (uint32_t)__popcll(be[j]);
     }
-  }
+  });
   __syncthreads();
   const uint32_t n = cnt[1];
   refine_cands<kRowThreads, kRowCap>(a, r, n, (uint32_t)a.k - better, better, list, n <= (uint32_t)kRowCap,
@@ -788,7 +834,10 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   // rows enough to fill every compute unit, or short ones: one workgroup per
   // row is enough parallelism and needs no hand-over between workgroups
   if (a.num_req >= num_cus() || a.max_len <= 32768) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(a.num_req), dim3(kRowThreads), 0, s, a);
+    if (a.map != nullptr || a.phys != nullptr)
+      hipLaunchKernelGGL((topk_row_kernel<1, true>), dim3(a.num_req), dim3(kRowThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((topk_row_kernel<1, false>), dim3(a.num_req), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
   }
   if (ws_state == 0) {
