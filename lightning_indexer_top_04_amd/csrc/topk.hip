@@ -844,10 +844,13 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
     const hipError_t e = launch_zero(static_cast<uint32_t*>(a.ws), topk_zero_words(a.num_req), s);
     if (e != hipSuccess) return e;
   }
-  // chunks sized for about two workgroups per compute unit
+  // chunks sized for about two workgroups per compute unit, and at most 256
+  // chunks per row: every chunk adds to the row histogram's few hot bins,
+  // whose atomics serialise (a 524288-score row in 512 chunks spent 10 us
+  // in the histogram launch, 4 us less in 128)
   const int64_t want = ceil_div((int64_t)a.num_req * a.max_len, 2 * (int64_t)num_cus());
   int per = kMinChunk / kBlock;
-  while (per * kBlock < kMaxChunk && per * kBlock < want) per *= 2;
+  while (per * kBlock < kMaxChunk && (per * kBlock < want || ceil_div(a.max_len, per * kBlock) > 256)) per *= 2;
   dim3 grid((unsigned)a.num_req, (unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)));
   const bool mapped = a.map != nullptr;
   // rows that start on 16-byte boundaries are read 4 (or 2) scores per load
