@@ -88,6 +88,26 @@ def test_scan_fp8_balanced_slices(lens):
             check_scores(sc[b, :L], ref, mag, f"req {b}")
 
 
+@pytest.mark.parametrize("R", [192, 193])
+def test_scan_fp8_balanced_slices_at_the_request_limit(R):
+    """Many short ragged requests: 192 take the balanced grid (at most a
+    quarter of the 768 resident workgroups), 193 the grid of one row per
+    request.  Every score of every request either way."""
+    rng = np.random.default_rng(R)
+    lens = [int(x) for x in rng.integers(1, 1300, size=R)]
+    lens[0] = 1300
+    di = small_dsa(lens, n_planted=4, attn=False)
+    ov = OracleView(di)
+    ik, req, _, _ = objs(di)
+    s = lsi.index_scores(ik, req, di.q_idx, di.w)
+    torch.cuda.synchronize()
+    sc = s.cpu().numpy()
+    for b in range(R):
+        L = ov.L(b)
+        ref, mag = ov.scores(b)
+        check_scores(sc[b, :L], ref, mag, f"req {b}")
+
+
 def test_scan_f32_tiny_case():
     di = synth.make_decode_inputs(synth.TINY_F32, device=DEV, with_attn=False)
     ov = OracleView(di)
