@@ -192,9 +192,11 @@ def main():
     # back-to-back launches on the stream (the figure reported) and the same
     # launches replayed from one graph (for comparison: graph replays insert
     # their own inter-node synchronisation, which is slower here)
-    t_sus = event_loop(lambda i: lsi.index_scores(ik, req_all, di.q_idx, di.w,
-                                                  scores=scores_all, stream=stream),
-                       n_sus, stream)
+    # five windows of 20 launches; the median window is reported
+    sus_windows = sorted(event_loop(lambda i: lsi.index_scores(ik, req_all, di.q_idx, di.w,
+                                                               scores=scores_all, stream=stream),
+                                    n_sus, stream) for _ in range(5))
+    t_sus = sus_windows[2]
     g_sus = capture([lambda: lsi.index_scores(ik, req_all, di.q_idx, di.w, scores=scores_all)
                      for _ in range(n_sus)])
     g_sus.replay()
@@ -232,7 +234,9 @@ def main():
                            "tokens_per_s": R * L / (t_sus * 1e-3), "GB_s": sus_gbs,
                            "frac": sus_gbs / HBM_PEAK_GBS,
                            "bytes_per_token": SCAN_BYTES_PER_TOKEN,
-                           "timing": "HIP events around 20 back-to-back launches on one stream",
+                           "timing": "HIP events around 20 back-to-back launches on one stream; "
+                                     "median of 5 such windows",
+                           "us_windows_min_max": [sus_windows[0] * 1e3, sus_windows[-1] * 1e3],
                            "us_graph_replay": t_sus_graph * 1e3},
         # the whole step against its algorithmic HBM time: the scan's keys and
         # scales, the gathered latent rows, the query and the output
