@@ -626,7 +626,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
   const int64_t bh = blockIdx.x;
   const float* pl = part_lse + bh * nsplit;
   if (threadIdx.x < 64) {
-    const float ls = threadIdx.x < nsplit ? pl[threadIdx.x] : -INFINITY;
+    const float ls = (int)threadIdx.x < nsplit ? pl[threadIdx.x] : -INFINITY;
     float M = ls;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.f : exp2f(ls - M);

@@ -315,7 +315,6 @@ struct DmaTile {
   static constexpr int kMoves = kBytes / 1024;
   static constexpr int kOps = kMoves + 1;
 };
-constexpr int kTileBytes = DmaTile<KIND_FP8>::kBytes;
 constexpr int kFlushTiles = 32;             // tiles of scores staged per wave (4 KB)
 
 // Key tiles are read once: the non-temporal hint keeps them from evicting the

@@ -482,11 +482,12 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
     if (lds_pages) {
       const int* pt = a.page_table + (int64_t)r * a.max_pages + pg0;
       static_assert(kSelPages <= 2 * kBlock, "two page ids per thread");
-      const int p0 = threadIdx.x < npg ? pt[threadIdx.x] : 0;
-      const int p1 = threadIdx.x + kBlock < npg ? pt[threadIdx.x + kBlock] : 0;
+      const int t = threadIdx.x;
+      const int p0 = t < npg ? pt[t] : 0;
+      const int p1 = t + kBlock < npg ? pt[t + kBlock] : 0;
       issue_fence();
-      if (threadIdx.x < npg) pages[threadIdx.x] = p0;
-      if (threadIdx.x + kBlock < npg) pages[threadIdx.x + kBlock] = p1;
+      if (t < npg) pages[t] = p0;
+      if (t + kBlock < npg) pages[t + kBlock] = p1;
     }
   }
   if (threadIdx.x < 2) before[threadIdx.x] = 0u;
