@@ -187,17 +187,23 @@ def _planted_positions(L, n, g_cpu):
 
 def make_decode_inputs(wl: Workload, device="cpu", planted: bool = True,
                        with_int4: bool = False,
-                       with_attn: bool = True) -> DecodeInputs:
+                       with_attn: bool = True, layer: int = 0) -> DecodeInputs:
     """Draw one decode step's inputs for workload wl.
 
     Small per-request tensors (q, w, page tables, planted positions) are
     drawn on the CPU and moved; the large pools are drawn on `device`.
+    `layer` > 0 draws another layer of the same batch: the same lengths and
+    page table (the layers of a model share them), its own queries, weights,
+    keys and planted positions.
     """
     g_cpu = _gen(wl.seed, "cpu")
     g_dev = _gen(wl.seed + 1000, device)
     seq = draw_seq_lens(wl, g_cpu)
     B = len(seq)
     pt, P = make_page_table(seq, g_cpu)
+    if layer:
+        g_cpu = _gen(wl.seed + 7919 * layer, "cpu")
+        g_dev = _gen(wl.seed + 1000 + 7919 * layer, device)
     H, d = wl.n_idx_heads, wl.idx_dim
 
     if wl.key_dtype == "f32":

@@ -36,6 +36,10 @@ Parity status per function
                                                publish no figure)
   prefill_index_topk                           pinned (reduces to decode on the
                                                visible prefix; causality)
+  selection_source, multilayer_decode          pinned (hand tables of the layer
+                                               schedule; reductions to
+                                               decode_step; identical adjacent
+                                               selections make MLI a no-op)
 """
 from __future__ import annotations
 
@@ -45,7 +49,7 @@ __all__ = [
     "decode_e4m3fn", "decode_bf16", "decode_int4",
     "request_rows", "index_scores", "score_magnitude", "topk", "band",
     "attention", "mla_decode", "decode_step", "two_stage_topk",
-    "prefill_index_topk",
+    "prefill_index_topk", "selection_source", "multilayer_decode",
 ]
 
 
@@ -278,6 +282,47 @@ def prefill_index_topk(q, w, keys, scale, hist_len: int, k: int,
         sel, tau = topk(s, k)
         res[int(i)] = (sel, tau, s)
     return res
+
+
+def selection_source(layer: int, retention: int, schedule: str) -> int:
+    """Which layer's selection layer `layer` attends ("Multi-layer Indexer"
+    abstract, first paragraph).
+
+    Indexer layers are the multiples of `retention`: IndexCache keeps an
+    indexer in one layer out of every `retention` and the rest reuse the
+    latest selection.  "serial": the latest indexer layer at or before
+    `layer` (its own selection when it has an indexer).  "mli": a layer
+    attends the selection of the previous indexer layer instead of its own,
+    i.e. the latest indexer layer strictly before it; layer 0 has none and
+    attends its own (a reading: the abstract does not treat the first layer).
+    """
+    if schedule == "serial" or layer == 0:
+        return (layer // retention) * retention
+    if schedule == "mli":
+        return ((layer - 1) // retention) * retention
+    raise ValueError(schedule)
+
+
+def multilayer_decode(layers, retention: int, schedule: str, k: int,
+                      sm_scale: float, dv: int):
+    """Several layers of one decode step for one request, each attending the
+    selection selection_source() names.
+
+    layers: list of dicts with q_idx, w, ikeys, iscale (indexer inputs, read
+    on indexer layers only), q_attn and kv (latent rows, MLA).  Returns
+    ({indexer layer: positions}, [(out, lse) per layer]).  Only what is
+    computed matters here; which kernels overlap is not visible in it.
+    """
+    sel = {}
+    for l, L in enumerate(layers):
+        if l % retention == 0:
+            s = index_scores(L["q_idx"], L["w"], L["ikeys"], L["iscale"])
+            sel[l], _ = topk(s, k)
+    outs = []
+    for l, L in enumerate(layers):
+        rows = np.sort(sel[selection_source(l, retention, schedule)])
+        outs.append(mla_decode(L["q_attn"], np.asarray(L["kv"])[rows], dv, sm_scale))
+    return sel, outs
 
 
 def lse_merge(parts):

@@ -486,3 +486,113 @@ def _attn_no_normalise(q, K, V, sc):
                                  _attn_values_from_keys, _attn_no_normalise])
 def test_attention_mutants_are_caught(mut):
     assert _fails(check_attention, mut)
+
+
+# ---- several layers: the MLI schedule and IndexCache retention ---------------
+# ("Multi-layer Indexer" abstract, first paragraph)
+
+# Which layer's selection each layer attends, written out by hand for small
+# stacks: indexer layers are the multiples of r; "serial" attends the latest
+# indexer layer at or before the layer, "mli" the latest strictly before it
+# (layer 0 attends its own).
+SOURCE_TABLES = {
+    (1, "serial", 6): [0, 1, 2, 3, 4, 5],
+    (1, "mli", 6): [0, 0, 1, 2, 3, 4],
+    (2, "serial", 6): [0, 0, 2, 2, 4, 4],
+    (2, "mli", 6): [0, 0, 0, 2, 2, 4],
+    (3, "mli", 7): [0, 0, 0, 0, 3, 3, 3],
+    (4, "serial", 9): [0, 0, 0, 0, 4, 4, 4, 4, 8],
+    (4, "mli", 9): [0, 0, 0, 0, 0, 4, 4, 4, 4],
+}
+
+
+def check_source_tables(fn):
+    for (r, sched, n), want in SOURCE_TABLES.items():
+        assert [fn(l, r, sched) for l in range(n)] == want, (r, sched)
+
+
+def test_selection_source_hand_tables():
+    check_source_tables(O.selection_source)
+
+
+def test_selection_source_invariants():
+    for r in (1, 2, 3, 5, 8):
+        for l in range(40):
+            s = O.selection_source(l, r, "serial")
+            m = O.selection_source(l, r, "mli")
+            assert s % r == 0 and m % r == 0          # always an indexer layer
+            assert s <= l < s + r                      # the latest one
+            assert m < l if l > 0 else m == 0
+            # MLI differs only on indexer layers after the first
+            assert m == (s - r if (l % r == 0 and l > 0) else s)
+
+
+def _src_mli_own(layer, r, sched):
+    return (layer // r) * r
+
+
+def _src_mli_two_back(layer, r, sched):
+    s = O.selection_source(layer, r, sched)
+    return max(s - r, 0) if sched == "mli" and layer > 0 else s
+
+
+def _src_serial_floor_wrong(layer, r, sched):
+    return O.selection_source(layer, r, sched) if sched == "mli" else layer - layer % max(r - 1, 1)
+
+
+@pytest.mark.parametrize("mut", [_src_mli_own, _src_mli_two_back, _src_serial_floor_wrong])
+def test_selection_source_mutants_are_caught(mut):
+    assert _fails(check_source_tables, mut)
+
+
+def _tiny_layers(n, rng, same_indexer=False):
+    L, HI, d, H, dk = 40, 3, 6, 4, 10
+    def indexer():
+        return dict(q_idx=rng.standard_normal((HI, d)), w=rng.uniform(0, 1, HI),
+                    ikeys=rng.standard_normal((L, d)), iscale=rng.uniform(0.5, 2.0, L))
+    shared = indexer()
+    return [dict(shared if same_indexer else indexer(),
+                 q_attn=rng.standard_normal((H, dk)), kv=rng.standard_normal((L, dk)))
+            for _ in range(n)]
+
+
+def _step(ix, at, k=8):
+    """decode_step with one layer's indexer inputs and another's attention."""
+    return O.decode_step(ix["q_idx"], ix["w"], ix["ikeys"], ix["iscale"], at["q_attn"],
+                         at["kv"], None, k, 0.3, 7)
+
+
+def test_multilayer_serial_is_decode_step_per_layer():
+    layers = _tiny_layers(5, np.random.default_rng(21))
+    sel, outs = O.multilayer_decode(layers, 1, "serial", 8, 0.3, 7)
+    for l, Ly in enumerate(layers):
+        s, _, _, out, lse = _step(Ly, Ly)
+        assert sorted(sel[l].tolist()) == sorted(s.tolist())
+        assert np.allclose(outs[l][0], out, atol=1e-12) and np.allclose(outs[l][1], lse)
+
+
+def test_multilayer_mli_and_retention_attend_the_named_layer():
+    layers = _tiny_layers(7, np.random.default_rng(22))
+    for r, sched in ((1, "mli"), (2, "serial"), (2, "mli"), (3, "mli")):
+        _, outs = O.multilayer_decode(layers, r, sched, 8, 0.3, 7)
+        for l in range(7):
+            j = SOURCE_TABLES.get((r, sched, 7), None)
+            j = j[l] if j else O.selection_source(l, r, sched)
+            _, _, _, out, lse = _step(layers[j], layers[l])
+            assert np.allclose(outs[l][0], out, atol=1e-12), (r, sched, l)
+    # the schedules differ where the selections differ
+    _, a = O.multilayer_decode(layers, 1, "serial", 8, 0.3, 7)
+    _, b = O.multilayer_decode(layers, 1, "mli", 8, 0.3, 7)
+    assert np.allclose(a[0][0], b[0][0]) and not np.allclose(a[3][0], b[3][0])
+
+
+def test_multilayer_identical_selections_make_mli_a_no_op():
+    """When neighbouring layers select the same tokens (the observation MLI
+    rests on, here exactly), attending the previous selection changes
+    nothing."""
+    layers = _tiny_layers(6, np.random.default_rng(23), same_indexer=True)
+    for r in (1, 2, 3):
+        _, a = O.multilayer_decode(layers, r, "serial", 8, 0.3, 7)
+        _, b = O.multilayer_decode(layers, r, "mli", 8, 0.3, 7)
+        for x, y in zip(a, b):
+            assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
