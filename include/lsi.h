@@ -173,6 +173,58 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys,
                         int32_t* count, void* out, float* lse,
                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- several layers of one decode step ------------------------------------
+ * MLI abstract: neighbouring layers select nearly the same tokens, so a layer
+ * may attend the selection of the previous indexer layer instead of its own;
+ * the indexer of a layer then no longer has to finish before that layer's
+ * attention and runs beside it.  The same paragraph describes IndexCache,
+ * which keeps an indexer in only a fraction 1/retention of the layers; the
+ * others reuse the latest selection.
+ *
+ * Layer l (0 <= l < n_layers) has its own caches and queries; all layers
+ * share `batch` (one page table, as the caches of one model's layers do).
+ * Layer l has an indexer when l % retention == 0; its selection goes to
+ * slot l / retention.  The selection layer l attends:
+ *   LSI_SCHED_SERIAL  that of the latest indexer layer j <= l (its own when
+ *                     it has an indexer): with retention 1 this is
+ *                     lsi_decode_step once per layer.
+ *   LSI_SCHED_MLI     that of the latest indexer layer j < l; layer 0 has
+ *                     none before it and attends its own.
+ * Arguments (per-layer arrays are HOST arrays of n_layers entries, or of
+ * n_slots = ceil(n_layers / retention) entries for idx and count):
+ *   ikeys[l]            LSI_FP8_E4M3 or LSI_F32 indexer cache (read for
+ *                       indexer layers only; the other entries are ignored)
+ *   kv[l]               LSI_BF16 latent cache, dk 576, dv 512; every layer's
+ *                       with the page size and page count of layer 0's
+ *   q_idx[l], w[l]      as for lsi_index_scores (indexer layers only)
+ *   q_attn[l], out[l], lse[l]   as for lsi_sparse_mla_decode
+ *   idx[slot] [num_req][k], count[slot] [num_req]: the selections
+ * Streams: LSI_SCHED_SERIAL enqueues everything on `stream`.  LSI_SCHED_MLI
+ * with a distinct s_index enqueues the indexer (scan and top-k) of layer l on
+ * s_index after layer l-1's attention (a model's indexer query comes from
+ * the previous layer's output) and the attention of layer l on `stream`; a
+ * layer's attention waits only for the selection it reads.  `stream`
+ * carries the final dependency.  With s_index NULL or equal to `stream`
+ * LSI_SCHED_MLI runs the same work in order on `stream`.  Calls on one
+ * device are serialised by a lock while they enqueue (they share two
+ * events).  1 <= retention <= n_layers <= 4096. */
+enum { LSI_SCHED_SERIAL = 0, LSI_SCHED_MLI = 1 };
+size_t lsi_multilayer_workspace_bytes(int32_t num_req, int32_t max_seq_len,
+                                      int32_t k, int32_t n_heads, int32_t dv);
+int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention,
+                              int32_t schedule, const lsi_paged_cache* ikeys,
+                              const lsi_paged_cache* kv,
+                              const lsi_batch* batch,
+                              const void* const* q_idx, int32_t n_idx_heads,
+                              int32_t idx_dim, const float* const* w,
+                              const void* const* q_attn, int32_t n_heads,
+                              int32_t dk, int32_t dv, float sm_scale,
+                              int32_t k, int32_t* const* idx,
+                              int32_t* const* count, void* const* out,
+                              float* const* lse, void* workspace,
+                              size_t ws_bytes, hipStream_t stream,
+                              hipStream_t s_index);
+
 /* ---- two-stage compact-key search ----------------------------------------
  * LeanSparse episode notes: decode searches compact indexer keys, then ranks
  * a short list of the original keys exactly.  Stage 1 scores every token with

@@ -259,6 +259,58 @@ struct PrefillEvents {
 std::mutex g_ev_mu;
 PrefillEvents g_ev[64];
 
+// ---- pieces shared by the single- and multi-layer decode steps ---------------
+// scan of every cached token (which also clears the top-k counters that the
+// selection uses next), then the top-k that also returns the physical rows
+int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                       const lsi_batch* batch, const void* q_idx, int32_t n_idx_heads,
+                       int32_t idx_dim, const float* w, int32_t k, int32_t* idx, int32_t* count,
+                       float* scores, int64_t ld, void* topk_ws, int32_t* phys, hipStream_t stream,
+                       const char* what) {
+  ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
+  sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
+  sa.zero_words = topk_zero_words(batch->num_req);
+  LSI_LAUNCH(run_scan(ikeys->dtype, sa, stream), std::string(what) + " (scan)");
+
+  TopkArgs t;
+  t.scores = scores;
+  t.ld = ld;
+  t.seq_lens = batch->seq_lens;
+  t.num_req = batch->num_req;
+  t.max_len = batch->max_seq_len;
+  t.k = k;
+  t.idx = idx;
+  t.count = count;
+  t.ws = topk_ws;
+  t.phys = phys;
+  t.page_table = batch->page_table;
+  t.max_pages = batch->max_pages;
+  t.page_size = kv->page_size;
+  t.num_pages = kv->num_pages;
+  LSI_LAUNCH(launch_topk(t, 1, stream), std::string(what) + " (top-k)");
+  return LSI_OK;
+}
+
+// attention over a selection whose physical rows the top-k already wrote
+int32_t enqueue_attend(const lsi_paged_cache* kv, const lsi_paged_cache* v, const lsi_batch* batch,
+                       const void* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
+                       const int32_t* idx, int32_t k, float sm_scale, void* out, float* lse,
+                       void* attn_wsp, const int32_t* phys, hipStream_t stream, const char* what) {
+  AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
+  a.phys = phys;
+  LSI_LAUNCH(run_attn(kv->dtype, a, stream), std::string(what) + " (attention)");
+  return LSI_OK;
+}
+
+// ---- multi-layer events --------------------------------------------------------
+constexpr int kMaxLayers = 4096;
+struct LayerEvents {
+  hipEvent_t attn_done = nullptr, selected = nullptr;
+  bool ready = false;
+};
+std::mutex g_ml_mu;
+LayerEvents g_ml_ev[64];
+
 }  // namespace
 }  // namespace lsi
 
@@ -266,7 +318,7 @@ using namespace lsi;
 
 extern "C" {
 
-int32_t lsi_version(void) { return 100; }
+int32_t lsi_version(void) { return 101; }
 
 const char* lsi_status_string(int32_t status) {
   switch (status) {
@@ -367,33 +419,135 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   ws += align_up((size_t)batch->num_req * k * sizeof(int32_t), kWsAlign);
   void* attn_wsp = ws;
 
-  // the scan also clears the top-k counters that the selection uses next
-  ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
-  sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
-  sa.zero_words = topk_zero_words(batch->num_req);
-  LSI_LAUNCH(run_scan(ikeys->dtype, sa, stream), "lsi_decode_step (scan)");
-
-  TopkArgs t;
-  t.scores = scores;
-  t.ld = ld;
-  t.seq_lens = batch->seq_lens;
-  t.num_req = batch->num_req;
-  t.max_len = batch->max_seq_len;
-  t.k = k;
-  t.idx = idx;
-  t.count = count;
-  t.ws = topk_ws;
-  t.phys = phys;
-  t.page_table = batch->page_table;
-  t.max_pages = batch->max_pages;
-  t.page_size = kv->page_size;
-  t.num_pages = kv->num_pages;
-  LSI_LAUNCH(launch_topk(t, 1, stream), "lsi_decode_step (top-k)");
-
-  AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
-  a.phys = phys;
-  LSI_LAUNCH(run_attn(kv->dtype, a, stream), "lsi_decode_step (attention)");
+  LSI_TRY(enqueue_select(ikeys, kv, batch, q_idx, n_idx_heads, idx_dim, w, k, idx, count, scores,
+                         ld, topk_ws, phys, stream, "lsi_decode_step"));
+  LSI_TRY(enqueue_attend(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse,
+                         attn_wsp, phys, stream, "lsi_decode_step"));
   return check_launch("lsi_decode_step");
+}
+
+size_t lsi_multilayer_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k,
+                                      int32_t n_heads, int32_t dv) {
+  if (num_req < 1 || max_seq_len < 0 || k < 1 || n_heads < 1) return 0;
+  const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
+  const size_t tk = topk_ws_bytes(num_req, max_seq_len);
+  const size_t ph = align_up((size_t)num_req * k * sizeof(int32_t), kWsAlign);
+  const size_t at = (n_heads % 16 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
+  return sc + tk + 2 * ph + at;
+}
+
+int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t schedule,
+                              const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                              const lsi_batch* batch, const void* const* q_idx,
+                              int32_t n_idx_heads, int32_t idx_dim, const float* const* w,
+                              const void* const* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
+                              float sm_scale, int32_t k, int32_t* const* idx,
+                              int32_t* const* count, void* const* out, float* const* lse,
+                              void* workspace, size_t ws_bytes, hipStream_t stream,
+                              hipStream_t s_index) {
+  LSI_REQUIRE(n_layers >= 1 && n_layers <= kMaxLayers, "n_layers must be in [1, 4096]");
+  LSI_REQUIRE(retention >= 1 && retention <= n_layers, "retention must be in [1, n_layers]");
+  LSI_REQUIRE(schedule == LSI_SCHED_SERIAL || schedule == LSI_SCHED_MLI, "unknown schedule");
+  LSI_REQUIRE(ikeys != nullptr && kv != nullptr && q_idx != nullptr && w != nullptr &&
+                  q_attn != nullptr && idx != nullptr && count != nullptr && out != nullptr &&
+                  lse != nullptr,
+              "the per-layer host arrays must be non-NULL");
+  LSI_TRY(check_batch(batch, true));
+  LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
+  const int64_t ld = scores_ld(batch->max_seq_len);
+  for (int l = 0; l < n_layers; ++l) {
+    const std::string at = "layer " + std::to_string(l) + ": ";
+    if (l % retention == 0) {
+      const int32_t st = validate_index(&ikeys[l], batch, q_idx[l], n_idx_heads, idx_dim, w[l],
+                                        nullptr, 0, true);
+      if (st != LSI_OK) return fail(st, at + g_last_error);
+      LSI_REQUIRE(ikeys[l].page_size == kv[l].page_size, at + "ikeys and kv must share the page size");
+      LSI_REQUIRE(idx[l / retention] != nullptr && count[l / retention] != nullptr,
+                  at + "idx and count must be non-NULL");
+    }
+    LSI_SUPPORT(kv[l].dtype == LSI_BF16, at + "the multi-layer step needs the bf16 latent cache");
+    LSI_REQUIRE(kv[l].num_pages == kv[0].num_pages && kv[l].page_size == kv[0].page_size,
+                at + "every layer's cache must have the shape of layer 0's");
+    const int32_t st = validate_attn(&kv[l], nullptr, batch, q_attn[l], n_heads, dk, dv,
+                                     idx[(l / retention)], k, sm_scale, out[l], lse[l]);
+    if (st != LSI_OK) return fail(st, at + g_last_error);
+  }
+  const size_t need = lsi_multilayer_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
+  LSI_TRY(check_ws(workspace, ws_bytes, need));
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
+  void* topk_ws = ws;
+  ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
+  int32_t* phys[2];
+  for (int i = 0; i < 2; ++i) {
+    phys[i] = reinterpret_cast<int32_t*>(ws);
+    ws += align_up((size_t)batch->num_req * k * sizeof(int32_t), kWsAlign);
+  }
+  void* attn_wsp = ws;
+
+  const bool mli = schedule == LSI_SCHED_MLI;
+  const bool split = mli && s_index != nullptr && s_index != stream;
+  hipStream_t si = split ? s_index : stream;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(LSI_ERR_HIP, "lsi_multilayer_decode: no current device");
+  std::lock_guard<std::mutex> lock(g_ml_mu);
+  LayerEvents& ev = g_ml_ev[dev];
+  if (split && !ev.ready) {
+    hipError_t e = hipEventCreateWithFlags(&ev.attn_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev.selected, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(LSI_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
+    ev.ready = true;
+  }
+#define LSI_HIP(expr)                                                                     \
+  do {                                                                                    \
+    const hipError_t _e = (expr);                                                         \
+    if (_e != hipSuccess)                                                                 \
+      return fail(LSI_ERR_HIP, std::string("lsi_multilayer_decode: ") + hipGetErrorString(_e)); \
+  } while (0)
+
+  // `pending`: a selection made on si that `stream` has not waited for yet.
+  // There is at most one: the next layer that reads it waits before the next
+  // indexer records the event again.
+  bool pending = false;
+  for (int l = 0; l < n_layers; ++l) {
+    const int slot = l / retention;
+    const bool indexer = l % retention == 0;
+    if (pending) {
+      LSI_HIP(hipStreamWaitEvent(stream, ev.selected, 0));
+      pending = false;
+    }
+    int src = slot;   // the selection this layer attends
+    if (indexer && mli && l > 0) {
+      // the indexer of layer l starts once layer l-1 is done (in a model its
+      // query comes from that layer's output) and runs beside the attention
+      // of layer l, which reads the previous indexer layer's selection
+      src = slot - 1;
+      if (split) {
+        LSI_HIP(hipEventRecord(ev.attn_done, stream));
+        LSI_HIP(hipStreamWaitEvent(si, ev.attn_done, 0));
+      }
+      LSI_TRY(enqueue_select(&ikeys[l], &kv[l], batch, q_idx[l], n_idx_heads, idx_dim, w[l], k,
+                             idx[slot], count[slot], scores, ld, topk_ws, phys[slot & 1], si,
+                             "lsi_multilayer_decode"));
+      if (split) {
+        LSI_HIP(hipEventRecord(ev.selected, si));
+        pending = true;   // the next layer waits for it; this one does not
+      }
+    } else if (indexer) {
+      LSI_TRY(enqueue_select(&ikeys[l], &kv[l], batch, q_idx[l], n_idx_heads, idx_dim, w[l], k,
+                             idx[slot], count[slot], scores, ld, topk_ws, phys[slot & 1], stream,
+                             "lsi_multilayer_decode"));
+    }
+    LSI_TRY(enqueue_attend(&kv[l], nullptr, batch, q_attn[l], n_heads, dk, dv, idx[src], k,
+                           sm_scale, out[l], lse[l], attn_wsp, phys[src & 1], stream,
+                           "lsi_multilayer_decode"));
+  }
+  if (pending) LSI_HIP(hipStreamWaitEvent(stream, ev.selected, 0));
+#undef LSI_HIP
+  return check_launch("lsi_multilayer_decode");
 }
 
 size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t n_cand,

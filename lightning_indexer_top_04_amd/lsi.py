@@ -18,12 +18,15 @@ LIB_PATH = os.path.join(HERE, "liblsi.so")
 # status codes and element types (include/lsi.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3, INT4 = 0, 1, 2, 3
+SCHED_SERIAL, SCHED_MLI = 0, 1
+SCHEDULES = {"serial": SCHED_SERIAL, "mli": SCHED_MLI}
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int4": INT4}
 
 EXPORTS = [
     "lsi_index_scores", "lsi_topk_workspace_bytes", "lsi_topk",
     "lsi_sparse_mla_workspace_bytes", "lsi_sparse_mla_decode",
     "lsi_decode_step_workspace_bytes", "lsi_decode_step",
+    "lsi_multilayer_workspace_bytes", "lsi_multilayer_decode",
     "lsi_two_stage_workspace_bytes", "lsi_two_stage_topk",
     "lsi_prefill_workspace_bytes", "lsi_prefill_index_topk",
     "lsi_status_string", "lsi_last_error", "lsi_version",
@@ -55,6 +58,7 @@ _S = C.c_size_t
 _F = C.c_float
 _PC = C.POINTER(PagedCache)
 _PB = C.POINTER(Batch)
+_PP = C.POINTER(C.c_void_p)
 
 _SIGS = {
     "lsi_index_scores": (_I, [_PC, _PB, _P, _I, _I, _P, _P, _L, _P]),
@@ -65,6 +69,9 @@ _SIGS = {
     "lsi_decode_step_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "lsi_decode_step": (_I, [_PC, _PC, _PC, _PB, _P, _I, _I, _P, _P, _I, _I, _I, _F, _I,
                              _P, _P, _P, _P, _P, _S, _P]),
+    "lsi_multilayer_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "lsi_multilayer_decode": (_I, [_I, _I, _I, _PC, _PC, _PB, _PP, _I, _I, _PP, _PP, _I, _I, _I,
+                                   _F, _I, _PP, _PP, _PP, _PP, _P, _S, _P, _P]),
     "lsi_two_stage_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "lsi_two_stage_topk": (_I, [_PC, _PC, _PB, _P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _S, _P]),
     "lsi_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
@@ -214,6 +221,62 @@ def decode_step(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests, q_idx: 
                                  k, _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _ptr(ws),
                                  ws.numel(), _stream(stream)), "lsi_decode_step")
     return idx, count, out, lse
+
+
+def _ptr_array(ts):
+    return (C.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in ts])
+
+
+def multilayer_workspace_bytes(B, max_seq_len, k, n_heads, dv) -> int:
+    return int(lib().lsi_multilayer_workspace_bytes(B, max_seq_len, k, n_heads, dv))
+
+
+class Layers:
+    """Per-layer descriptors and pointer arrays of lsi_multilayer_decode, built
+    once so that repeated calls (and graph capture) only pass pointers.
+
+    ikeys[l] / q_idx[l] / w[l] may be None on layers without an indexer
+    (l % retention != 0)."""
+
+    def __init__(self, ikeys: list, kvs: list, req: Requests, q_idx: list, w: list,
+                 q_attn: list, k: int, dv: int, retention: int = 1):
+        n = len(kvs)
+        assert len(ikeys) == len(q_idx) == len(w) == len(q_attn) == n
+        self.n, self.retention, self.k, self.dv, self.req = n, retention, k, dv, req
+        B, H, dk = q_attn[0].shape
+        dev = q_attn[0].device
+        self.H, self.dk = H, dk
+        idx_l = [l for l in range(n) if l % retention == 0]
+        self.HI, self.dI = q_idx[idx_l[0]].shape[1:]
+        self.n_slots = len(idx_l)
+        self.idx = [torch.empty(B, k, dtype=torch.int32, device=dev) for _ in range(self.n_slots)]
+        self.count = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(self.n_slots)]
+        self.out = [torch.empty(B, H, dv, dtype=q_attn[0].dtype, device=dev) for _ in range(n)]
+        self.lse = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(n)]
+        blank = PagedCache(0, 0, 0, 0, None, None)
+        self._keep = (ikeys, kvs, q_idx, w, q_attn)
+        self.c_ikeys = (PagedCache * n)(*[blank if c is None else c.c for c in ikeys])
+        self.c_kv = (PagedCache * n)(*[c.c for c in kvs])
+        self.c_qidx, self.c_w, self.c_qattn = _ptr_array(q_idx), _ptr_array(w), _ptr_array(q_attn)
+        self.c_idx, self.c_count = _ptr_array(self.idx), _ptr_array(self.count)
+        self.c_out, self.c_lse = _ptr_array(self.out), _ptr_array(self.lse)
+        nb = multilayer_workspace_bytes(B, req.max_seq_len, k, H, dv)
+        self.ws = _ws(nb, dev)
+
+
+def multilayer_decode(layers: Layers, sm_scale: float, schedule: str = "mli", stream=None,
+                      index_stream=None):
+    """lsi_multilayer_decode over prepared Layers; returns (idx, count, out, lse)
+    lists (selections per indexer slot, outputs per layer)."""
+    L = layers
+    s_main = _stream(stream)
+    s_idx = _stream(index_stream) if index_stream is not None else None
+    _check(lib().lsi_multilayer_decode(L.n, L.retention, SCHEDULES[schedule], L.c_ikeys, L.c_kv,
+                                       L.req.ref, L.c_qidx, L.HI, L.dI, L.c_w, L.c_qattn, L.H,
+                                       L.dk, L.dv, sm_scale, L.k, L.c_idx, L.c_count, L.c_out,
+                                       L.c_lse, _ptr(L.ws), L.ws.numel(), s_main, s_idx),
+           "lsi_multilayer_decode")
+    return L.idx, L.count, L.out, L.lse
 
 
 def two_stage_topk(ikeys4: Cache, ikeys8: Cache, req: Requests, q: torch.Tensor,

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.lsi_version() == 100
+    assert L.lsi_version() == 101
     assert L.lsi_status_string(0) == b"ok"
     assert b"invalid" in L.lsi_status_string(1)
     assert b"workspace" in L.lsi_status_string(3)
@@ -132,3 +132,49 @@ def test_prefill_and_two_stage_validation(L):
     assert L.lsi_two_stage_topk(C.byref(k8), C.byref(k4), C.byref(b), 0x5000, 64, 128,
                                 0x6000, 200, 100, 0x7000, 0x8000, None, 0x100000, 1 << 30,
                                 None) == lsi.ERR_INVALID_ARG
+
+
+def test_multilayer_validation(L):
+    b = _batch()
+    n = 4
+    ik = (lsi.PagedCache * n)(*[_cache() for _ in range(n)])
+    kv = (lsi.PagedCache * n)(*[lsi.PagedCache(lsi.BF16, 64, 8, 576, 0x4000, None)
+                                for _ in range(n)])
+    arr = lambda base, m=n: (C.c_void_p * m)(*[base + 0x100 * i for i in range(m)])
+    need = L.lsi_multilayer_workspace_bytes(1, 256, 64, 128, 512)
+    # two buffers of selection rows: larger than one layer's step
+    assert need > L.lsi_decode_step_workspace_bytes(1, 256, 64, 128, 512)
+
+    def call(n_layers=n, r=1, sched=lsi.SCHED_MLI, ikeys=ik, kvs=kv, idx=None, ws=0x100000,
+             nb=need, q_idx=None):
+        return L.lsi_multilayer_decode(n_layers, r, sched, ikeys, kvs, C.byref(b),
+                                       arr(0x10000) if q_idx is None else q_idx, 64, 128,
+                                       arr(0x20000), arr(0x30000), 128, 576, 512, 0.04, 64,
+                                       arr(0x40000) if idx is None else idx, arr(0x50000),
+                                       arr(0x60000), arr(0x70000), ws, nb, None, None)
+    assert call(n_layers=0) == lsi.ERR_INVALID_ARG
+    assert call(n_layers=5000) == lsi.ERR_INVALID_ARG
+    assert call(r=0) == lsi.ERR_INVALID_ARG
+    assert call(r=n + 1) == lsi.ERR_INVALID_ARG
+    assert call(sched=7) == lsi.ERR_INVALID_ARG
+    assert call(ikeys=None) == lsi.ERR_INVALID_ARG
+    assert call(ws=None) == lsi.ERR_WORKSPACE
+    assert call(nb=need - 1) == lsi.ERR_WORKSPACE
+    # an indexer slot without an output row
+    idx = arr(0x40000)
+    idx[2] = None
+    assert call(idx=idx) == lsi.ERR_INVALID_ARG
+    assert b"layer 2" in L.lsi_last_error()
+    # layers 1 and 3 have no indexer at retention 2: their indexer query is
+    # not read, and two selection slots suffice
+    q = arr(0x10000)
+    q[1] = q[3] = None
+    assert call(r=2, q_idx=q, idx=arr(0x40000, 2), ws=None) == lsi.ERR_WORKSPACE
+    assert call(r=1, q_idx=q, ws=None) == lsi.ERR_INVALID_ARG
+    # every layer's cache must match layer 0's shape, and be the bf16 latent
+    kv2 = (lsi.PagedCache * n)(*[lsi.PagedCache(lsi.BF16, 64, 8 if i < 3 else 9, 576, 0x4000,
+                                                None) for i in range(n)])
+    assert call(kvs=kv2) == lsi.ERR_INVALID_ARG
+    kv3 = (lsi.PagedCache * n)(*[lsi.PagedCache(lsi.F32, 64, 8, 64, 0x4000, None)
+                                 for _ in range(n)])
+    assert call(kvs=kv3) == lsi.ERR_UNSUPPORTED
