@@ -296,6 +296,38 @@ def other_workloads(lsi, synth, torch, dev):
         del g
         return e0.elapsed_time(e1) / (reps * n)
 
+    # the un-planted twin of the one-request step: no planted tokens, so the
+    # scores are one continuous distribution and the k-th score falls in a
+    # crowded histogram bin (thousands of candidates to refine); 8 rotating
+    # input sets (1.3 GB, more than the last-level cache)
+    nset, L1 = 8, 131072
+    wl = synth.scaled(synth.DSA_128K, seq_lens=(L1,) * nset, num_req=nset)
+    di = synth.make_decode_inputs(wl, device=dev, planted=False)
+    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    kv = lsi.Cache(di.kv, None, "bf16", 576)
+    reqs = [lsi.Requests(di.seq_lens[r:r + 1], di.page_table[r:r + 1], L1) for r in range(nset)]
+    views = [(di.q_idx[r:r + 1], di.w[r:r + 1], di.q_attn[r:r + 1]) for r in range(nset)]
+    k, H, dv = 2048, 128, 512
+    idx = torch.empty(1, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    o = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(1, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(lsi.decode_step_workspace_bytes(1, L1, k, H, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def unplanted_steps():
+        for r in range(nset):
+            qi, wr, qa = views[r]
+            lsi.decode_step(ik, kv, None, reqs[r], qi, wr, qa, k, wl.sm_scale, dv, out=o,
+                            lse=lse, idx=idx, count=cnt, ws=ws)
+
+    t = graph_ms(unplanted_steps, n=1, reps=10) / nset
+    out["decode_step_unplanted_l131072"] = {
+        "us_per_step": t * 1e3, "tokens_per_s": L1 / (t * 1e-3), "steps_per_s": 1e3 / t,
+        "sets": nset}
+    del di, ik, kv, reqs, views, idx, cnt, o, lse, ws
+    torch.cuda.empty_cache()
+
     # ragged batch: 64 requests, L ~ U{10000..195000}
     wl = synth.BATCH_RAGGED
     di = synth.make_decode_inputs(wl, device=dev)

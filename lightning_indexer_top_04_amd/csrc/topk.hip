@@ -34,6 +34,7 @@ constexpr int kBlock = 512;
 constexpr int kLdsCand = 16384;          // candidates refined in LDS
 constexpr int kBatch = 8;                // loads in flight per thread in a streaming pass
 constexpr int kRefPer = 8;               // candidates per thread in a refinement pass
+constexpr int kRefBatch = 4096;          // members per batch of the level-2 pass
 constexpr int kRefThreads = 1024;        // threads of the one-workgroup refinement
 constexpr int kSelPages = 520;           // page ids a select workgroup stages (8192 positions
                                          // over pages of 16 or more tokens)
@@ -340,9 +341,12 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
         const bool eq = (eqm >> j) & 1u;
         const uint64_t bw = __ballot(win);
         const uint64_t be = __ballot(eq);
+        // winners are staged behind the kept ones (te + tw <= n <= CAP) and
+        // written out below in batches: an output row that needs a page-table
+        // load would otherwise cost one round trip per j
         if (win) {
           const uint32_t o = ow + (uint32_t)__popcll(bw & below);
-          if (o < (uint32_t)a.k) emit(a, r, o, out_value(a, r, sl[j]));
+          if (o < (uint32_t)a.k) lslot[te + (o - out_pos)] = sl[j];
         }
         if (eq) {
           const uint32_t o = oe + (uint32_t)__popcll(be & below);
@@ -353,6 +357,9 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
         oe += (uint32_t)__popcll(be);
       }
       wg_sync(true);
+      if (out_pos < (uint32_t)a.k)
+        emit_range<NT>(a, r, out_pos, min(tw, (uint32_t)a.k - out_pos),
+                       [&](uint32_t i) { return lslot[te + i]; });
       out_pos += tw;
       need -= better;
       n = te;
@@ -494,6 +501,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   __syncthreads();
   uint32_t better;
   const uint32_t digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
+  const uint32_t members = hist[digit];   // of the whole row
   if (c == 0 && threadIdx.x == 0) {
     uint32_t* rec = ws.rec + (size_t)r * 4;
     rec[0] = digit;
@@ -542,6 +550,23 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 0; j < PER; ++j)
     if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
+  // the members' next 12 key bits go into the row's second histogram, so the
+  // refinement starts from it: counted in LDS first (the level-1 histogram
+  // there is no longer read), then one global add per non-empty bin
+  // (not needed when every member is kept)
+  if ((tot >> 16) != 0u && members > (uint32_t)a.k - better) {   // uniform
+    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((eq >> j) & 1u) atomicAdd(&hist[(key[j] >> 8) & (kBins - 1)], 1u);
+    __syncthreads();
+    uint32_t* g2 = ws.h2 + (size_t)r * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kBlock) {
+      const uint32_t n = hist[i];
+      if (n) atomicAdd(&g2[i], n);
+    }
+  }
   constexpr int G = PER < 8 ? PER : 8;
 #pragma unroll
   for (int g0 = 0; g0 < PER; g0 += G) {
@@ -589,49 +614,109 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
   if (L <= a.k) return;
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
   // the threshold bin's members are the candidates (everything above it has
-  // been written already); the first kRefThreads*kGather of them are loaded
-  // along with the record that says how many there are
+  // been written already); their second histogram (key bits [19:8]) was
+  // built by the select, so one ordered pass over them settles 12 more bits.
+  // The histogram, the record and the first batch of members are loaded
+  // together.
+  constexpr int kU = kRefBatch / kRefThreads;
   const uint32_t* rec = ws.rec + (size_t)r * 4;
   const int2* cand = ws.cand + (size_t)r * a.max_len;
-  int2 e0[kGather];
+  const uint32_t* g2 = ws.h2 + (size_t)r * kBins;
+  const int tid = threadIdx.x;
+  uint32_t hv[kBins / kRefThreads];
+  int2 e[kU];
 #pragma unroll
-  for (int u = 0; u < kGather; ++u) e0[u] = cand[min((int)threadIdx.x + u * kRefThreads, a.max_len - 1)];
+  for (int m = 0; m < kBins / kRefThreads; ++m) hv[m] = g2[tid + m * kRefThreads];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) e[u] = cand[min(tid + u * kRefThreads, a.max_len - 1)];
   const uint32_t better = rec[1];
   const uint32_t n = rec[2];
-  int32_t* list = ws.list + (size_t)r * a.max_len;
-  const bool in_lds = n <= (uint32_t)kLdsCand;
-  if (in_lds) {
+  issue_fence();
 #pragma unroll
-    for (int u = 0; u < kGather; ++u) {
-      const uint32_t i = threadIdx.x + u * kRefThreads;
-      if (i < n) {
-        lslot[i] = e0[u].x;
-        lkey[i] = (uint32_t)e0[u].y;
+  for (int m = 0; m < kBins / kRefThreads; ++m) hist[tid + m * kRefThreads] = hv[m];
+  const uint32_t need = (uint32_t)a.k - better;
+  if (n <= need) {
+    // every member is kept (then n == need): written out directly, every
+    // output row (and its page) looked up before any store
+    for (uint32_t base = 0; base < n; base += kRefBatch) {
+      if (base > 0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) e[u] = cand[min(base + tid + u * kRefThreads, n - 1)];
       }
-    }
-    if (n > (uint32_t)(kRefThreads * kGather)) {
-      // the rest in one batch of loads (a loop of smaller batches would
-      // cost a round trip each)
-      constexpr int kRest = kLdsCand / kRefThreads - kGather;
-      int2 e[kRest];
+      int wv[kU], wp[kU];
 #pragma unroll
-      for (int u = 0; u < kRest; ++u)
-        e[u] = cand[min(threadIdx.x + (u + kGather) * kRefThreads, n - 1)];
+      for (int u = 0; u < kU; ++u) wv[u] = base + tid + u * kRefThreads < n ? out_value(a, r, e[u].x) : -1;
 #pragma unroll
-      for (int u = 0; u < kRest; ++u) {
-        const uint32_t i = threadIdx.x + (u + kGather) * kRefThreads;
+      for (int u = 0; u < kU; ++u) wp[u] = a.phys ? phys_of(a, r, wv[u]) : -1;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = base + tid + u * kRefThreads;
         if (i < n) {
-          lslot[i] = e[u].x;
-          lkey[i] = (uint32_t)e[u].y;
+          a.idx[(int64_t)r * a.k + better + i] = wv[u];
+          if (a.phys) a.phys[(int64_t)r * a.k + better + i] = wp[u];
         }
       }
     }
-  } else {
-    for (uint32_t i = threadIdx.x; i < n; i += kRefThreads) list[i] = cand[i].x;
+    if (tid == 0) a.count[r] = (int32_t)(better + n);
+    return;
   }
-  __syncthreads();
-  refine_cands<kRefThreads, kLdsCand>(a, r, n, (uint32_t)a.k - better, better, list, in_lds, hist, tmp, lkey,
-                                 lslot, 20, 0u);
+  wg_sync(true);
+  uint32_t better2;
+  const uint32_t bin2 = (uint32_t)find_threshold<kRefThreads>(hist, need, true, tmp, &better2, true);
+  const uint32_t n2 = hist[bin2];
+  const bool in_lds = n2 <= (uint32_t)kLdsCand;
+  int32_t* list = ws.list + (size_t)r * a.max_len;
+  uint32_t ow = better, oe = 0;
+  for (uint32_t base = 0; base < n; base += kRefBatch) {
+    if (base > 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) e[u] = cand[min(base + tid + u * kRefThreads, n - 1)];
+    }
+    uint32_t win = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (base + tid + u * kRefThreads < n) {
+        const uint32_t d = ((uint32_t)e[u].y >> 8) & (kBins - 1);
+        win |= (uint32_t)(d > bin2) << u;
+        eq |= (uint32_t)(d == bin2) << u;
+      }
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<kRefThreads>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot, true);
+    uint32_t o = ow + (pre & 0xFFFF);
+    uint32_t q = oe + (pre >> 16);
+    // winners: every output row (and its page) is looked up before any store
+    int wv[kU], wp[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) wv[u] = ((win >> u) & 1u) ? out_value(a, r, e[u].x) : -1;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) wp[u] = a.phys ? phys_of(a, r, wv[u]) : -1;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if ((win >> u) & 1u) {
+        if (o < (uint32_t)a.k) {
+          a.idx[(int64_t)r * a.k + o] = wv[u];
+          if (a.phys) a.phys[(int64_t)r * a.k + o] = wp[u];
+        }
+        ++o;
+      }
+      if ((eq >> u) & 1u) {
+        if (in_lds) {
+          lslot[q] = e[u].x;
+          lkey[q] = (uint32_t)e[u].y;
+        } else {
+          list[q] = e[u].x;
+        }
+        ++q;
+      }
+    }
+    ow += tot & 0xFFFF;
+    oe += tot >> 16;
+  }
+  wg_sync(in_lds);
+  // the members that share the level-2 digit: key bits [7:0], then position
+  refine_cands<kRefThreads, kLdsCand>(a, r, n2, need - better2, better + better2, list, in_lds, hist,
+                                      tmp, lkey, lslot, 8, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -820,10 +905,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
 
 size_t topk_ws_bytes(int num_req, int max_len) {
   const size_t R = (size_t)num_req;
-  return align_up(R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (3 * R * max_len + 4 * R) * 4, 256);
+  return align_up(2 * R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (3 * R * max_len + 4 * R) * 4, 256);
 }
 
-int64_t topk_zero_words(int num_req) { return (int64_t)num_req * kBins; }
+int64_t topk_zero_words(int num_req) { return (int64_t)num_req * 2 * kBins; }
 
 hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t s) {
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, kBlock * 4), 1024));

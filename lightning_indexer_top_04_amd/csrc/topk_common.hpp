@@ -11,10 +11,12 @@ constexpr int kBins = 4096;      // 12-bit digits
 constexpr int kMinChunk = 1024;  // smallest chunk of positions per workgroup
 constexpr int kMaxChunk = 8192;  // largest
 
-// Per-row workspace of the multi-workgroup top-k.  Only hist must be zero
-// when a call starts; every other word is written before it is read.
+// Per-row workspace of the multi-workgroup top-k.  Only hist and h2 must be
+// zero when a call starts (they are adjacent); every other word is written
+// before it is read.
 struct Ws {
   uint32_t* hist;    // [R][kBins] histogram of the top 12 key bits
+  uint32_t* h2;      // [R][kBins] threshold-bin members by key bits [19:8]
   uint16_t* suf;     // [R][nchunk][kBins] per chunk: elements with digit >= bin
   int2* cand;        // [R][max_len] threshold-bin members (slot, key), in chunk order
   int32_t* list;     // [R][max_len] their slots, compacted (when too many for LDS)
@@ -28,7 +30,8 @@ __host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   Ws w;
   w.nchunk = max_chunks(max_len);
   w.hist = static_cast<uint32_t*>(ws);
-  w.suf = reinterpret_cast<uint16_t*>(w.hist + (size_t)R * kBins);
+  w.h2 = w.hist + (size_t)R * kBins;
+  w.suf = reinterpret_cast<uint16_t*>(w.h2 + (size_t)R * kBins);
   w.cand = reinterpret_cast<int2*>(w.suf + (size_t)R * w.nchunk * kBins);
   w.list = reinterpret_cast<int32_t*>(w.cand + (size_t)R * max_len);
   w.rec = reinterpret_cast<uint32_t*>(w.list + (size_t)R * max_len);

@@ -247,6 +247,25 @@ def test_topk_exact_ties_keep_lowest_positions(L):
         assert set(idx[b][:cnt[b]].tolist()) == set(ref.tolist())
 
 
+def test_topk_crowded_threshold_bins():
+    """Rows whose k-th score shares its top 12 key bits with a whole row's
+    worth of others: one row inside one binade eighth (the members span many
+    batches of the second-digit pass), one whose scores differ only in the
+    low 8 bits (the second digit keeps them all, more than fit in LDS), and
+    a narrow normal row."""
+    rng = np.random.default_rng(29)
+    L = 131072
+    a = (2.0 + rng.uniform(0.0, 0.2499, L)).astype(np.float32)
+    bits = np.full(L, 0x40000000, dtype=np.uint32) + rng.integers(0, 256, L).astype(np.uint32)
+    b = bits.view(np.float32)
+    c = (1.4 + 0.3 * rng.standard_normal(L)).astype(np.float32)
+    sc = np.stack([a, b, c, a[::-1].copy()])
+    _, _, st = _topk_case(sc, 2048, [L, L, L, 40000])
+    assert all(x["diff"] == 0 for x in st), st
+    _, _, st = _topk_case(sc, 20000, [L, L, 50000, 20001])
+    assert all(x["diff"] == 0 for x in st), st
+
+
 @pytest.mark.parametrize("L", [64, 40000])
 def test_topk_negative_scores_signed_zero_and_infinities(L):
     sc = np.array([[-3.0, -0.0, 0.0, -np.inf, np.inf, -1e-30, 2.0, -2.0] + [-5.0] * (L - 8)])
