@@ -234,7 +234,12 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention,
  *   q [num_req][64][128] bf16, w [num_req][64] float.
  *   idx [num_req][k], count [num_req] as for lsi_topk.
  *   cand (optional, may be NULL) [num_req][n_cand] receives the stage-1
- *   candidates (-1 padded).  k <= n_cand <= 65536. */
+ *   candidates (-1 padded).  k <= n_cand <= 65536.
+ * ikeys8->data and ->scale may be pinned host memory (hipHostMalloc) instead
+ * of device memory (LeanSparse: only the compact keys need to stay in GPU
+ * memory, the short list of originals is fetched from the host): stage 2
+ * then reads the candidates' rows across the host bus.  Pageable host
+ * memory returns LSI_ERR_INVALID_ARG. */
 size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len,
                                      int32_t n_cand, int32_t k);
 int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4,

@@ -259,6 +259,28 @@ struct PrefillEvents {
 std::mutex g_ev_mu;
 PrefillEvents g_ev[64];
 
+// A pointer kernels may read: device memory as it is, pinned host memory
+// through the device address of its mapping (the same allocation seen from
+// the GPU; reads cross the host bus).  Pageable host memory is rejected.
+int32_t device_view(const void* p, const void** out, const char* what) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // the failed query must not read as a launch error later
+    return fail(LSI_ERR_INVALID_ARG, std::string(what) + " is neither device memory nor pinned host memory");
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = p;
+    return LSI_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer != nullptr) {
+    // the offset of p inside the allocation carries over to its device address
+    const ptrdiff_t off = at.hostPointer ? static_cast<const char*>(p) - static_cast<const char*>(at.hostPointer) : 0;
+    *out = static_cast<const char*>(at.devicePointer) + off;
+    return LSI_OK;
+  }
+  return fail(LSI_ERR_INVALID_ARG, std::string(what) + " is neither device memory nor pinned host memory");
+}
+
 // ---- pieces shared by the single- and multi-layer decode steps ---------------
 // scan of every cached token (which also clears the top-k counters that the
 // selection uses next), then the top-k that also returns the physical rows
@@ -580,6 +602,13 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   LSI_REQUIRE(idx != nullptr && count != nullptr, "idx and count must be non-NULL");
   LSI_TRY(check_ws(workspace, ws_bytes,
                    lsi_two_stage_workspace_bytes(batch->num_req, batch->max_seq_len, n_cand, k)));
+  // the original keys may live in pinned host memory: the rescoring reads
+  // only the candidates' rows, over the host bus
+  lsi_paged_cache k8 = *ikeys8;
+  LSI_TRY(device_view(ikeys8->data, &k8.data, "ikeys8->data"));
+  const void* sc8 = nullptr;
+  LSI_TRY(device_view(ikeys8->scale, &sc8, "ikeys8->scale"));
+  k8.scale = static_cast<const float*>(sc8);
   const int B = batch->num_req;
   char* ws = static_cast<char*>(workspace);
   float* s4 = reinterpret_cast<float*>(ws);
@@ -612,7 +641,7 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   LSI_LAUNCH(launch_topk(ta, 1, stream), "lsi_two_stage_topk (first top-k)");
 
   // stage 2: exact fp8 scores of the candidates only, keep k
-  ScanArgs a8 = scan_args(ikeys8, batch, q, n_heads, dim, w, s8, n_cand);
+  ScanArgs a8 = scan_args(&k8, batch, q, n_heads, dim, w, s8, n_cand);
   a8.positions = cl;
   a8.n_pos = n_cand;
   a8.zero_ptr = static_cast<uint32_t*>(t2);

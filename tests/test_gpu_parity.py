@@ -282,6 +282,65 @@ def test_topk_small_k_and_large_k(reps):
 
 
 # ----------------------------------------------------------------------------
+# Two-stage compact-key search
+# ----------------------------------------------------------------------------
+
+def _two_stage_case(host, lens, n_cand, k, seed):
+    wl = synth.scaled(synth.TWO_STAGE_512K, seq_lens=tuple(lens), num_req=len(lens),
+                      n_planted=64, seed=seed)
+    di = synth.make_decode_inputs(wl, device=DEV, with_int4=True, with_attn=False)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    if host:   # the originals in pinned host memory, read across the bus
+        ik8 = lsi.Cache(di.ikeys.cpu().pin_memory(), di.iscale.cpu().pin_memory(), "fp8", 128)
+    else:
+        ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, max(lens))
+    idx, cnt, cand = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, n_cand, k, want_cand=True)
+    torch.cuda.synchronize()
+    return di, idx.cpu().numpy(), cnt.cpu().numpy(), cand.cpu().numpy()
+
+
+@pytest.mark.parametrize("host", [False, True])
+def test_two_stage_ragged_against_oracle(host):
+    """Both stages per request against the oracle: the compact scan's
+    candidates, then the exact rescoring of exactly those; with the original
+    keys on the device or in pinned host memory."""
+    lens, n_cand, k = [30000, 9000, 3000], 4096, 512
+    di, idx, cnt, cand = _two_stage_case(host, lens, n_cand, k, 13)
+    ov = OracleView(di)
+    for b, L in enumerate(lens):
+        nc = min(n_cand, L)
+        K4, s4 = ov.keys4(b)
+        I4 = O.index_scores(ov.q_idx[b], ov.w[b], K4, s4)
+        check_topk(cand[b], nc, I4, n_cand, f"stage 1 req {b}")
+        c_sorted = np.sort(cand[b, :nc])
+        K8, s8 = ov.keys(b)
+        I8 = O.index_scores(ov.q_idx[b], ov.w[b], K8[c_sorted], s8[c_sorted])
+        fin = idx[b, :cnt[b]]
+        assert set(fin.tolist()) <= set(c_sorted.tolist())
+        pos = np.full(k, -1)
+        pos[:len(fin)] = np.searchsorted(c_sorted, fin)
+        check_topk(pos, cnt[b], I8, k, f"stage 2 req {b}")
+
+
+def test_two_stage_host_originals_equal_device_and_pageable_is_rejected():
+    lens = [70000, 20000]
+    _, i_d, c_d, cd_d = _two_stage_case(False, lens, 8192, 2048, 19)
+    _, i_h, c_h, cd_h = _two_stage_case(True, lens, 8192, 2048, 19)
+    assert np.array_equal(c_d, c_h)
+    assert np.array_equal(np.sort(cd_d, axis=1), np.sort(cd_h, axis=1))
+    assert np.array_equal(np.sort(i_d, axis=1), np.sort(i_h, axis=1))
+    di = small_dsa([5000], attn=False)
+    ik4 = lsi.Cache(torch.zeros(di.ikeys.shape[0], 64, 64, dtype=torch.uint8, device=DEV),
+                    torch.ones(di.ikeys.shape[0], 64, device=DEV), "int4", 128)
+    pageable = lsi.Cache(di.ikeys.cpu(), di.iscale.cpu(), "fp8", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, 5000)
+    with pytest.raises(lsi.LsiError) as e:
+        lsi.two_stage_topk(ik4, pageable, req, di.q_idx, di.w, 1024, 256)
+    assert e.value.status == lsi.ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------
 # Sparse attention
 # ----------------------------------------------------------------------------
 
