@@ -664,6 +664,9 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
   uint32_t better2;
   const uint32_t bin2 = (uint32_t)find_threshold<kRefThreads>(hist, need, true, tmp, &better2, true);
   const uint32_t n2 = hist[bin2];
+  // when the second threshold bin's members are all kept (the usual case:
+  // one or two of them) they leave in the pass below with the winners
+  const bool take_eq = n2 <= need - better2;
   const bool in_lds = n2 <= (uint32_t)kLdsCand;
   int32_t* list = ws.list + (size_t)r * a.max_len;
   uint32_t ow = better, oe = 0;
@@ -677,8 +680,8 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
     for (int u = 0; u < kU; ++u) {
       if (base + tid + u * kRefThreads < n) {
         const uint32_t d = ((uint32_t)e[u].y >> 8) & (kBins - 1);
-        win |= (uint32_t)(d > bin2) << u;
-        eq |= (uint32_t)(d == bin2) << u;
+        win |= (uint32_t)(d > bin2 || (take_eq && d == bin2)) << u;
+        eq |= (uint32_t)(!take_eq && d == bin2) << u;
       }
     }
     uint32_t tot;
@@ -712,6 +715,10 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
     }
     ow += tot & 0xFFFF;
     oe += tot >> 16;
+  }
+  if (take_eq) {
+    if (tid == 0) a.count[r] = (int32_t)min(better + better2 + n2, (uint32_t)a.k);
+    return;
   }
   wg_sync(in_lds);
   // the members that share the level-2 digit: key bits [7:0], then position
