@@ -55,10 +55,15 @@ def _check(dis, layers, retention, sched, what):
             assert np.allclose(layers.lse[l][b].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
 
 
-@pytest.mark.parametrize("retention,sched", [(1, "serial"), (1, "mli"), (2, "serial"),
-                                             (2, "mli"), (3, "mli")])
-def test_multilayer_against_oracle(retention, sched):
-    wl = _wl([5000, 2300, 700], 512)
+@pytest.mark.parametrize("retention,sched,lens", [
+    (1, "serial", (5000, 2300, 700)), (1, "mli", (5000, 2300, 700)),
+    (2, "serial", (5000, 2300, 700)), (2, "mli", (5000, 2300, 700)),
+    (3, "mli", (5000, 2300, 700)),
+    (2, "mli", (3000, 400, 0)),          # fewer tokens than k, and an empty request
+    (5, "mli", (4100, 900)),             # one indexer for all five layers
+])
+def test_multilayer_against_oracle(retention, sched, lens):
+    wl = _wl(list(lens), 512)
     dis, layers = _build(wl, 5, retention)
     side = torch.cuda.Stream()
     lsi.multilayer_decode(layers, wl.sm_scale, sched, index_stream=side)
