@@ -1,6 +1,7 @@
 """Benchmark of the DSA-style decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets R] [--no-cpu] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets R] [--no-cpu]
+                    [--no-extra | --extra unplanted,ragged,two_stage,prefill,multilayer]
 
 Workload: one request with 131072 cached tokens (64 indexer heads x 128,
 fp8 E4M3FN keys with per-token scales, bf16 queries; k = 2048; sparse MLA with
@@ -18,8 +19,11 @@ the launch stream, the scan's roofline (algorithmic 136 B per token: 128 key
 bytes, a 4-byte scale and a 4-byte score written, against 8 TB/s), a
 sustained scan of 32 x 128K tokens in one launch, the CPU
 oracle's throughput on a bounded sample of the same step, and (unless
---no-extra) the ragged 64-request decode step, the two-stage compact-key
-search at 512K and the prefill indexer chunk, each against its own roofline.
+--no-extra; --extra picks a subset) the un-planted twin of the step, the
+ragged 64-request decode step, the two-stage compact-key search at 512K
+(original keys on the device and in pinned host memory), the prefill
+indexer chunk, and 61 layers of one 128K request under the serial, MLI and
+IndexCache schedules.
 """
 from __future__ import annotations
 
@@ -39,6 +43,9 @@ BYTES_PER_TOKEN = 132          # 128 fp8 key bytes + 4-byte scale
 SCAN_BYTES_PER_TOKEN = BYTES_PER_TOKEN + 4   # ... and the fp32 score the scan writes
 
 
+EXTRAS = ("unplanted", "ragged", "two_stage", "prefill", "multilayer")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -48,7 +55,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the ragged-batch, two-stage and prefill measurements")
+                   help="skip every workload but the one-request step and the sustained scan")
+    p.add_argument("--extra", default=",".join(EXTRAS),
+                   help="which other workloads to measure (comma-separated subset of "
+                        + ", ".join(EXTRAS) + ")")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 512 MiB device copy (known traffic) for counter scaling")
     return p.parse_args()
@@ -255,7 +265,7 @@ def main():
         del q_idx, w, q_attn, reqs, ik, kv, ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        res["other_workloads"] = other_workloads(lsi, synth, torch, dev)
+        res["other_workloads"] = other_workloads(lsi, synth, torch, dev, tuple(args.extra.split(",")))
 
     if args.calib_copy:
         # a plain elementwise copy of known size (512 MiB read, 512 MiB
@@ -271,7 +281,7 @@ def main():
     print(json.dumps(res))
 
 
-def other_workloads(lsi, synth, torch, dev):
+def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
     """Throughput of the ragged 64-request decode step, the two-stage
     compact-key search at 512K and the prefill indexer chunk, each against
     its own roofline (HBM bytes, or bf16 MFMA flops for the prefill)."""
@@ -296,137 +306,142 @@ def other_workloads(lsi, synth, torch, dev):
         del g
         return e0.elapsed_time(e1) / (reps * n)
 
-    # the un-planted twin of the one-request step: no planted tokens, so the
-    # scores are one continuous distribution and the k-th score falls in a
-    # crowded histogram bin (thousands of candidates to refine); 8 rotating
-    # input sets (1.3 GB, more than the last-level cache)
-    nset, L1 = 8, 131072
-    wl = synth.scaled(synth.DSA_128K, seq_lens=(L1,) * nset, num_req=nset)
-    di = synth.make_decode_inputs(wl, device=dev, planted=False)
-    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
-    kv = lsi.Cache(di.kv, None, "bf16", 576)
-    reqs = [lsi.Requests(di.seq_lens[r:r + 1], di.page_table[r:r + 1], L1) for r in range(nset)]
-    views = [(di.q_idx[r:r + 1], di.w[r:r + 1], di.q_attn[r:r + 1]) for r in range(nset)]
-    k, H, dv = 2048, 128, 512
-    idx = torch.empty(1, k, dtype=torch.int32, device=dev)
-    cnt = torch.empty(1, dtype=torch.int32, device=dev)
-    o = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(1, H, dtype=torch.float32, device=dev)
-    ws = torch.empty(lsi.decode_step_workspace_bytes(1, L1, k, H, dv), dtype=torch.uint8,
-                     device=dev)
+    if "unplanted" in extra:
+        # the un-planted twin of the one-request step: no planted tokens, so the
+        # scores are one continuous distribution and the k-th score falls in a
+        # crowded histogram bin (thousands of candidates to refine); 8 rotating
+        # input sets (1.3 GB, more than the last-level cache)
+        nset, L1 = 8, 131072
+        wl = synth.scaled(synth.DSA_128K, seq_lens=(L1,) * nset, num_req=nset)
+        di = synth.make_decode_inputs(wl, device=dev, planted=False)
+        ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+        kv = lsi.Cache(di.kv, None, "bf16", 576)
+        reqs = [lsi.Requests(di.seq_lens[r:r + 1], di.page_table[r:r + 1], L1) for r in range(nset)]
+        views = [(di.q_idx[r:r + 1], di.w[r:r + 1], di.q_attn[r:r + 1]) for r in range(nset)]
+        k, H, dv = 2048, 128, 512
+        idx = torch.empty(1, k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(1, dtype=torch.int32, device=dev)
+        o = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(1, H, dtype=torch.float32, device=dev)
+        ws = torch.empty(lsi.decode_step_workspace_bytes(1, L1, k, H, dv), dtype=torch.uint8,
+                         device=dev)
 
-    def unplanted_steps():
-        for r in range(nset):
-            qi, wr, qa = views[r]
-            lsi.decode_step(ik, kv, None, reqs[r], qi, wr, qa, k, wl.sm_scale, dv, out=o,
-                            lse=lse, idx=idx, count=cnt, ws=ws)
+        def unplanted_steps():
+            for r in range(nset):
+                qi, wr, qa = views[r]
+                lsi.decode_step(ik, kv, None, reqs[r], qi, wr, qa, k, wl.sm_scale, dv, out=o,
+                                lse=lse, idx=idx, count=cnt, ws=ws)
 
-    t = graph_ms(unplanted_steps, n=1, reps=10) / nset
-    out["decode_step_unplanted_l131072"] = {
-        "us_per_step": t * 1e3, "tokens_per_s": L1 / (t * 1e-3), "steps_per_s": 1e3 / t,
-        "sets": nset}
-    del di, ik, kv, reqs, views, idx, cnt, o, lse, ws
-    torch.cuda.empty_cache()
+        t = graph_ms(unplanted_steps, n=1, reps=10) / nset
+        out["decode_step_unplanted_l131072"] = {
+            "us_per_step": t * 1e3, "tokens_per_s": L1 / (t * 1e-3), "steps_per_s": 1e3 / t,
+            "sets": nset}
+        del di, ik, kv, reqs, views, idx, cnt, o, lse, ws
+        torch.cuda.empty_cache()
 
-    # ragged batch: 64 requests, L ~ U{10000..195000}
-    wl = synth.BATCH_RAGGED
-    di = synth.make_decode_inputs(wl, device=dev)
-    seq = di.seq_lens
-    maxL = int(seq.max().item())
-    ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
-    kv = lsi.Cache(di.kv, None, "bf16", 576)
-    req = lsi.Requests(seq, di.page_table, maxL)
-    B, k, H, dv = seq.numel(), 2048, 128, 512
-    idx = torch.empty(B, k, dtype=torch.int32, device=dev)
-    cnt = torch.empty(B, dtype=torch.int32, device=dev)
-    o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    ws = torch.empty(lsi.decode_step_workspace_bytes(B, maxL, k, H, dv), dtype=torch.uint8,
-                     device=dev)
-    t = graph_ms(lambda: lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k,
-                                         wl.sm_scale, dv, out=o, lse=lse, idx=idx, count=cnt,
-                                         ws=ws), n=2, reps=5)
-    tokens = int(seq.sum().item())
-    byts = tokens * BYTES_PER_TOKEN + B * (k * 576 * 2 + H * 576 * 2 + H * dv * 2)
-    out["ragged_decode_b64"] = {
-        "requests": B, "tokens": tokens, "us_per_step": t * 1e3,
-        "tokens_per_s": tokens / (t * 1e-3), "steps_per_s": 1e3 / t,
-        "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
-                     "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
-    del di, ik, kv, req, idx, cnt, o, lse, ws
-    torch.cuda.empty_cache()
+    if "ragged" in extra:
+        # ragged batch: 64 requests, L ~ U{10000..195000}
+        wl = synth.BATCH_RAGGED
+        di = synth.make_decode_inputs(wl, device=dev)
+        seq = di.seq_lens
+        maxL = int(seq.max().item())
+        ik = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+        kv = lsi.Cache(di.kv, None, "bf16", 576)
+        req = lsi.Requests(seq, di.page_table, maxL)
+        B, k, H, dv = seq.numel(), 2048, 128, 512
+        idx = torch.empty(B, k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, dtype=torch.int32, device=dev)
+        o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+        ws = torch.empty(lsi.decode_step_workspace_bytes(B, maxL, k, H, dv), dtype=torch.uint8,
+                         device=dev)
+        t = graph_ms(lambda: lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k,
+                                             wl.sm_scale, dv, out=o, lse=lse, idx=idx, count=cnt,
+                                             ws=ws), n=2, reps=5)
+        tokens = int(seq.sum().item())
+        byts = tokens * BYTES_PER_TOKEN + B * (k * 576 * 2 + H * 576 * 2 + H * dv * 2)
+        out["ragged_decode_b64"] = {
+            "requests": B, "tokens": tokens, "us_per_step": t * 1e3,
+            "tokens_per_s": tokens / (t * 1e-3), "steps_per_s": 1e3 / t,
+            "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
+                         "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        del di, ik, kv, req, idx, cnt, o, lse, ws
+        torch.cuda.empty_cache()
 
-    # two-stage compact-key search at 524288 tokens: int4 scan, 8192
-    # candidates, exact fp8 rescoring, 2048 kept
-    wl = synth.TWO_STAGE_512K
-    di = synth.make_decode_inputs(wl, device=dev, with_int4=True, with_attn=False)
-    L = 524288
-    ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
-    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
-    req = lsi.Requests(di.seq_lens, di.page_table, L)
-    t = graph_ms(lambda: lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048), n=4)
-    byts = L * 68 + 8192 * BYTES_PER_TOKEN
-    out["two_stage_l524288"] = {
-        "tokens": L, "us_per_call": t * 1e3, "tokens_per_s": L / (t * 1e-3),
-        "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
-                     "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
-    # the same search with the original fp8 keys in pinned host memory: only
-    # the compact keys (68 B/token) occupy GPU memory; the rescoring reads the
-    # 8192 candidates' rows across the host bus
-    ik8h = lsi.Cache(di.ikeys.cpu().pin_memory(), di.iscale.cpu().pin_memory(), "fp8", 128)
-    th = graph_ms(lambda: lsi.two_stage_topk(ik4, ik8h, req, di.q_idx, di.w, 8192, 2048), n=4)
-    out["two_stage_l524288"]["host_originals"] = {
-        "us_per_call": th * 1e3, "tokens_per_s": L / (th * 1e-3),
-        "gpu_bytes_per_token": 68, "gpu_bytes_per_token_device_originals": 68 + 132,
-        "bus_bytes_per_call": 8192 * 132}
-    del di, ik8, ik4, ik8h, req
-    torch.cuda.empty_cache()
+    if "two_stage" in extra:
+        # two-stage compact-key search at 524288 tokens: int4 scan, 8192
+        # candidates, exact fp8 rescoring, 2048 kept
+        wl = synth.TWO_STAGE_512K
+        di = synth.make_decode_inputs(wl, device=dev, with_int4=True, with_attn=False)
+        L = 524288
+        ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+        ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+        req = lsi.Requests(di.seq_lens, di.page_table, L)
+        t = graph_ms(lambda: lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048), n=4)
+        byts = L * 68 + 8192 * BYTES_PER_TOKEN
+        out["two_stage_l524288"] = {
+            "tokens": L, "us_per_call": t * 1e3, "tokens_per_s": L / (t * 1e-3),
+            "roofline": {"bound": "hbm", "algorithmic_bytes": byts,
+                         "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        # the same search with the original fp8 keys in pinned host memory: only
+        # the compact keys (68 B/token) occupy GPU memory; the rescoring reads the
+        # 8192 candidates' rows across the host bus
+        ik8h = lsi.Cache(di.ikeys.cpu().pin_memory(), di.iscale.cpu().pin_memory(), "fp8", 128)
+        th = graph_ms(lambda: lsi.two_stage_topk(ik4, ik8h, req, di.q_idx, di.w, 8192, 2048), n=4)
+        out["two_stage_l524288"]["host_originals"] = {
+            "us_per_call": th * 1e3, "tokens_per_s": L / (th * 1e-3),
+            "gpu_bytes_per_token": 68, "gpu_bytes_per_token_device_originals": 68 + 132,
+            "bus_bytes_per_call": 8192 * 132}
+        del di, ik8, ik4, ik8h, req
+        torch.cuda.empty_cache()
 
-    # prefill chunk: 4096 queries over 65536 history + the chunk, causal
-    wl = synth.PREFILL_CHUNK
-    pi = synth.make_prefill_inputs(wl, device=dev)
-    Hh = pi.hist_len
-    hist_k_host = pi.keys[:Hh].cpu().pin_memory()
-    hist_s_host = pi.scale[:Hh].cpu().pin_memory()
-    hist_k_dev = pi.keys[:Hh].contiguous()
-    hist_s_dev = pi.scale[:Hh].contiguous()
-    chunk_k = pi.keys[Hh:].contiguous()
-    chunk_s = pi.scale[Hh:].contiguous()
-    copy_stream = torch.cuda.Stream()
-    T = pi.T
-    pairs = T * Hh + T * (T + 1) // 2
-    flops = pairs * 64 * 128 * 2
+    if "prefill" in extra:
+        # prefill chunk: 4096 queries over 65536 history + the chunk, causal
+        wl = synth.PREFILL_CHUNK
+        pi = synth.make_prefill_inputs(wl, device=dev)
+        Hh = pi.hist_len
+        hist_k_host = pi.keys[:Hh].cpu().pin_memory()
+        hist_s_host = pi.scale[:Hh].cpu().pin_memory()
+        hist_k_dev = pi.keys[:Hh].contiguous()
+        hist_s_dev = pi.scale[:Hh].contiguous()
+        chunk_k = pi.keys[Hh:].contiguous()
+        chunk_s = pi.scale[Hh:].contiguous()
+        copy_stream = torch.cuda.Stream()
+        T = pi.T
+        pairs = T * Hh + T * (T + 1) // 2
+        flops = pairs * 64 * 128 * 2
 
-    def prefill_ms(hk, hs, reps=5):
-        lsi.prefill_index_topk(hk, hs, chunk_k, chunk_s, pi.q, pi.w, 2048, 8192,
-                               copy_stream=copy_stream)
-        torch.cuda.synchronize()
-        st = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(reps):
+        def prefill_ms(hk, hs, reps=5):
             lsi.prefill_index_topk(hk, hs, chunk_k, chunk_s, pi.q, pi.w, 2048, 8192,
                                    copy_stream=copy_stream)
-        e1.record(st)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / reps
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                lsi.prefill_index_topk(hk, hs, chunk_k, chunk_s, pi.q, pi.w, 2048, 8192,
+                                       copy_stream=copy_stream)
+            e1.record(st)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / reps
 
-    t_host = prefill_ms(hist_k_host, hist_s_host)
-    t_dev = prefill_ms(hist_k_dev, hist_s_dev)
-    out["prefill_t4096_h65536"] = {
-        "queries": T, "pairs": pairs, "ms_history_from_pinned_host": t_host,
-        "ms_history_on_device": t_dev,
-        "roofline": {"bound": "mfma", "useful_flops": flops, "dtype": "bf16",
-                     "achieved_TFLOP_s": flops / (t_dev * 1e-3) / 1e12, "peak": 2500.0,
-                     "frac": flops / (t_dev * 1e-3) / 1e12 / 2500.0,
-                     "note": "indexer scores of every (query, visible token) pair plus the "
-                             "per-query top-k, history on the device; the pinned-host "
-                             "figure includes the block copies over PCIe"}}
-    del pi, hist_k_host, hist_s_host, hist_k_dev, hist_s_dev, chunk_k, chunk_s
-    torch.cuda.empty_cache()
-    out["multilayer_l131072_x61"] = multilayer(lsi, synth, torch, dev, graph_ms)
+        t_host = prefill_ms(hist_k_host, hist_s_host)
+        t_dev = prefill_ms(hist_k_dev, hist_s_dev)
+        out["prefill_t4096_h65536"] = {
+            "queries": T, "pairs": pairs, "ms_history_from_pinned_host": t_host,
+            "ms_history_on_device": t_dev,
+            "roofline": {"bound": "mfma", "useful_flops": flops, "dtype": "bf16",
+                         "achieved_TFLOP_s": flops / (t_dev * 1e-3) / 1e12, "peak": 2500.0,
+                         "frac": flops / (t_dev * 1e-3) / 1e12 / 2500.0,
+                         "note": "indexer scores of every (query, visible token) pair plus the "
+                                 "per-query top-k, history on the device; the pinned-host "
+                                 "figure includes the block copies over PCIe"}}
+        del pi, hist_k_host, hist_s_host, hist_k_dev, hist_s_dev, chunk_k, chunk_s
+        torch.cuda.empty_cache()
+    if "multilayer" in extra:
+        out["multilayer_l131072_x61"] = multilayer(lsi, synth, torch, dev, graph_ms)
     return out
 
 
