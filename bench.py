@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--extra", default=",".join(EXTRAS),
                    help="which other workloads to measure (comma-separated subset of "
                         + ", ".join(EXTRAS) + ")")
+    p.add_argument("--only-extra", action="store_true",
+                   help="measure only the --extra workloads and print them (no step line; "
+                        "for kernel traces of one workload group)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 512 MiB device copy (known traffic) for counter scaling")
     return p.parse_args()
@@ -89,6 +92,10 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
+    if args.only_extra:
+        print(json.dumps({"other_workloads": other_workloads(lsi, synth, torch, dev,
+                                                             tuple(args.extra.split(",")))}))
+        return
     R = args.sets
     L = 131072
     wl = synth.scaled(synth.DSA_128K, seq_lens=tuple([L] * R), num_req=R)
