@@ -625,8 +625,20 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
   __shared__ float stat[2];
   const int64_t bh = blockIdx.x;
   const float* pl = part_lse + bh * nsplit;
+  const int d0 = threadIdx.x * 4;
+  // The first kFirst partials are loaded together with the log-sum-exps
+  // (they do not depend on the weights): one round trip instead of one per
+  // group of loads.  Indexes past nsplit read the last partial again and get
+  // weight 0.
+  constexpr int kFirst = 32;
+  const float ls_raw = (int)threadIdx.x < nsplit ? pl[threadIdx.x & (kMaxSplit - 1)] : -INFINITY;
+  f32x4 v[kFirst];
+#pragma unroll
+  for (int s = 0; s < kFirst; ++s)
+    v[s] = *reinterpret_cast<const f32x4*>(part_o + (bh * nsplit + min(s, nsplit - 1)) * kDV + d0);
+  __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x < 64) {
-    const float ls = (int)threadIdx.x < nsplit ? pl[threadIdx.x] : -INFINITY;
+    const float ls = ls_raw;
     float M = ls;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.f : exp2f(ls - M);
@@ -641,11 +653,12 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
   __syncthreads();
   const float M = stat[0];
   const float wsum = stat[1];
-  const int d0 = threadIdx.x * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (bh * nsplit + s) * kDV + d0);
-    acc += wts[s] * v;
+#pragma unroll
+  for (int s = 0; s < kFirst; ++s) acc += wts[s] * v[s];
+  for (int s = kFirst; s < nsplit; ++s) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (bh * nsplit + s) * kDV + d0);
+    acc += wts[s] * x;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV;
