@@ -220,6 +220,31 @@ def main():
     torch.cuda.synchronize()
     t_sus_graph = event_loop(lambda i: g_sus.replay(), 3, torch.cuda.current_stream()) / n_sus
     sus_gbs = R * L * SCAN_BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
+    del g_sus
+
+    # spread of the step time: the same graph of R steps replayed 10 more
+    # times (after the timed region), each replay between HIP events
+    per_replay = sorted(event_loop(lambda i: g_all.replay(), 1, stream) / R for _ in range(10))
+    pct = lambda q: per_replay[min(len(per_replay) - 1, int(round(q * (len(per_replay) - 1))))]
+
+    # achievable-bandwidth reference on the same device: plain streams over
+    # 1 GiB (torch's full sum, a per-row sum that writes 1/4096 of what it
+    # reads, and a copy counted as read + write); the best rate is reported
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(big)
+    rows = big.view(-1, 4096)
+    refs = {"sum": (lambda i: big.sum(), 1 << 30),
+            "row_sum": (lambda i: rows.sum(1), (1 << 30) + (1 << 18)),
+            "copy": (lambda i: dst.copy_(big), 2 << 30)}
+    ref_gbs = {}
+    for name, (fn, nbytes) in refs.items():
+        fn(0)
+        torch.cuda.synchronize()
+        ref_gbs[name] = nbytes / (event_loop(fn, 10, stream) * 1e-3) / 1e9
+    read_gbs = max(ref_gbs.values())
+    del big, dst, rows
+    torch.cuda.empty_cache()
+    traffic = measured_traffic()
 
     step_bytes = L * BYTES_PER_TOKEN + k * 576 * 2 + H * 576 * 2 + H * dv * 2
     res = {
@@ -241,10 +266,14 @@ def main():
         "decode_steps_per_s": 1e3 / ms_step,
         "timing": "HIP graph replay (one step per input set); eager per-call figure below",
         "eager_ms_per_step": eager_ms,
+        "step_us_p10_p50_p90": [pct(0.1) * 1e3, pct(0.5) * 1e3, pct(0.9) * 1e3],
         "phases_us": {"scan": t_scan * 1e3, "topk": t_topk * 1e3, "mla": t_mla * 1e3},
+        "scan_tokens_per_s": L / (t_scan * 1e-3),
         "roofline": {"kernel": "scan_dma_kernel<0, 2> (fp8 keys)", "bound": "hbm", "achieved": scan_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(),
+                     "traffic": traffic,
+                     "traffic_GB_s": None if traffic is None else traffic / (t_scan * 1e-3) / 1e9,
+                     "overfetch": None if traffic is None else traffic / (L * SCAN_BYTES_PER_TOKEN),
                      "note": "131072 tokens x 136 B per launch / average launch time "
                              "(HIP events around graph replays of the scan)"},
         "scan_sustained": {"tokens": R * L, "us": t_sus * 1e3,
@@ -254,7 +283,13 @@ def main():
                            "timing": "HIP events around 20 back-to-back launches on one stream; "
                                      "median of 5 such windows",
                            "us_windows_min_max": [sus_windows[0] * 1e3, sus_windows[-1] * 1e3],
-                           "us_graph_replay": t_sus_graph * 1e3},
+                           "us_graph_replay": t_sus_graph * 1e3,
+                           "stream_reference_GB_s": read_gbs,
+                           "frac_of_stream_reference": sus_gbs / read_gbs,
+                           "stream_reference": {"GB_s": ref_gbs,
+                                                "how": "HIP events around 10 launches each over "
+                                                       "1 GiB of float32: torch sum, per-row sum, "
+                                                       "copy (read + write)"}},
         # the whole step against its algorithmic HBM time: the scan's keys and
         # scales, the gathered latent rows, the query and the output
         "step_roofline": {"algorithmic_bytes": step_bytes,
@@ -268,7 +303,7 @@ def main():
     if not args.no_extra:
         # the other workloads of the pages' configurations, measured on the
         # same device after the 128K sets are released
-        del g_all, g_rem, g_scan, g_topk, g_mla, g_sus, di, scores, scores_all, sc_rows, idx_sel
+        del g_all, g_rem, g_scan, g_topk, g_mla, di, scores, scores_all, sc_rows, idx_sel
         del q_idx, w, q_attn, reqs, ik, kv, ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
