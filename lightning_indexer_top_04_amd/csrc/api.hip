@@ -675,7 +675,8 @@ size_t lsi_prefill_workspace_bytes(int32_t hist_len, int32_t T, int32_t dim, int
   const size_t bufk = align_up((size_t)block_tokens * dim, kWsAlign);
   const size_t bufs = align_up((size_t)block_tokens * 4, kWsAlign);
   const size_t sc = scores_external ? 0 : align_up((size_t)T * ld * 4, kWsAlign);
-  return 2 * (bufk + bufs) + sc + topk_ws_bytes(T, (int)ld);
+  const size_t rg = align_up((size_t)T * 8, kWsAlign);
+  return 2 * (bufk + bufs) + sc + rg + topk_ws_bytes(T, (int)ld);
 }
 
 int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale, int32_t hist_len,
@@ -714,6 +715,8 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
     sc = reinterpret_cast<float*>(ws);
     ws += align_up((size_t)T * ld * 4, kWsAlign);
   }
+  uint32_t* range = reinterpret_cast<uint32_t*>(ws);   // [T][2] key range of each row
+  ws += align_up((size_t)T * 8, kWsAlign);
   void* tws = ws;
 
   int dev = 0;
@@ -738,6 +741,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
       return fail(LSI_ERR_HIP, std::string("lsi_prefill_index_topk: ") + hipGetErrorString(_e)); \
   } while (0)
 
+  LSI_HIP(launch_zero(range, 2 * (int64_t)T, s_compute));
   // the copy stream must not overwrite buffers a previous call still reads
   LSI_HIP(hipEventRecord(ev.start, s_compute));
   LSI_HIP(hipStreamWaitEvent(s_copy, ev.start, 0));
@@ -748,6 +752,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   pa.hist_len = hist_len;
   pa.scores = sc;
   pa.ld = ld;
+  pa.range = range;
   const int nblk = (int)ceil_div(hist_len, block_tokens);
   for (int blk = 0; blk < nblk; ++blk) {
     const int j = blk & 1;
@@ -775,6 +780,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   t.scores = sc;
   t.ld = ld;
   t.causal_base = hist_len;
+  t.range = range;
   t.num_req = T;
   t.max_len = (int)ld;
   t.k = k;

@@ -44,6 +44,7 @@ struct TopkArgs {
   const int32_t* seq_lens = nullptr;  // per-row length (clamped to max_len)
   int lens_const = -1;             // if >= 0: every row has this length
   int causal_base = -1;            // if >= 0: row r has length causal_base+r+1
+  const uint32_t* range = nullptr; // optional [R][2]: ~(min key), max key of row r
   int num_req = 0;
   int max_len = 0;
   int k = 0;
@@ -106,6 +107,9 @@ struct PrefillScanArgs {
   int hist_len = 0;                // query i sits at hist_len + i
   float* scores = nullptr;         // [T][ld]
   int64_t ld = 0;
+  // optional [T][2]: per query row, atomic maxima of ~key and key over the
+  // scores written (zero before the first block), i.e. the row's key range
+  uint32_t* range = nullptr;
 };
 hipError_t launch_prefill_scan(const PrefillScanArgs& a, hipStream_t s);
 

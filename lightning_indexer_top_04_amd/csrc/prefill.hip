@@ -89,6 +89,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanAr
   stage(0, raw, sc);
   if (ntile > 1) fetch(1, raw, sc);
   __syncthreads();
+  // key range of the scores this wave writes (the row top-k's first digit
+  // spans it; recording it here spares that kernel a pass over the row)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 
   for (int tile = 0; tile < ntile; ++tile) {
     const int cur = tile & 1;
@@ -121,11 +124,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanAr
         const float total = half_swap_sum(part);
         const int local = tile * kTile + 32 * half + m;
         const int pos = a.tok0 + local;
-        if (h == 0 && local < a.n_tok && pos <= my_last)
-          a.scores[(int64_t)qi * a.ld + pos] = total * ksc[cur][32 * half + m];
+        if (h == 0 && local < a.n_tok && pos <= my_last) {
+          const float v = total * ksc[cur][32 * half + m];
+          a.scores[(int64_t)qi * a.ld + pos] = v;
+          const uint32_t key = float_key(v);
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
       }
     }
     __syncthreads();
+  }
+  if (a.range && active) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if (lane == 0 && kmax >= kmin) {
+      atomicMax(&a.range[2 * (int64_t)qi], ~kmin);
+      atomicMax(&a.range[2 * (int64_t)qi + 1], kmax);
+    }
   }
 }
 

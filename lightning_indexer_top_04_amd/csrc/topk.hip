@@ -807,13 +807,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     }
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for_batches([&](int, const uint32_t (&kk)[kBatch]) {
+  if (a.range) {
+    // the producer recorded the row's key range (the same keys)
+    kmin = ~a.range[2 * (int64_t)r];
+    kmax = a.range[2 * (int64_t)r + 1];
+  } else {
+    for_batches([&](int, const uint32_t (&kk)[kBatch]) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      kmin = min(kmin, kk[j]);
-      kmax = max(kmax, kk[j]);
-    }
-  });
+      for (int j = 0; j < kBatch; ++j) {
+        kmin = min(kmin, kk[j]);
+        kmax = max(kmax, kk[j]);
+      }
+    });
+  }
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
