@@ -173,6 +173,31 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys,
                         int32_t* count, void* out, float* lse,
                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- fused decode step without allocation ---------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc.  Computes
+ * exactly what lsi_decode_step computes, with the same arguments except the
+ * workspace: its scratch is a library-owned device array of
+ * LSI_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, allocated with the library's
+ * code on that GPU and held until the process ends.  The call allocates and
+ * frees nothing.  A call that needs more scratch than that
+ * (lsi_decode_step_workspace_bytes() above the limit) returns
+ * LSI_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race and give undefined results;
+ * calls ordered on one stream are safe. */
+#define LSI_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int32_t lsi_decode_step_noalloc(const lsi_paged_cache* ikeys,
+                                const lsi_paged_cache* kv,
+                                const lsi_paged_cache* v,
+                                const lsi_batch* batch, const void* q_idx,
+                                int32_t n_idx_heads, int32_t idx_dim,
+                                const float* w, const void* q_attn,
+                                int32_t n_heads, int32_t dk, int32_t dv,
+                                float sm_scale, int32_t k, int32_t* idx,
+                                int32_t* count, void* out, float* lse,
+                                hipStream_t stream);
+
 /* ---- several layers of one decode step ------------------------------------
  * MLI abstract: neighbouring layers select nearly the same tokens, so a layer
  * may attend the selection of the previous indexer layer instead of its own;

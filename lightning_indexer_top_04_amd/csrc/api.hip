@@ -416,22 +416,35 @@ size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len, int
   return sc + tk + ph + at;
 }
 
-int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
-                        const lsi_paged_cache* v, const lsi_batch* batch, const void* q_idx,
-                        int32_t n_idx_heads, int32_t idx_dim, const float* w, const void* q_attn,
-                        int32_t n_heads, int32_t dk, int32_t dv, float sm_scale, int32_t k,
-                        int32_t* idx, int32_t* count, void* out, float* lse, void* workspace,
-                        size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace lsi {
+namespace {
+
+int32_t validate_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                             const lsi_paged_cache* v, const lsi_batch* batch, const void* q_idx,
+                             int32_t n_idx_heads, int32_t idx_dim, const float* w,
+                             const void* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
+                             float sm_scale, int32_t k, const int32_t* idx, const int32_t* count,
+                             const void* out, const float* lse) {
   LSI_TRY(check_batch(batch, true));
-  const int64_t ld = scores_ld(batch->max_seq_len);
   LSI_TRY(validate_index(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, nullptr, 0, true));
   LSI_REQUIRE(ikeys->page_size == kv->page_size, "ikeys and kv must share the page size");
   LSI_REQUIRE(k >= 1 && k <= 65536, "k must be in [1, 65536]");
   LSI_REQUIRE(idx != nullptr && count != nullptr, "idx and count must be non-NULL");
   LSI_TRY(validate_attn(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse));
-  const size_t need = lsi_decode_step_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
-  LSI_TRY(check_ws(workspace, ws_bytes, need));
+  return LSI_OK;
+}
 
+// The launches of one decode step over a validated call and a workspace of
+// at least lsi_decode_step_workspace_bytes().
+int32_t enqueue_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                            const lsi_paged_cache* v, const lsi_batch* batch, const void* q_idx,
+                            int32_t n_idx_heads, int32_t idx_dim, const float* w,
+                            const void* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
+                            float sm_scale, int32_t k, int32_t* idx, int32_t* count, void* out,
+                            float* lse, void* workspace, hipStream_t stream, const char* what) {
+  const int64_t ld = scores_ld(batch->max_seq_len);
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
@@ -442,10 +455,76 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   void* attn_wsp = ws;
 
   LSI_TRY(enqueue_select(ikeys, kv, batch, q_idx, n_idx_heads, idx_dim, w, k, idx, count, scores,
-                         ld, topk_ws, phys, stream, "lsi_decode_step"));
+                         ld, topk_ws, phys, stream, what));
   LSI_TRY(enqueue_attend(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse,
-                         attn_wsp, phys, stream, "lsi_decode_step"));
-  return check_launch("lsi_decode_step");
+                         attn_wsp, phys, stream, what));
+  return check_launch(what);
+}
+
+// Library-owned scratch of lsi_decode_step_noalloc: one copy of this array
+// per GPU, which holds it until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+constexpr size_t kNoAllocScratch = LSI_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+int32_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(LSI_ERR_HIP, "lsi_decode_step_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LSI_ERR_HIP, std::string("lsi_decode_step_noalloc: scratch address: ") + hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LSI_OK;
+}
+
+}  // namespace
+}  // namespace lsi
+
+extern "C" {
+
+int32_t lsi_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                        const lsi_paged_cache* v, const lsi_batch* batch, const void* q_idx,
+                        int32_t n_idx_heads, int32_t idx_dim, const float* w, const void* q_attn,
+                        int32_t n_heads, int32_t dk, int32_t dv, float sm_scale, int32_t k,
+                        int32_t* idx, int32_t* count, void* out, float* lse, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  LSI_TRY(validate_decode_step(ikeys, kv, v, batch, q_idx, n_idx_heads, idx_dim, w, q_attn, n_heads,
+                               dk, dv, sm_scale, k, idx, count, out, lse));
+  const size_t need = lsi_decode_step_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
+  LSI_TRY(check_ws(workspace, ws_bytes, need));
+  return enqueue_decode_step(ikeys, kv, v, batch, q_idx, n_idx_heads, idx_dim, w, q_attn, n_heads, dk,
+                             dv, sm_scale, k, idx, count, out, lse, workspace, stream,
+                             "lsi_decode_step");
+}
+
+int32_t lsi_decode_step_noalloc(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
+                                const lsi_paged_cache* v, const lsi_batch* batch,
+                                const void* q_idx, int32_t n_idx_heads, int32_t idx_dim,
+                                const float* w, const void* q_attn, int32_t n_heads, int32_t dk,
+                                int32_t dv, float sm_scale, int32_t k, int32_t* idx,
+                                int32_t* count, void* out, float* lse, hipStream_t stream) {
+  LSI_TRY(validate_decode_step(ikeys, kv, v, batch, q_idx, n_idx_heads, idx_dim, w, q_attn, n_heads,
+                               dk, dv, sm_scale, k, idx, count, out, lse));
+  const size_t need = lsi_decode_step_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
+  if (need > kNoAllocScratch)
+    return fail(LSI_ERR_WORKSPACE, "lsi_decode_step_noalloc: the call needs " + std::to_string(need) +
+                                       " bytes of scratch; the library's fixed scratch holds " +
+                                       std::to_string(kNoAllocScratch));
+  void* ws = nullptr;
+  LSI_TRY(scratch_for_current_device(&ws));
+  return enqueue_decode_step(ikeys, kv, v, batch, q_idx, n_idx_heads, idx_dim, w, q_attn, n_heads, dk,
+                             dv, sm_scale, k, idx, count, out, lse, ws, stream,
+                             "lsi_decode_step_noalloc");
 }
 
 size_t lsi_multilayer_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k,

@@ -25,7 +25,7 @@ DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int4": INT4}
 EXPORTS = [
     "lsi_index_scores", "lsi_topk_workspace_bytes", "lsi_topk",
     "lsi_sparse_mla_workspace_bytes", "lsi_sparse_mla_decode",
-    "lsi_decode_step_workspace_bytes", "lsi_decode_step",
+    "lsi_decode_step_workspace_bytes", "lsi_decode_step", "lsi_decode_step_noalloc",
     "lsi_multilayer_workspace_bytes", "lsi_multilayer_decode",
     "lsi_two_stage_workspace_bytes", "lsi_two_stage_topk",
     "lsi_prefill_workspace_bytes", "lsi_prefill_index_topk",
@@ -69,6 +69,8 @@ _SIGS = {
     "lsi_decode_step_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "lsi_decode_step": (_I, [_PC, _PC, _PC, _PB, _P, _I, _I, _P, _P, _I, _I, _I, _F, _I,
                              _P, _P, _P, _P, _P, _S, _P]),
+    "lsi_decode_step_noalloc": (_I, [_PC, _PC, _PC, _PB, _P, _I, _I, _P, _P, _I, _I, _I, _F, _I,
+                                     _P, _P, _P, _P, _P]),
     "lsi_multilayer_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "lsi_multilayer_decode": (_I, [_I, _I, _I, _PC, _PC, _PB, _PP, _I, _I, _PP, _PP, _I, _I, _I,
                                    _F, _I, _PP, _PP, _PP, _PP, _P, _S, _P, _P]),
@@ -220,6 +222,24 @@ def decode_step(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests, q_idx: 
                                  _ptr(q_idx), HI, dI, _ptr(w), _ptr(q_attn), H, dk, dv, sm_scale,
                                  k, _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _ptr(ws),
                                  ws.numel(), _stream(stream)), "lsi_decode_step")
+    return idx, count, out, lse
+
+
+# scratch of lsi_decode_step_noalloc, per GPU (LSI_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_step_noalloc(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests,
+                        q_idx: torch.Tensor, w: torch.Tensor, q_attn: torch.Tensor, k: int,
+                        sm_scale: float, dv: int, out, lse, idx, count, stream=None):
+    """lsi_decode_step_noalloc: the fused step with the library's own scratch;
+    every output buffer is the caller's (nothing is allocated here either)."""
+    B, HI, dI = q_idx.shape
+    _, H, dk = q_attn.shape
+    _check(lib().lsi_decode_step_noalloc(ikeys.ref, kv.ref, None if v is None else v.ref, req.ref,
+                                         _ptr(q_idx), HI, dI, _ptr(w), _ptr(q_attn), H, dk, dv,
+                                         sm_scale, k, _ptr(idx), _ptr(count), _ptr(out), _ptr(lse),
+                                         _stream(stream)), "lsi_decode_step_noalloc")
     return idx, count, out, lse
 
 

@@ -178,3 +178,21 @@ def test_multilayer_validation(L):
     kv3 = (lsi.PagedCache * n)(*[lsi.PagedCache(lsi.F32, 64, 8, 64, 0x4000, None)
                                  for _ in range(n)])
     assert call(kvs=kv3) == lsi.ERR_UNSUPPORTED
+
+
+def test_decode_step_noalloc_validation(L):
+    """The no-allocation step validates like lsi_decode_step and rejects a
+    call whose scratch exceeds the library's fixed array before anything is
+    enqueued (no GPU is touched here)."""
+    ik, kv = _cache(), lsi.PagedCache(lsi.BF16, 64, 8, 576, 0x4000, None)
+
+    def call(b, H=128, k=2048):
+        return L.lsi_decode_step_noalloc(C.byref(ik), C.byref(kv), None, C.byref(b), 0x5000, 64,
+                                         128, 0x6000, 0x7000, H, 576, 512, 0.04, k, 0x8000, 0x9000,
+                                         0xA000, 0xB000, None)
+    assert call(_batch(), H=72) == lsi.ERR_UNSUPPORTED
+    assert call(_batch(), k=0) == lsi.ERR_INVALID_ARG
+    big = lsi.Batch(64, 4688, 300000, 0, 0x1000, 0x2000)
+    assert L.lsi_decode_step_workspace_bytes(64, 300000, 2048, 128, 512) > lsi.NOALLOC_SCRATCH_BYTES
+    assert call(big) == lsi.ERR_WORKSPACE
+    assert b"scratch" in L.lsi_last_error()
