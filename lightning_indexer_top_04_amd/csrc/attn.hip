@@ -132,7 +132,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
 }
 
-__global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
+__global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
                                                                 int nsplit, int units, float* part_o,
                                                                 float* part_lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t kvs[kKvBytes];
@@ -141,14 +141,24 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
   __shared__ float red_l[4][kMH];
   __shared__ float alpha_s[kMH];
   __shared__ int rows_all[kMaxSplitRows];
+  // the 16 heads' query rows (16 x 1152 bytes), moved in once per workgroup:
+  // chunk j (16 bytes) of head n at position 72 n + ((j & ~7) | ((j ^ n) & 7)),
+  // so that the 16 heads' reads of one chunk spread over the banks
+  __shared__ __attribute__((aligned(1024))) uint8_t qlds[kMH * kD * 2];
 
+  // Block ids map to XCDs round-robin (bid % 8).  Every split of one head
+  // group of one request runs on one XCD, so the combine of that group (placed
+  // on the same XCD) reads their partials from that XCD's L2; the selected
+  // rows, shared by all head groups, are what crosses XCDs instead.
   const int n_hg = a.n_heads / kMH;
   const int bid = blockIdx.x;
-  const int u = (bid / (8 * n_hg)) * 8 + (bid & 7);
-  const int hg = (bid >> 3) % n_hg;
-  if (u >= units) return;
-  const int b = u / nsplit;
-  const int split = u % nsplit;
+  const int jx = bid >> 3;
+  const int inst = 8 * (jx / nsplit) + (bid & 7);     // (request, head group) instance
+  const int split = jx % nsplit;
+  if (inst >= a.num_req * n_hg) return;
+  const int b = inst / n_hg;
+  const int hg = inst % n_hg;
+  (void)units;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,10 +202,12 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
   }
   __syncthreads();
 
-  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32u + 8g .. +7];
-  // loaded once the first block's gather is in flight (an ordinary load
-  // issued before the gather would make it wait for the load)
-  const __bf16* qh = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.n_heads + head) * kD;
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32t + 8g .. +7],
+  // read from qlds after the first block's wait (every wave needs all 16
+  // heads; one DMA of the group's rows per workgroup instead of a load per
+  // wave, which had the workgroups of one XCD queue on the same L2 lines)
+  const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
+                                                       ((int64_t)b * a.n_heads + hg * kMH) * kD);
   bf16x8 qr[kD / 32];
 
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv);
@@ -228,10 +240,22 @@ __global__ __launch_bounds__(kMThreads, 2) void mla_bf16_kernel(AttnArgs a, int 
       }
     }
     if (base == 0) {
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
+      // 18 DMAs of 1 KB fill qlds; wave w issues numbers w, w + 4, ...
+      for (int i = w; i < kMH * kD * 2 / 1024; i += 4) {
+        const int p = 64 * i + lane;                        // 16-byte position in qlds
+        const int hn = p / 72, jj = p - 72 * hn;
+        const int j = (jj & ~7) | ((jj ^ hn) & 7);          // global chunk stored there
+        dma_row16<0>(qlds + 1024 * i, qg + hn * (kD * 2) + 16 * j);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (base == 0) {
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) {
+        const int j = 4 * t + g;
+        qr[t] = *reinterpret_cast<const bf16x8*>(qlds + 16 * (72 * n + ((j & ~7) | ((j ^ n) & 7))));
+      }
+    }
 
     // ---- S^T for rows 16w + (0..15): A = K rows from LDS, B = Q^T
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -623,7 +647,11 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
   constexpr int kMaxSplit = 64;
   __shared__ float wts[kMaxSplit];
   __shared__ float stat[2];
-  const int64_t bh = blockIdx.x;
+  // (request, head) of this block: head group instance bh / 16 sits on XCD
+  // (bh / 16) % 8, the XCD whose workgroups wrote its partials
+  const int jx = blockIdx.x >> 3;
+  const int64_t bh = 16 * (8 * (int64_t)(jx / 16) + (blockIdx.x & 7)) + jx % 16;
+  if (bh >= (int64_t)a.num_req * a.n_heads) return;
   const float* pl = part_lse + bh * nsplit;
   const int d0 = threadIdx.x * 4;
   // The first kFirst partials are loaded together with the log-sum-exps
@@ -754,9 +782,9 @@ MlaPlan plan_mla(int num_req, int n_heads, int k) {
   const bool wide = n_heads % kWH == 0 && num_req >= kWideMinReq;
   const int groups = num_req * (n_heads / (wide ? kWH : kMH));
   const int max_rows = wide ? kWMaxRows : kMaxSplitRows;
-  // about one (wide) or two (narrow) workgroups per CU, at least one block
-  // per split, at most max_rows rows per workgroup
-  int ns = (int)ceil_div((int64_t)num_cus() * (wide ? 1 : 2), std::max(groups, 1));
+  // about one workgroup per CU (both kernels' LDS allows one), at least one
+  // block per split, at most max_rows rows per workgroup
+  int ns = (int)ceil_div((int64_t)num_cus(), std::max(groups, 1));
   ns = std::min(ns, std::max(1, blocks));
   ns = std::max(ns, (int)ceil_div(blocks, max_rows / kMBlk));
   ns = std::min(std::max(ns, 1), 64);
@@ -779,16 +807,24 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
   float* part_o = static_cast<float*>(a.ws);
   float* part_lse = part_o ? part_o + (size_t)a.num_req * a.n_heads * nsplit * kDV : nullptr;
   const int units = a.num_req * nsplit;
-  const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / (p.wide ? kWH : kMH));
-  if (p.wide)
+  if (p.wide) {
+    const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / kWH);
     hipLaunchKernelGGL(mla_bf16_wide_kernel, dim3(grid), dim3(kWThreads), 0, s, a, rows_per_split, nsplit,
                        units, part_o, part_lse);
-  else
+  } else {
+    // 8 XCDs x (head group instances per XCD) x splits
+    const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
+    const int grid = (int)(8 * ceil_div(inst, 8) * nsplit);
     hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, a, rows_per_split, nsplit,
                        units, part_o, part_lse);
-  if (nsplit > 1)
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.num_req * a.n_heads), dim3(kDV / 4), 0, s, a,
-                       nsplit, part_o, part_lse);
+  }
+  if (nsplit > 1) {
+    // one block per (request, head), laid out so that head group instance i
+    // (16 heads) lands on XCD i % 8 like its partials
+    const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(8 * 16 * ceil_div(inst, 8))), dim3(kDV / 4), 0, s,
+                       a, nsplit, part_o, part_lse);
+  }
   return hipGetLastError();
 }
 
