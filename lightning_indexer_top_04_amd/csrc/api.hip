@@ -288,7 +288,7 @@ int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
                        const lsi_batch* batch, const void* q_idx, int32_t n_idx_heads,
                        int32_t idx_dim, const float* w, int32_t k, int32_t* idx, int32_t* count,
                        float* scores, int64_t ld, void* topk_ws, int32_t* phys, hipStream_t stream,
-                       const char* what) {
+                       const char* what, bool defer = false) {
   ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
   sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
   sa.zero_words = topk_zero_words(batch->num_req);
@@ -309,6 +309,7 @@ int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.max_pages = batch->max_pages;
   t.page_size = kv->page_size;
   t.num_pages = kv->num_pages;
+  t.defer = defer ? 1 : 0;
   LSI_LAUNCH(launch_topk(t, 1, stream), std::string(what) + " (top-k)");
   return LSI_OK;
 }
@@ -317,9 +318,13 @@ int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
 int32_t enqueue_attend(const lsi_paged_cache* kv, const lsi_paged_cache* v, const lsi_batch* batch,
                        const void* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
                        const int32_t* idx, int32_t k, float sm_scale, void* out, float* lse,
-                       void* attn_wsp, const int32_t* phys, hipStream_t stream, const char* what) {
+                       void* attn_wsp, const int32_t* phys, hipStream_t stream, const char* what,
+                       void* deferred_topk_ws = nullptr, int32_t* idx_out = nullptr) {
   AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
   a.phys = phys;
+  a.tk_ws = deferred_topk_ws;
+  a.tk_max_len = batch->max_seq_len;
+  a.idx_out = idx_out;
   LSI_LAUNCH(run_attn(kv->dtype, a, stream), std::string(what) + " (attention)");
   return LSI_OK;
 }
@@ -454,10 +459,15 @@ int32_t enqueue_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache*
   ws += align_up((size_t)batch->num_req * k * sizeof(int32_t), kWsAlign);
   void* attn_wsp = ws;
 
+  // The threshold bin of long rows is left to the attention kernel when the
+  // 16-head latent kernel runs (one launch fewer): it resolves the slots it
+  // reads from the top-k workspace and writes their positions to idx.
+  const bool defer = kv->dtype == LSI_BF16 && mla_resolves(batch->num_req, n_heads, k) &&
+                     topk_can_defer(batch->num_req, batch->max_seq_len);
   LSI_TRY(enqueue_select(ikeys, kv, batch, q_idx, n_idx_heads, idx_dim, w, k, idx, count, scores,
-                         ld, topk_ws, phys, stream, what));
+                         ld, topk_ws, phys, stream, what, defer));
   LSI_TRY(enqueue_attend(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse,
-                         attn_wsp, phys, stream, what));
+                         attn_wsp, phys, stream, what, defer ? topk_ws : nullptr, defer ? idx : nullptr));
   return check_launch(what);
 }
 

@@ -22,6 +22,7 @@
 // Splits of the selection are merged with their log-sum-exp by a small
 // combine kernel.
 #include "lsi_internal.hpp"
+#include "topk_common.hpp"
 
 namespace lsi {
 namespace {
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   // chunk j (16 bytes) of head n at position 72 n + ((j & ~7) | ((j ^ n) & 7)),
   // so that the 16 heads' reads of one chunk spread over the banks
   __shared__ __attribute__((aligned(1024))) uint8_t qlds[kMH * kD * 2];
+  __shared__ uint32_t rtmp[32];
 
   // Block ids map to XCDs round-robin (bid % 8).  Every split of one head
   // group of one request runs on one XCD, so the combine of that group (placed
@@ -195,10 +197,29 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
       }
     }
   }
+  bool unresolved = false;
 #pragma unroll
   for (int i = 0; i < kRowsPerThread; ++i) {
     const int e = tid + i * kMThreads;
     if (e < nr) rows_all[e] = (prow[i] < 0 || prow[i] >= n_rows_pool) ? -1 : prow[i];
+    unresolved |= e < nr && prow[i] == kUnresolvedRow;
+  }
+  if (a.tk_ws != nullptr && __syncthreads_or(unresolved)) {
+    // Part of this slice lies in a threshold bin that the top-k left open:
+    // work out the kept members (every workgroup that needs them reaches the
+    // same set and order) and take the rows of this slice's slots.  The
+    // block buffer is free until the gather below.
+    const topk::Ws tw = topk::carve(a.tk_ws, a.num_req, a.tk_max_len);
+    topk::resolve_members<kMThreads>(tw, b, a.tk_max_len, a.k, reinterpret_cast<uint32_t*>(kvs), rtmp, r0, r1,
+                                     [&](int slot, int pos) {
+                                       int row = -1;
+                                       if (pos >= 0 && pos < L) {
+                                         const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+                                         if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
+                                       }
+                                       rows_all[slot - r0] = (row < 0 || row >= n_rows_pool) ? -1 : row;
+                                       if (hg == 0) a.idx_out[(int64_t)b * a.k + slot] = pos;
+                                     });
   }
   __syncthreads();
 
@@ -793,6 +814,8 @@ MlaPlan plan_mla(int num_req, int n_heads, int k) {
 }
 
 }  // namespace
+
+bool mla_resolves(int num_req, int n_heads, int k) { return !plan_mla(num_req, n_heads, k).wide; }
 
 size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k) {
   const MlaPlan p = plan_mla(num_req, n_heads, k);

@@ -60,13 +60,22 @@ struct TopkArgs {
   int max_pages = 0;
   int page_size = 1;
   int num_pages = 0;
+  // Long rows only (several workgroups per row), with phys: leave the
+  // threshold bin to the attention that reads the selection.  When every
+  // member of the bin is kept the select writes them itself; otherwise it
+  // writes kUnresolvedRow into phys[r][better .. k) and no refinement runs:
+  // the attention resolves those slots (resolve_members) and writes idx.
+  int defer = 0;
 };
+constexpr int32_t kUnresolvedRow = -2;
 size_t topk_ws_bytes(int num_req, int max_len);
 // words of the workspace that must be zero when the top-k starts
 int64_t topk_zero_words(int num_req);
 // ws_state: 0 = counters not cleared (clear them first), 1 = already cleared
 hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s);
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t s);
+// whether launch_topk takes the path that honours TopkArgs::defer
+bool topk_can_defer(int num_req, int max_len);
 
 // ---- attention -------------------------------------------------------------
 struct AttnArgs {
@@ -90,8 +99,17 @@ struct AttnArgs {
   void* out = nullptr;             // [num_req][H][dv]
   float* lse = nullptr;            // [num_req][H]
   void* ws = nullptr;
+  // optional: the top-k workspace of a selection made with TopkArgs::defer
+  // (phys rows equal to kUnresolvedRow are resolved from it, and their
+  // positions written to idx), and that top-k's max_len
+  void* tk_ws = nullptr;
+  int tk_max_len = 0;
+  int32_t* idx_out = nullptr;      // [num_req][k], receives the resolved positions
 };
 size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k);
+// whether launch_mla_bf16 resolves deferred selections (AttnArgs::tk_ws) for
+// this shape (the 16-head kernel does; the 32-head batch kernel does not)
+bool mla_resolves(int num_req, int n_heads, int k);
 hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

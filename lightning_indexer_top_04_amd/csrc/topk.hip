@@ -502,11 +502,20 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   uint32_t better;
   const uint32_t digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
   const uint32_t members = hist[digit];   // of the whole row
+  // better < k <= better + members: every member is kept exactly when
+  // members == k - better; with `defer` the members then leave with the
+  // winners, and otherwise their slots are left to the attention
+  const bool members_out = a.defer && members <= (uint32_t)a.k - better;
   if (c == 0 && threadIdx.x == 0) {
     uint32_t* rec = ws.rec + (size_t)r * 4;
     rec[0] = digit;
     rec[1] = better;
     rec[2] = hist[digit];
+  }
+  if (a.defer && c == 0) {
+    if (threadIdx.x == 0) a.count[r] = a.k;
+    if (!members_out)
+      for (int i = (int)better + (int)threadIdx.x; i < a.k; i += kBlock) a.phys[(int64_t)r * a.k + i] = kUnresolvedRow;
   }
   // winners and threshold-bin members of the chunks before this one, from
   // their suffix counts (one load pair per earlier chunk)
@@ -547,9 +556,12 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   // winners in groups of eight (fewer live registers: four workgroups fit
   // per compute unit)
   int2* cand = ws.cand + (size_t)r * a.max_len;
+  uint32_t om = better + oc;        // output slot of this workgroup's first member
+  if (!members_out) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
+    for (int j = 0; j < PER; ++j)
+      if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
+  }
   // the members' next 12 key bits go into the row's second histogram, so the
   // refinement starts from it: counted in LDS first (the level-1 histogram
   // there is no longer read), then one global add per non-empty bin
@@ -567,6 +579,9 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
       if (n) atomicAdd(&g2[i], n);
     }
   }
+  // with members_out the members are emitted like winners, at slots after
+  // every winner of the row
+  const uint32_t emit = members_out ? (win | eq) : win;
   constexpr int G = PER < 8 ? PER : 8;
 #pragma unroll
   for (int g0 = 0; g0 < PER; g0 += G) {
@@ -575,7 +590,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
     for (int u = 0; u < G; ++u) {
       const int j = g0 + u;
       const int i = chunk_pos<VW>(begin, j);
-      wv[u] = ((win >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
+      wv[u] = ((emit >> j) & 1u) ? (MAPPED ? out_value(a, r, i) : i) : -1;
     }
     if (lds_pages) {
       // every page read first, then the rows (non-winners read a valid dummy)
@@ -599,6 +614,12 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
           if (a.phys) a.phys[(int64_t)r * a.k + ow] = wp[u];
         }
         ++ow;
+      } else if (members_out && ((eq >> (g0 + u)) & 1u)) {
+        if (om < (uint32_t)a.k) {
+          a.idx[(int64_t)r * a.k + om] = wv[u];
+          a.phys[(int64_t)r * a.k + om] = wp[u];
+        }
+        ++om;
       }
     }
   }
@@ -972,8 +993,13 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
 #undef LSI_TOPK_PER
     default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kRefThreads), 0, s, a);
+  if (!a.defer) hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kRefThreads), 0, s, a);
   return hipGetLastError();
+}
+
+bool topk_can_defer(int num_req, int max_len) {
+  // the multi-workgroup path (the only one that defers)
+  return !(num_req >= num_cus() || max_len <= 32768);
 }
 
 }  // namespace lsi

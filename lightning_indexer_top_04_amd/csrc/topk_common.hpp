@@ -110,5 +110,124 @@ __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uin
   return bin;
 }
 
+// ---------------------------------------------------------------------------
+// The threshold bin of a row whose selection was left unfinished (TopkArgs::
+// defer): the row's `members` candidates sit in ws.cand (in chunk order), the
+// second histogram (key bits [19:8] of the members) in ws.h2, and the record
+// {threshold bin, count above it, members} in ws.rec.  The kept members are,
+// in candidate-list order, those whose key bits [19:8] exceed the second
+// threshold bin, then, inside that bin, those whose key bits [7:0] exceed the
+// third, then, among exact ties, the lowest positions: the same set as the
+// one-workgroup refinement keeps.  The i-th kept member takes output slot
+// better + i.  Every workgroup that calls this computes the same thresholds
+// and the same order; put(slot, position) is called for the slots in
+// [lo, hi).  NT threads; hist (kBins words) and tmp (32 words) are LDS.
+// ---------------------------------------------------------------------------
+template <int NT, class Put>
+__device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_t* hist, uint32_t* tmp,
+                                int lo, int hi, Put&& put) {
+  constexpr int E = 8;                       // candidates per thread and batch
+  const int tid = threadIdx.x;
+  const uint32_t* rec = ws.rec + (size_t)r * 4;
+  const uint32_t better = rec[1];
+  const uint32_t members = rec[2];
+  const int2* cand = ws.cand + (size_t)r * max_len;
+  const uint32_t* g2 = ws.h2 + (size_t)r * kBins;
+  const uint32_t need = (uint32_t)k - better;
+  // f(pos, key) over every candidate, E consecutive ones per thread
+  auto pass = [&](auto&& f) {
+    for (uint32_t base = 0; base < members; base += NT * E) {
+      int2 e[E];
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const uint32_t i = base + tid * E + u;
+        e[u] = i < members ? cand[i] : make_int2(-1, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < E; ++u)
+        if (e[u].x >= 0) f(e[u].x, (uint32_t)e[u].y);
+    }
+  };
+  // level 2: key bits [19:8], histogram built by the select
+  for (int i = tid; i < kBins; i += NT) hist[i] = g2[i];
+  __syncthreads();
+  uint32_t better2;
+  const uint32_t bin2 = (uint32_t)find_threshold<NT>(hist, need, true, tmp, &better2);
+  const uint32_t n2 = hist[bin2];
+  const bool take2 = n2 <= need - better2;
+  // level 3: key bits [7:0] of the members in bin2
+  uint32_t bin3 = 0, take3 = 1, pos_t = 0;
+  if (!take2) {
+    const uint32_t need_b = need - better2;
+    __syncthreads();
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    pass([&](int, uint32_t key) {
+      if (((key >> 8) & (kBins - 1)) == bin2) atomicAdd(&hist[key & 255u], 1u);
+    });
+    __syncthreads();
+    uint32_t better3;
+    bin3 = (uint32_t)find_threshold<NT>(hist, need_b, true, tmp, &better3);
+    const uint32_t n3 = hist[bin3];
+    take3 = n3 <= need_b - better3;
+    if (!take3) {
+      // exact ties (the same key): the need_c lowest positions, by a radix
+      // select over position bits [30:20], [19:9], [8:0] (ascending)
+      uint32_t need_c = need_b - better3;
+      uint32_t prefix = 0;
+      const int shifts[3] = {20, 9, 0};
+      const int widths[3] = {11, 11, 9};
+      for (int lv = 0; lv < 3; ++lv) {
+        const int sh = shifts[lv];
+        const uint32_t mask = (1u << widths[lv]) - 1u;
+        __syncthreads();
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        pass([&](int pos, uint32_t key) {
+          if (((key >> 8) & (kBins - 1)) == bin2 && (key & 255u) == bin3 &&
+              (lv == 0 || ((uint32_t)pos >> (sh + widths[lv])) == prefix))
+            atomicAdd(&hist[((uint32_t)pos >> sh) & mask], 1u);
+        });
+        __syncthreads();
+        uint32_t below;
+        const uint32_t bin = (uint32_t)find_threshold<NT>(hist, need_c, false, tmp, &below);
+        prefix = (prefix << widths[lv]) | bin;
+        need_c -= below;
+      }
+      pos_t = prefix;   // the need_c-th smallest tied position: keep positions <= pos_t
+    }
+  }
+  // the ordered pass: kept members in list order, slots better + running index
+  auto kept = [&](int pos, uint32_t key) -> bool {
+    const uint32_t d2 = (key >> 8) & (kBins - 1);
+    if (d2 != bin2) return d2 > bin2;
+    if (take2) return true;
+    const uint32_t d3 = key & 255u;
+    if (d3 != bin3) return d3 > bin3;
+    return take3 || (uint32_t)pos <= pos_t;
+  };
+  uint32_t run = 0;
+  for (uint32_t base = 0; base < members && better + run < (uint32_t)hi; base += NT * E) {
+    int2 e[E];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const uint32_t i = base + tid * E + u;
+      e[u] = i < members ? cand[i] : make_int2(-1, 0);
+      if (e[u].x >= 0 && kept(e[u].x, (uint32_t)e[u].y)) m |= 1u << u;
+    }
+    uint32_t tot;
+    uint32_t o = run + block_excl_scan<NT>((uint32_t)__popc(m), tmp, &tot) + better;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      if ((m >> u) & 1u) {
+        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, e[u].x);
+        ++o;
+      }
+    }
+    run += tot;
+  }
+}
+
 }  // namespace topk
 }  // namespace lsi

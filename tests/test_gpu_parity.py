@@ -540,3 +540,65 @@ def test_decode_step_graph_replays_match_eager():
             check_attention(out[b].float().cpu().numpy(), e_out[b].cpu().numpy().astype(np.float64),
                             f"replay {rep} req {b}")
         assert torch.allclose(lse, e_lse, rtol=1e-5, atol=1e-5), rep
+
+
+# ----------------------------------------------------------------------------
+# Fused step with the threshold bin left to the attention kernel (rows longer
+# than 32768 positions, few requests): the selection must be exactly the
+# top-k of the step's own scores (same float decisions), ties to the lower
+# positions, whatever depth of the radix the threshold needs.
+# ----------------------------------------------------------------------------
+
+def _exact_topk_of(scores, L, k):
+    s = scores[:L].astype(np.float64)
+    order = np.lexsort((np.arange(L), -s))
+    return np.sort(order[:min(k, L)])
+
+
+def _set_key(di, b, positions, codes_row, scales):
+    pt = di.page_table[b].cpu().numpy()
+    pos = np.asarray(positions, dtype=np.int64)
+    pages = torch.from_numpy(pt[pos // synth.PAGE].astype(np.int64)).to(DEV)
+    slots = torch.from_numpy(pos % synth.PAGE).to(DEV)
+    di.ikeys[pages, slots] = codes_row.to(DEV)
+    di.iscale[pages, slots] = torch.as_tensor(scales, dtype=torch.float32).to(DEV)
+
+
+@pytest.mark.parametrize("case", ["unplanted", "ties", "near_ties", "two_requests"])
+def test_decode_step_threshold_bin_resolved_by_attention(case):
+    lens = (70001,) if case != "two_requests" else (40000, 1500)
+    k = 2048
+    wl = synth.scaled(synth.DSA_128K, seed=31, seq_lens=lens, num_req=len(lens), n_planted=0, k=k)
+    di = synth.make_decode_inputs(wl, device=DEV, planted=False)
+    ik, req, kv, _ = objs(di)
+    if case in ("ties", "near_ties"):
+        s0 = lsi.index_scores(ik, req, di.q_idx, di.w)[0, :lens[0]]
+        top = int(torch.argmax(s0).item())
+        rng = np.random.default_rng(41)
+        pos = rng.choice(lens[0], size=3000, replace=False)
+        pt = di.page_table[0].cpu().numpy()
+        page, slot = int(pt[top // synth.PAGE]), top % synth.PAGE
+        row = di.ikeys[page, slot].clone()
+        sc = float(di.iscale[page, slot].item())
+        if case == "ties":
+            scales = np.full(3000, sc, dtype=np.float32)
+        else:
+            scales = (np.float32(sc) * (1.0 + np.arange(3000) * 2.0 ** -22)).astype(np.float32)
+        _set_key(di, 0, pos, row, scales)
+    scores = lsi.index_scores(ik, req, di.q_idx, di.w)
+    idx, cnt, out, lse = lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k,
+                                         di.wl.sm_scale, di.wl.dv)
+    torch.cuda.synchronize()
+    sc_h, idx_h, cnt_h = scores.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    ov = OracleView(di)
+    for b, L in enumerate(lens):
+        n = min(k, L)
+        assert cnt_h[b] == n
+        assert np.all(idx_h[b, n:] == -1)
+        got = np.sort(idx_h[b, :n])
+        assert np.array_equal(got, _exact_topk_of(sc_h[b], L, k)), f"{case} req {b}"
+        I, _ = ov.scores(b)
+        st = check_topk(idx_h[b], cnt_h[b], I, k, f"{case} req {b}")
+        ro, _ = ov.attention(b, idx_h[b, :n])
+        st.update(check_attention(out[b].float().cpu().numpy(), ro, f"{case} attn {b}"))
+        print(case, b, st)
