@@ -15,9 +15,12 @@ loop would run them; the timed region covers exactly K steps.
 
 Printed (one JSON line): tokens/s = 131072 * steps / time (whole step timed,
 inputs resident in HBM), decode steps/s, per-phase averages from HIP events on
-the launch stream, the scan's roofline (algorithmic 136 B per token: 128 key
-bytes, a 4-byte scale and a 4-byte score written, against 8 TB/s), a
-sustained scan of 32 x 128K tokens in one launch, the CPU
+the launch stream, every kernel of the step timed with HIP events recorded on
+its stream between launches (library profiling marks), the roofline of the
+step's longest kernel (its algorithmic bytes per launch over its mean
+duration, against 8 TB/s; the scan's algorithmic bytes are 132 per token:
+128 key bytes and a 4-byte scale, the 4-byte score it writes being reported
+as overhead), a sustained scan of 32 x 128K tokens in one launch, the CPU
 oracle's throughput on a bounded sample of the same step, and (unless
 --no-extra; --extra picks a subset) the un-planted twin of the step, the
 ragged 64-request decode step, the two-stage compact-key search at 512K
@@ -34,13 +37,19 @@ import os
 import sys
 import time
 
+# the CPU oracle's BLAS pool: as many threads as this process may run on,
+# unless the environment already fixes it (set before numpy is imported)
+_AFFINITY = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_AFFINITY))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "indexer-scanned tokens/s and decode steps/s (index+top-k+sparse attn) @128K ctx"
 HBM_PEAK_GBS = 8000.0
-BYTES_PER_TOKEN = 132          # 128 fp8 key bytes + 4-byte scale
-SCAN_BYTES_PER_TOKEN = BYTES_PER_TOKEN + 4   # ... and the fp32 score the scan writes
+BYTES_PER_TOKEN = 132          # 128 fp8 key bytes + 4-byte scale (algorithmic scan bytes)
+SCORE_BYTES_PER_TOKEN = 4      # the fp32 score the scan writes (implementation overhead)
 
 
 EXTRAS = ("unplanted", "ragged", "two_stage", "prefill", "multilayer")
@@ -112,8 +121,7 @@ def main():
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
     out = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(1, H, dtype=torch.float32, device=dev)
-    ws = torch.empty(lsi.decode_step_workspace_bytes(1, L, k, H, dv), dtype=torch.uint8,
-                     device=dev)
+    ws = lsi.decode_step_workspace(1, L, k, H, dv, dev)
     def step(r, stream=None):
         lsi.decode_step(ik, kv, None, reqs[r], q_idx[r], w[r], q_attn[r], k, wl.sm_scale, dv,
                         out=out, lse=lse, idx=idx, count=cnt, ws=ws, stream=stream)
@@ -196,7 +204,42 @@ def main():
     t_scan = per_launch_ms(g_scan)
     t_topk = per_launch_ms(g_topk)
     t_mla = per_launch_ms(g_mla)
-    scan_gbs = L * SCAN_BYTES_PER_TOKEN / (t_scan * 1e-3) / 1e9
+
+    # ---- every kernel of the step, timed live: HIP events recorded on the
+    # launch stream before the step's first kernel and after each kernel
+    # (lsi_profile_events), over n_prof steps queued behind a sleep kernel so
+    # that the device runs them back to back --------------------------------
+    n_prof = 4 * R
+    timer = lsi.KernelTimer(capacity=8 * n_prof)
+    torch.cuda.synchronize()
+    try:
+        torch.cuda._sleep(2_000_000)
+    except Exception:
+        pass
+    with timer:
+        for i in range(n_prof):
+            step(i % R)
+    kern = {}
+    for name, ms in timer.intervals():
+        kern.setdefault(name, []).append(ms * 1e3)
+    alg = {   # algorithmic HBM bytes per launch (one 131072-token request)
+        "scan_dma_kernel<fp8>": L * BYTES_PER_TOKEN,
+        "topk_hist_kernel": L * 4,
+        "topk_select_kernel": L * 4 + k * 4,
+        "topk_refine_kernel": k * 4,
+        "mla_bf16_kernel": k * 576 * 2 + H * 576 * 2,
+        "mla_combine_kernel": H * dv * 2,
+    }
+    kernels = {}
+    for name, v in kern.items():
+        mean_us = sum(v) / len(v)
+        b = alg.get(name)
+        kernels[name] = {"launches": len(v), "mean_us": mean_us,
+                         "median_us": sorted(v)[len(v) // 2], "algorithmic_bytes": b,
+                         "GB_s": None if b is None else b / (mean_us * 1e-6) / 1e9,
+                         "frac_of_hbm_peak": None if b is None else b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    dom = max(kernels, key=lambda n: kernels[n]["mean_us"])
+    scan_us = kernels.get("scan_dma_kernel<fp8>", {}).get("mean_us", t_scan * 1e3)
 
     # ---- sustained scan: all R requests in one launch ---------------------
     req_all = lsi.Requests(di.seq_lens, di.page_table, L)
@@ -219,7 +262,7 @@ def main():
     g_sus.replay()
     torch.cuda.synchronize()
     t_sus_graph = event_loop(lambda i: g_sus.replay(), 3, torch.cuda.current_stream()) / n_sus
-    sus_gbs = R * L * SCAN_BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
+    sus_gbs = R * L * BYTES_PER_TOKEN / (t_sus * 1e-3) / 1e9
     del g_sus
 
     # spread of the step time: the same graph of R steps replayed 10 more
@@ -244,7 +287,7 @@ def main():
     read_gbs = max(ref_gbs.values())
     del big, dst, rows
     torch.cuda.empty_cache()
-    traffic = measured_traffic()
+    traffic = measured_traffic(dom)
 
     step_bytes = L * BYTES_PER_TOKEN + k * 576 * 2 + H * 576 * 2 + H * dv * 2
     res = {
@@ -267,19 +310,35 @@ def main():
         "timing": "HIP graph replay (one step per input set); eager per-call figure below",
         "eager_ms_per_step": eager_ms,
         "step_us_p10_p50_p90": [pct(0.1) * 1e3, pct(0.5) * 1e3, pct(0.9) * 1e3],
-        "phases_us": {"scan": t_scan * 1e3, "topk": t_topk * 1e3, "mla": t_mla * 1e3},
-        "scan_tokens_per_s": L / (t_scan * 1e-3),
-        "roofline": {"kernel": "scan_dma_kernel<0, 2> (fp8 keys)", "bound": "hbm", "achieved": scan_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS,
+        "phases_us": {"scan": t_scan * 1e3, "topk": t_topk * 1e3, "mla": t_mla * 1e3,
+                      "how": "each phase's standalone entry point (index_scores, topk, "
+                             "sparse_mla_decode) over the 32 sets, graph replays between HIP events"},
+        "scan_tokens_per_s": L / (scan_us * 1e-6),
+        "step_kernels": {"kernels": kernels,
+                         "how": f"{n_prof} eager steps queued behind a sleep kernel; HIP events "
+                                "recorded on the launch stream before the step's first kernel and "
+                                "after each kernel (lsi_profile_events); mean of the intervals",
+                         "sum_of_means_us": sum(x["mean_us"] for x in kernels.values())},
+        "roofline": {"kernel": dom, "bound": "hbm",
+                     "achieved": kernels[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kernels[dom]["frac_of_hbm_peak"],
                      "traffic": traffic,
-                     "traffic_GB_s": None if traffic is None else traffic / (t_scan * 1e-3) / 1e9,
-                     "overfetch": None if traffic is None else traffic / (L * SCAN_BYTES_PER_TOKEN),
-                     "note": "131072 tokens x 136 B per launch / average launch time "
-                             "(HIP events around graph replays of the scan)"},
+                     "traffic_GB_s": None if traffic is None else traffic / (kernels[dom]["mean_us"] * 1e-6) / 1e9,
+                     "overfetch": None if traffic is None or not kernels[dom]["algorithmic_bytes"]
+                     else traffic / kernels[dom]["algorithmic_bytes"],
+                     "note": f"the step's longest kernel: {kernels[dom]['algorithmic_bytes']} "
+                             f"algorithmic bytes per launch / its mean duration "
+                             f"{kernels[dom]['mean_us']:.2f} us (step_kernels)"},
+        "scan_roofline": {"kernel": "scan_dma_kernel<fp8>", "bound": "hbm",
+                          "bytes_per_token": BYTES_PER_TOKEN,
+                          "achieved_GB_s": L * BYTES_PER_TOKEN / (scan_us * 1e-6) / 1e9,
+                          "frac": L * BYTES_PER_TOKEN / (scan_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "score_write_overhead_bytes_per_token": SCORE_BYTES_PER_TOKEN},
         "scan_sustained": {"tokens": R * L, "us": t_sus * 1e3,
                            "tokens_per_s": R * L / (t_sus * 1e-3), "GB_s": sus_gbs,
                            "frac": sus_gbs / HBM_PEAK_GBS,
-                           "bytes_per_token": SCAN_BYTES_PER_TOKEN,
+                           "bytes_per_token": BYTES_PER_TOKEN,
+                           "score_write_overhead_bytes_per_token": SCORE_BYTES_PER_TOKEN,
                            "timing": "HIP events around 20 back-to-back launches on one stream; "
                                      "median of 5 such windows",
                            "us_windows_min_max": [sus_windows[0] * 1e3, sus_windows[-1] * 1e3],
@@ -365,8 +424,7 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
         cnt = torch.empty(1, dtype=torch.int32, device=dev)
         o = torch.empty(1, H, dv, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(1, H, dtype=torch.float32, device=dev)
-        ws = torch.empty(lsi.decode_step_workspace_bytes(1, L1, k, H, dv), dtype=torch.uint8,
-                         device=dev)
+        ws = lsi.decode_step_workspace(1, L1, k, H, dv, dev)
 
         def unplanted_steps():
             for r in range(nset):
@@ -395,8 +453,7 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
         cnt = torch.empty(B, dtype=torch.int32, device=dev)
         o = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-        ws = torch.empty(lsi.decode_step_workspace_bytes(B, maxL, k, H, dv), dtype=torch.uint8,
-                         device=dev)
+        ws = lsi.decode_step_workspace(B, maxL, k, H, dv, dev)
         t = graph_ms(lambda: lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k,
                                              wl.sm_scale, dv, out=o, lse=lse, idx=idx, count=cnt,
                                              ws=ws), n=2, reps=5)
@@ -529,23 +586,23 @@ def multilayer(lsi, synth, torch, dev, graph_ms, n_layers=61):
                     "beside layer l's attention on a second stream, after layer l-1"}
 
 
-def measured_traffic():
-    """HBM bytes per launch of the 128K scan from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the scan
-    source has changed since the counters were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` in the one-request step, from the
+    committed counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain copy), or None when there is none for that kernel or its source
+    file has changed since the counters were taken."""
     import hashlib
-    summ = os.path.join(ROOT, "profiles", "scan_fp8_dsa128k_counters.json")
-    src = os.path.join(ROOT, "lightning_indexer_top_04_amd", "csrc", "scan.hip")
+    summ = os.path.join(ROOT, "profiles", "kernel_counters_dsa128k.json")
     try:
         with open(summ) as f:
-            rec = json.load(f)
-        with open(src, "rb") as f:
+            rec = json.load(f)["kernels"][kernel]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
+    except (OSError, KeyError, ValueError):
         return None
-    if rec.get("scan_hip_sha256") != digest:
+    if rec.get("source_sha256") != digest:
         return None
-    return rec["single_request"]["bytes_per_launch"]
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(di, wl, L, seconds):
@@ -554,11 +611,11 @@ def cpu_baseline(di, wl, L, seconds):
 
     import oracle as O
     from lightning_indexer_top_04_amd import synth
-    try:
+    try:   # the BLAS pool's size as numpy runs it (set from the environment at start-up)
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = int(os.environ.get("OMP_NUM_THREADS", _AFFINITY))
     pt = di.page_table[0].cpu().numpy()
     n_pages = L // 64
     pages = di.page_table[0, :n_pages].long()
@@ -597,7 +654,8 @@ def cpu_baseline(di, wl, L, seconds):
     except Exception:
         pass
     del pt
-    return {"value": L * n / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": L * n / el, "unit": "tokens/s", "cores": int(threads),
+            "affinity_cpus": _AFFINITY, "kind": "oracle",
             "steps_per_s": n / el,
             "sample": f"{n} oracle decode steps of one 131072-token request "
                       f"(numpy float64, {el:.1f}s)",

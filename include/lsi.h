@@ -28,9 +28,13 @@
  *     *_workspace_bytes() function returns; its contents on entry do not
  *     matter and on return are unspecified.
  *   - Work is enqueued on the caller's stream; no call synchronises the host.
- *     Arguments are validated on the host BEFORE anything is enqueued; on a
- *     non-zero status nothing was enqueued.  A launch failure returns
- *     LSI_ERR_HIP.  lsi_last_error() gives a per-thread message.
+ *     Arguments are validated on the host BEFORE anything is enqueued:
+ *     LSI_ERR_INVALID_ARG, LSI_ERR_UNSUPPORTED and LSI_ERR_WORKSPACE mean
+ *     nothing was enqueued.  LSI_ERR_HIP (a launch or runtime call failed)
+ *     can come after some of a call's kernels or copies were already
+ *     enqueued: the call's outputs (and, for lsi_decode_step, its workspace
+ *     state words) are then undefined.  lsi_last_error_detail() gives a
+ *     per-thread message.
  *   - Paged caches: token s of request b lives in physical page
  *     page_table[b][s / page_size], slot s % page_size.  Indexer keys and
  *     attention KV use the same page table and page size.  A page id outside
@@ -160,7 +164,17 @@ int32_t lsi_sparse_mla_decode(const lsi_paged_cache* kv,
 /* ---- fused decode step ---------------------------------------------------
  * lsi_index_scores -> lsi_topk -> lsi_sparse_mla_decode for one layer, on
  * one stream, with the scores kept in the workspace.  Arguments have the
- * meanings given above; idx/count receive the selection. */
+ * meanings given above; idx/count receive the selection.
+ * Workspace state: unlike the other calls' scratch, the first
+ * lsi_decode_step_state_bytes(num_req) bytes of this call's workspace carry
+ * state from one call to the next.  They must be zero when a workspace is
+ * first used (allocate it zero-filled, or clear it once); every call that
+ * returns LSI_OK leaves them zero again, so a workspace can be reused call
+ * after call with no clearing.  After a call that returned an error, or if
+ * the buffer was used for anything else in between, clear them again.
+ * (One-request steps build the top-k's histograms inside the scan, which
+ * adds into these words; the attention kernel clears them afterwards.) */
+size_t lsi_decode_step_state_bytes(int32_t num_req);
 size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len,
                                        int32_t k, int32_t n_heads,
                                        int32_t dv);
@@ -182,7 +196,9 @@ int32_t lsi_decode_step(const lsi_paged_cache* ikeys,
  * code on that GPU and held until the process ends.  The call allocates and
  * frees nothing.  A call that needs more scratch than that
  * (lsi_decode_step_workspace_bytes() above the limit) returns
- * LSI_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * LSI_ERR_WORKSPACE before anything is enqueued.  The array starts zeroed,
+ * which is the state lsi_decode_step's workspace needs, and every successful
+ * call leaves its state words zero again.  Every call on one GPU uses
  * the same array: calls that overlap on one GPU (on different streams, or
  * from different threads without ordering) race and give undefined results;
  * calls ordered on one stream are safe. */
@@ -304,9 +320,40 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys,
                                size_t ws_bytes, hipStream_t s_compute,
                                hipStream_t s_copy);
 
+/* ---- workspace sizes through one call -------------------------------------
+ * The same figures as the *_workspace_bytes functions above, selected by op.
+ * Fields that an op does not use are ignored.  For LSI_OP_PREFILL, num_req
+ * is T (the chunk's queries) and max_seq_len is hist_len.  Returns 0 for an
+ * unknown op or invalid sizes. */
+enum {
+  LSI_OP_TOPK = 1, LSI_OP_SPARSE_MLA = 2, LSI_OP_DECODE_STEP = 3,
+  LSI_OP_MULTILAYER = 4, LSI_OP_TWO_STAGE = 5, LSI_OP_PREFILL = 6
+};
+typedef struct {
+  int32_t num_req, max_seq_len, k, n_heads, dv;  /* decode-side calls          */
+  int32_t n_cand;                                /* LSI_OP_TWO_STAGE           */
+  int32_t dim, block_tokens, scores_external;    /* LSI_OP_PREFILL             */
+} lsi_ws_query;
+size_t lsi_workspace_bytes(int32_t op, const lsi_ws_query* q);
+
+/* ---- kernel timing ---------------------------------------------------------
+ * Profiling aid for the calling host thread.  With events != NULL, every
+ * kernel that later calls from this thread launch takes the next two caller
+ * events (created with timing enabled) as its start and stop events, given
+ * to the dispatch itself (hipExtLaunchKernel), and names[i] (host array of
+ * capacity / 2 entries, may be NULL) receives a static string naming the
+ * kernel of pair i = (events[2i], events[2i+1]), until `capacity` events are
+ * used.  The elapsed time of a pair is that kernel's duration; nothing extra
+ * is enqueued.  lsi_profile_events(NULL, NULL, 0) stops.  Returns the number
+ * of events used since the previous call. */
+int32_t lsi_profile_events(hipEvent_t* events, const char** names,
+                           int32_t capacity);
+
 /* ---- diagnostics ---------------------------------------------------------*/
 const char* lsi_status_string(int32_t status);   /* static string          */
-const char* lsi_last_error(void);                /* per-thread detail       */
+const char* lsi_last_error_detail(void);         /* per-thread detail of the
+                                                    last failure            */
+const char* lsi_last_error(void);                /* the same string         */
 int32_t lsi_version(void);                       /* major*10000+minor*100+patch */
 
 #ifdef __cplusplus

@@ -9,6 +9,24 @@ namespace lsi {
 
 namespace {
 thread_local std::string g_last_error;
+// profiling marks of the calling thread (lsi_profile_events)
+struct ProfState {
+  hipEvent_t* ev = nullptr;
+  const char** names = nullptr;
+  int cap = 0;
+  int used = 0;
+};
+thread_local ProfState g_prof;
+}
+
+bool prof_next(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  ProfState& p = g_prof;
+  if (p.ev == nullptr || p.used + 2 > p.cap) return false;
+  *start = p.ev[p.used];
+  *stop = p.ev[p.used + 1];
+  if (p.names) p.names[p.used / 2] = name;
+  p.used += 2;
+  return true;
 }
 
 void set_error(const std::string& msg) { g_last_error = msg; }
@@ -288,10 +306,11 @@ int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
                        const lsi_batch* batch, const void* q_idx, int32_t n_idx_heads,
                        int32_t idx_dim, const float* w, int32_t k, int32_t* idx, int32_t* count,
                        float* scores, int64_t ld, void* topk_ws, int32_t* phys, hipStream_t stream,
-                       const char* what, bool defer = false) {
+                       const char* what, bool defer = false, uint32_t* hist_rep = nullptr) {
   ScanArgs sa = scan_args(ikeys, batch, q_idx, n_idx_heads, idx_dim, w, scores, ld);
   sa.zero_ptr = static_cast<uint32_t*>(topk_ws);
   sa.zero_words = topk_zero_words(batch->num_req);
+  sa.hist_rep = hist_rep;
   LSI_LAUNCH(run_scan(ikeys->dtype, sa, stream), std::string(what) + " (scan)");
 
   TopkArgs t;
@@ -310,6 +329,7 @@ int32_t enqueue_select(const lsi_paged_cache* ikeys, const lsi_paged_cache* kv,
   t.page_size = kv->page_size;
   t.num_pages = kv->num_pages;
   t.defer = defer ? 1 : 0;
+  t.hist_rep = hist_rep;
   LSI_LAUNCH(launch_topk(t, 1, stream), std::string(what) + " (top-k)");
   return LSI_OK;
 }
@@ -319,12 +339,15 @@ int32_t enqueue_attend(const lsi_paged_cache* kv, const lsi_paged_cache* v, cons
                        const void* q_attn, int32_t n_heads, int32_t dk, int32_t dv,
                        const int32_t* idx, int32_t k, float sm_scale, void* out, float* lse,
                        void* attn_wsp, const int32_t* phys, hipStream_t stream, const char* what,
-                       void* deferred_topk_ws = nullptr, int32_t* idx_out = nullptr) {
+                       void* deferred_topk_ws = nullptr, int32_t* idx_out = nullptr,
+                       uint32_t* zero_ptr = nullptr, int64_t zero_words = 0) {
   AttnArgs a = attn_args(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse, attn_wsp);
   a.phys = phys;
   a.tk_ws = deferred_topk_ws;
   a.tk_max_len = batch->max_seq_len;
   a.idx_out = idx_out;
+  a.zero_ptr = zero_ptr;
+  a.zero_words = zero_words;
   LSI_LAUNCH(run_attn(kv->dtype, a, stream), std::string(what) + " (attention)");
   return LSI_OK;
 }
@@ -359,6 +382,20 @@ const char* lsi_status_string(int32_t status) {
 }
 
 const char* lsi_last_error(void) { return g_last_error.c_str(); }
+const char* lsi_last_error_detail(void) { return g_last_error.c_str(); }
+
+int32_t lsi_profile_events(hipEvent_t* events, const char** names, int32_t capacity) {
+  const int32_t recorded = g_prof.used;
+  if (events == nullptr || capacity <= 0) {
+    g_prof = ProfState{};
+  } else {
+    g_prof.ev = events;
+    g_prof.names = names;
+    g_prof.cap = capacity;
+    g_prof.used = 0;
+  }
+  return recorded;
+}
 
 int32_t lsi_index_scores(const lsi_paged_cache* ikeys, const lsi_batch* batch, const void* q,
                          int32_t n_heads, int32_t dim, const float* w, float* scores, int64_t ld,
@@ -411,14 +448,20 @@ int32_t lsi_sparse_mla_decode(const lsi_paged_cache* kv, const lsi_paged_cache* 
   return check_launch("lsi_sparse_mla_decode");
 }
 
+size_t lsi_decode_step_state_bytes(int32_t num_req) {
+  if (num_req < 1) return 0;
+  return align_up((size_t)num_req * kHistReps * kHistWords * sizeof(uint32_t), kWsAlign);
+}
+
 size_t lsi_decode_step_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k,
                                        int32_t n_heads, int32_t dv) {
   if (num_req < 1 || max_seq_len < 0 || k < 1 || n_heads < 1) return 0;
+  const size_t st = lsi_decode_step_state_bytes(num_req);
   const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
   const size_t tk = topk_ws_bytes(num_req, max_seq_len);
   const size_t ph = align_up((size_t)num_req * k * sizeof(int32_t), kWsAlign);
   const size_t at = (n_heads % 16 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
-  return sc + tk + ph + at;
+  return st + sc + tk + ph + at;
 }
 
 }  // extern "C"
@@ -451,6 +494,10 @@ int32_t enqueue_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache*
                             float* lse, void* workspace, hipStream_t stream, const char* what) {
   const int64_t ld = scores_ld(batch->max_seq_len);
   char* ws = static_cast<char*>(workspace);
+  // state kept between calls (zero on entry and on return): the replicated
+  // histograms the scan builds for the top-k
+  uint32_t* hist_rep = reinterpret_cast<uint32_t*>(ws);
+  ws += lsi_decode_step_state_bytes(batch->num_req);
   float* scores = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
   void* topk_ws = ws;
@@ -464,10 +511,16 @@ int32_t enqueue_decode_step(const lsi_paged_cache* ikeys, const lsi_paged_cache*
   // reads from the top-k workspace and writes their positions to idx.
   const bool defer = kv->dtype == LSI_BF16 && mla_resolves(batch->num_req, n_heads, k) &&
                      topk_can_defer(batch->num_req, batch->max_seq_len);
+  // One request with fp8 keys: the scan also builds the top-k's histograms
+  // (no histogram launch); the attention clears them again afterwards.
+  const bool scan_hist = defer && ikeys->dtype == LSI_FP8_E4M3 &&
+                         scan_builds_hist(batch->num_req, batch->max_seq_len, ikeys->page_size);
   LSI_TRY(enqueue_select(ikeys, kv, batch, q_idx, n_idx_heads, idx_dim, w, k, idx, count, scores,
-                         ld, topk_ws, phys, stream, what, defer));
+                         ld, topk_ws, phys, stream, what, defer, scan_hist ? hist_rep : nullptr));
   LSI_TRY(enqueue_attend(kv, v, batch, q_attn, n_heads, dk, dv, idx, k, sm_scale, out, lse,
-                         attn_wsp, phys, stream, what, defer ? topk_ws : nullptr, defer ? idx : nullptr));
+                         attn_wsp, phys, stream, what, defer ? topk_ws : nullptr, defer ? idx : nullptr,
+                         scan_hist ? hist_rep : nullptr,
+                         scan_hist ? (int64_t)batch->num_req * kHistReps * kHistWords : 0));
   return check_launch(what);
 }
 
@@ -618,7 +671,6 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t sched
     if (_e != hipSuccess)                                                                 \
       return fail(LSI_ERR_HIP, std::string("lsi_multilayer_decode: ") + hipGetErrorString(_e)); \
   } while (0)
-
   // `pending`: a selection made on si that `stream` has not waited for yet.
   // There is at most one: the next layer that reads it waits before the next
   // indexer records the event again.
@@ -829,7 +881,6 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
     if (_e != hipSuccess)                                                                 \
       return fail(LSI_ERR_HIP, std::string("lsi_prefill_index_topk: ") + hipGetErrorString(_e)); \
   } while (0)
-
   LSI_HIP(launch_zero(range, 2 * (int64_t)T, s_compute));
   // the copy stream must not overwrite buffers a previous call still reads
   LSI_HIP(hipEventRecord(ev.start, s_compute));
@@ -882,3 +933,20 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
 }
 
 }  // extern "C"
+
+extern "C" size_t lsi_workspace_bytes(int32_t op, const lsi_ws_query* q) {
+  if (q == nullptr) return 0;
+  switch (op) {
+    case LSI_OP_TOPK: return lsi_topk_workspace_bytes(q->num_req, q->max_seq_len, q->k);
+    case LSI_OP_SPARSE_MLA: return lsi_sparse_mla_workspace_bytes(q->num_req, q->n_heads, q->dv, q->k);
+    case LSI_OP_DECODE_STEP:
+      return lsi_decode_step_workspace_bytes(q->num_req, q->max_seq_len, q->k, q->n_heads, q->dv);
+    case LSI_OP_MULTILAYER:
+      return lsi_multilayer_workspace_bytes(q->num_req, q->max_seq_len, q->k, q->n_heads, q->dv);
+    case LSI_OP_TWO_STAGE: return lsi_two_stage_workspace_bytes(q->num_req, q->max_seq_len, q->n_cand, q->k);
+    case LSI_OP_PREFILL:
+      return lsi_prefill_workspace_bytes(q->max_seq_len, q->num_req, q->dim, q->block_tokens, q->k,
+                                         q->scores_external);
+    default: return 0;
+  }
+}

@@ -152,6 +152,13 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   // group of one request runs on one XCD, so the combine of that group (placed
   // on the same XCD) reads their partials from that XCD's L2; the selected
   // rows, shared by all head groups, are what crosses XCDs instead.
+  if (a.zero_ptr) {
+    // clear the scan-built histograms the selection has read (they must be
+    // zero when the next scan starts)
+    const int64_t nthreads = (int64_t)gridDim.x * kMThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kMThreads + threadIdx.x; i < a.zero_words; i += nthreads)
+      a.zero_ptr[i] = 0u;
+  }
   const int n_hg = a.n_heads / kMH;
   const int bid = blockIdx.x;
   const int jx = bid >> 3;
@@ -211,12 +218,7 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
     // block buffer is free until the gather below.
     const topk::Ws tw = topk::carve(a.tk_ws, a.num_req, a.tk_max_len);
     topk::resolve_members<kMThreads>(tw, b, a.tk_max_len, a.k, reinterpret_cast<uint32_t*>(kvs), rtmp, r0, r1,
-                                     [&](int slot, int pos) {
-                                       int row = -1;
-                                       if (pos >= 0 && pos < L) {
-                                         const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-                                         if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
-                                       }
+                                     [&](int slot, int pos, int row) {
                                        rows_all[slot - r0] = (row < 0 || row >= n_rows_pool) ? -1 : row;
                                        if (hg == 0) a.idx_out[(int64_t)b * a.k + slot] = pos;
                                      });
@@ -832,20 +834,20 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
   const int units = a.num_req * nsplit;
   if (p.wide) {
     const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / kWH);
-    hipLaunchKernelGGL(mla_bf16_wide_kernel, dim3(grid), dim3(kWThreads), 0, s, a, rows_per_split, nsplit,
+    launch(mla_bf16_wide_kernel, dim3(grid), dim3(kWThreads), 0, s, "mla_bf16_wide_kernel", a, rows_per_split, nsplit,
                        units, part_o, part_lse);
   } else {
     // 8 XCDs x (head group instances per XCD) x splits
     const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
     const int grid = (int)(8 * ceil_div(inst, 8) * nsplit);
-    hipLaunchKernelGGL(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, a, rows_per_split, nsplit,
+    launch(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, "mla_bf16_kernel", a, rows_per_split, nsplit,
                        units, part_o, part_lse);
   }
   if (nsplit > 1) {
     // one block per (request, head), laid out so that head group instance i
     // (16 heads) lands on XCD i % 8 like its partials
     const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(8 * 16 * ceil_div(inst, 8))), dim3(kDV / 4), 0, s,
+    launch(mla_combine_kernel, dim3((unsigned)(8 * 16 * ceil_div(inst, 8))), dim3(kDV / 4), 0, s, "mla_combine_kernel",
                        a, nsplit, part_o, part_lse);
   }
   return hipGetLastError();
@@ -853,7 +855,7 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   const size_t smem = sizeof(float) * (a.dk + 256 + 256 + 8);
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.n_heads, a.num_req), dim3(256), smem, s, a);
+  launch(attn_f32_kernel, dim3(a.n_heads, a.num_req), dim3(256), smem, s, "attn_f32_kernel", a);
   return hipGetLastError();
 }
 

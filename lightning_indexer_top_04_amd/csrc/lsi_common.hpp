@@ -1,6 +1,7 @@
 // Shared device and host helpers of liblsi (gfx950 / CDNA4 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +81,23 @@ __device__ __forceinline__ float wave_sum(float x) {
 void set_error(const std::string& msg);
 int32_t fail(int32_t status, const std::string& msg);
 int32_t check_launch(const char* what);
+// Kernel timing (lsi_profile_events): with profiling on for the calling
+// thread, hands out the next pair of caller events for a kernel named `name`
+// (false when off or when the caller's events are used up).
+bool prof_next(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through this: with timing on, the
+// start and stop events travel with the dispatch itself (no extra packets on
+// the stream, so the timed kernel runs as it would untimed).
+template <class K, class... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, const char* name,
+                   Args... args) {
+  hipEvent_t e0, e1;
+  if (prof_next(name, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+}
 
 inline int ilog2(int v) {
   int r = 0;

@@ -31,7 +31,17 @@ struct ScanArgs {
   // top-k that follows finds its counters at zero without another launch
   uint32_t* zero_ptr = nullptr;
   int64_t zero_words = 0;
+  // optional (fp8 keys, contiguous walk, one request, slices of at most
+  // 4096 positions: scan_builds_hist): every workgroup adds the histogram of
+  // its scores' top 12 key bits (and of their top 6 bits) into replica
+  // blockIdx % kHistReps of the row's replicated histogram, which must be
+  // zero when the scan starts ([num_req][kHistReps][kHistWords] words)
+  uint32_t* hist_rep = nullptr;
 };
+constexpr int kHistReps = 8;
+constexpr int kHistWords = 4096 + 64;     // 12-bit digits, then 6-bit digits
+// whether a scan of this shape can build the replicated histogram
+bool scan_builds_hist(int num_req, int max_seq_len, int page_size);
 
 hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s);
@@ -66,6 +76,10 @@ struct TopkArgs {
   // writes kUnresolvedRow into phys[r][better .. k) and no refinement runs:
   // the attention resolves those slots (resolve_members) and writes idx.
   int defer = 0;
+  // optional: the row histograms were built by the scan (ScanArgs::hist_rep,
+  // the same array): no histogram launch; the select reads them and places
+  // its outputs with one returning atomic per workgroup
+  const uint32_t* hist_rep = nullptr;
 };
 constexpr int32_t kUnresolvedRow = -2;
 size_t topk_ws_bytes(int num_req, int max_len);
@@ -105,6 +119,10 @@ struct AttnArgs {
   void* tk_ws = nullptr;
   int tk_max_len = 0;
   int32_t* idx_out = nullptr;      // [num_req][k], receives the resolved positions
+  // optional: clear this many uint32 words at zero_ptr (grid-stride; the
+  // scan-built histograms, once the selection has read them)
+  uint32_t* zero_ptr = nullptr;
+  int64_t zero_words = 0;
 };
 size_t mla_ws_bytes(int num_req, int n_heads, int dv, int k);
 // whether launch_mla_bf16 resolves deferred selections (AttnArgs::tk_ws) for

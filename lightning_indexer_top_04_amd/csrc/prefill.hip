@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanAr
 
 hipError_t launch_prefill_scan(const PrefillScanArgs& a, hipStream_t s) {
   dim3 grid((unsigned)ceil_div(a.T, kQPerWg));
-  hipLaunchKernelGGL(prefill_scan_kernel, grid, dim3(kThreads), 0, s, a);
+  launch(prefill_scan_kernel, grid, dim3(kThreads), 0, s, "prefill_scan_kernel", a);
   return hipGetLastError();
 }
 

@@ -864,6 +864,31 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   }
   // no DMA may still be writing this workgroup's LDS when it retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (a.hist_rep != nullptr) {
+    // The histogram of this workgroup's scores for the top-k that follows:
+    // 12-bit and 6-bit top key digits, counted in the ring's LDS (no DMA is
+    // in flight any more) and added to one of the row's replicas (workgroups
+    // spread over kHistReps copies, so that the few hot bins take a sixteenth
+    // of the atomics each).  Every score of the wave is still in its staging
+    // buffer: the host enables this for slices of at most 32 tiles per wave.
+    uint32_t* lh = reinterpret_cast<uint32_t*>(&ring[0][0]);
+    static_assert(sizeof(ring) >= kHistWords * 4, "the ring holds the histogram");
+    __syncthreads();
+    for (int i = tid; i < kHistWords; i += kThreads) lh[i] = 0u;
+    __syncthreads();
+    const int nsc = myn > 0 ? min(myn * kTile, (end - begin) - my0 * kTile) : 0;
+    for (int i = lane; i < nsc; i += 64) {
+      const uint32_t key = float_key(stage[i]);
+      atomicAdd(&lh[key >> 20], 1u);
+      atomicAdd(&lh[4096 + (key >> 26)], 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = a.hist_rep + ((size_t)b * kHistReps + blockIdx.x % kHistReps) * kHistWords;
+    for (int i = tid; i < kHistWords; i += kThreads) {
+      const uint32_t v = lh[i];
+      if (v) atomicAdd(&gh[i], v);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -905,6 +930,8 @@ __global__ __launch_bounds__(256) void scan_f32_kernel(ScanArgs a) {
   a.scores[(int64_t)b * a.ld + s] = total;
 }
 
+}  // namespace
+
 int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather, int wg_per_cu) {
   // aim at one wave of resident workgroups over the whole batch
   const int64_t target = (int64_t)num_cus() * wg_per_cu;
@@ -914,6 +941,14 @@ int pick_chunk(int64_t num_req, int64_t max_items, int page_size, bool gather, i
   if (!gather) chunk = std::min<int64_t>(chunk, std::max<int64_t>(kMaxChunk, unit));
   return (int)std::min<int64_t>(chunk, 1 << 24);
 }
+
+bool scan_builds_hist(int num_req, int max_seq_len, int page_size) {
+  // one request walks the contiguous path; each wave's run must fit its
+  // staging buffer (32 tiles: slices of at most 4096 positions)
+  return num_req == 1 && pick_chunk(1, max_seq_len, page_size, false, 3) <= kWaves * kFlushTiles * kTile;
+}
+
+namespace {
 
 template <int KIND>
 hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
@@ -947,7 +982,7 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
             break;
           }
         }
-        hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), dim3((unsigned)G), dim3(kThreads), 0, s, a,
+        launch((scan_dma_kernel<KIND, kRingTiles>), dim3((unsigned)G), dim3(kThreads), 0, s, KIND == KIND_FP8 ? "scan_dma_kernel<fp8>" : "scan_dma_kernel<int4>", a,
                            (int)unit, ps, (int)n_u, (int)sp_u);
         return hipGetLastError();
       }
@@ -957,10 +992,11 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   // the DMA scan stages a slice's page ids, two per thread
   if (!gather && (chunk + a.page_size - 1) / a.page_size > kMaxChunkPages) return hipErrorInvalidValue;
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
-  if (!gather)
-    hipLaunchKernelGGL((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, a, chunk, ps, 0, 0);
-  else
-    hipLaunchKernelGGL(scan_gather_kernel<KIND>, grid, dim3(kThreads), 0, s, a, chunk, ps);
+  if (!gather) {
+    launch((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, KIND == KIND_FP8 ? "scan_dma_kernel<fp8>" : "scan_dma_kernel<int4>", a, chunk, ps, 0, 0);
+  } else {
+    launch(scan_gather_kernel<KIND>, grid, dim3(kThreads), 0, s, KIND == KIND_FP8 ? "scan_gather_kernel<fp8>" : "scan_gather_kernel<int4>", a, chunk, ps);
+  }
   return hipGetLastError();
 }
 
@@ -972,7 +1008,7 @@ hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s) { return launch_mf
 hipError_t launch_scan_f32(const ScanArgs& a, hipStream_t s) {
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_seq_len, 256)), (unsigned)a.num_req);
   const size_t smem = sizeof(float) * ((size_t)a.n_heads * a.dim + a.n_heads);
-  hipLaunchKernelGGL(scan_f32_kernel, grid, dim3(256), smem, s, a);
+  launch(scan_f32_kernel, grid, dim3(256), smem, s, "scan_f32_kernel", a);
   return hipGetLastError();
 }
 

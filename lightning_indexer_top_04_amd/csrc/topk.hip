@@ -437,6 +437,24 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
   if (threadIdx.x == 0) a.count[r] = (int32_t)min(out_pos, (uint32_t)a.k);
 }
 
+// Lane t of a wave holds the count of priority position t (t = 0 first).
+// Returns the position at which the running count first reaches need
+// (1 <= need <= total) and, in *before, the count of the positions ahead of
+// it; every lane gets both.
+__device__ __forceinline__ int wave_threshold64(uint32_t cnt, uint32_t need, uint32_t* before) {
+  const int lane = threadIdx.x & 63;
+  uint32_t inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  const uint64_t m = __ballot(inc >= need);
+  const int p = m ? __ffsll((unsigned long long)m) - 1 : 63;
+  *before = __shfl(inc - cnt, p);
+  return p;
+}
+
 // MAPPED: outputs go through the slot map (their pages are looked up per
 // winner); otherwise the chunk's page-table entries are staged in LDS
 template <int PER, bool MAPPED, int VW>
@@ -445,6 +463,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t tmp[32];
   __shared__ uint32_t before[2];
+  __shared__ uint32_t thr[4];
   __shared__ int pages[MAPPED ? 1 : kSelPages];
   const int r = blockIdx.x;   // rows fastest: every row's early (full) chunks
   const int c = blockIdx.y;   // are dispatched before the empty tails
@@ -470,13 +489,27 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   uint32_t key[PER];
   load_keys<PER, VW>(row, begin, end, key);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
-  {
+  // scan-built histograms: kHistReps replicas of [4096 12-bit | 64 6-bit] bins
+  const uint32_t* hr = a.hist_rep ? a.hist_rep + (size_t)r * kHistReps * kHistWords : nullptr;
+  constexpr int kRepPer = kHistReps * 64 / kBlock;   // replica bins per thread and level
+  static_assert(kRepPer >= 1 && kRepPer * kBlock == kHistReps * 64, "replica bins tile the workgroup");
+  if (hr == nullptr) {
     uint32_t hv[kBins / kBlock];
 #pragma unroll
     for (int m = 0; m < kBins / kBlock; ++m) hv[m] = gh[threadIdx.x + m * kBlock];
     issue_fence();
 #pragma unroll
     for (int m = 0; m < kBins / kBlock; ++m) hist[threadIdx.x + m * kBlock] = hv[m];
+  } else {
+    uint32_t cv[kRepPer];
+#pragma unroll
+    for (int m = 0; m < kRepPer; ++m) {
+      const int e = threadIdx.x + m * kBlock;
+      cv[m] = hr[(e >> 6) * kHistWords + 4096 + (e & 63)];
+    }
+    issue_fence();
+#pragma unroll
+    for (int m = 0; m < kRepPer; ++m) hist[threadIdx.x + m * kBlock] = cv[m];
   }
   bool lds_pages = !MAPPED && a.phys;
   int pg0 = 0, off;
@@ -499,9 +532,55 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   }
   if (threadIdx.x < 2) before[threadIdx.x] = 0u;
   __syncthreads();
-  uint32_t better;
-  const uint32_t digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
-  const uint32_t members = hist[digit];   // of the whole row
+  uint32_t better, digit, members;   // threshold bin of the whole row, count above it, in it
+  if (hr == nullptr) {
+    digit = (uint32_t)find_threshold<kBlock>(hist, (uint32_t)a.k, true, tmp, &better);
+    members = hist[digit];
+  } else {
+    // the 6-bit digit first (one wave, lane t = super-bin 63 - t), then the
+    // 64 12-bit bins inside the threshold super-bin
+    if (threadIdx.x < 64) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int rep = 0; rep < kHistReps; ++rep) c += hist[rep * 64 + 63 - threadIdx.x];
+      uint32_t bs;
+      const int p = wave_threshold64(c, (uint32_t)a.k, &bs);
+      if (threadIdx.x == 0) {
+        thr[0] = 63u - (uint32_t)p;
+        thr[1] = bs;
+      }
+    }
+    __syncthreads();
+    const uint32_t sb = thr[0];
+    uint32_t fv[kRepPer];
+#pragma unroll
+    for (int m = 0; m < kRepPer; ++m) {
+      const int e = threadIdx.x + m * kBlock;
+      fv[m] = hr[(e >> 6) * kHistWords + 64 * sb + (e & 63)];
+    }
+    issue_fence();
+#pragma unroll
+    for (int m = 0; m < kRepPer; ++m) hist[kHistReps * 64 + threadIdx.x + m * kBlock] = fv[m];
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int rep = 0; rep < kHistReps; ++rep) c += hist[kHistReps * 64 + rep * 64 + 63 - threadIdx.x];
+      uint32_t b2;
+      const int p = wave_threshold64(c, (uint32_t)a.k - thr[1], &b2);
+      if (threadIdx.x == (unsigned)p) {
+        thr[2] = 64u * sb + 63u - (uint32_t)p;
+        thr[3] = c;
+      }
+      if (threadIdx.x == 0) before[0] = thr[1] + b2;   // (read below, before being reset)
+    }
+    __syncthreads();
+    digit = thr[2];
+    members = thr[3];
+    better = before[0];
+    __syncthreads();
+    if (threadIdx.x < 2) before[threadIdx.x] = 0u;
+  }
   // better < k <= better + members: every member is kept exactly when
   // members == k - better; with `defer` the members then leave with the
   // winners, and otherwise their slots are left to the attention
@@ -510,7 +589,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
     uint32_t* rec = ws.rec + (size_t)r * 4;
     rec[0] = digit;
     rec[1] = better;
-    rec[2] = hist[digit];
+    rec[2] = members;
   }
   if (a.defer && c == 0) {
     if (threadIdx.x == 0) a.count[r] = a.k;
@@ -520,7 +599,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   // winners and threshold-bin members of the chunks before this one, from
   // their suffix counts (one load pair per earlier chunk)
   // (summed per wave first: LDS atomics on one address serialise per lane)
-  if ((int)(threadIdx.x & ~63u) < c) {
+  if (hr == nullptr && (int)(threadIdx.x & ~63u) < c) {
     uint32_t nw = 0, ne = 0;
     for (int c2 = threadIdx.x; c2 < c; c2 += kBlock) {
       const uint16_t* sf = ws.suf + ((size_t)r * ws.nchunk + c2) * kBins;
@@ -550,6 +629,19 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   }
   uint32_t tot;
   const uint32_t pre = block_excl_scan<kBlock>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot);
+  if (hr != nullptr) {
+    // no per-chunk counts: the chunk's winners and members take their place
+    // in the row's output with one returning atomic (the row's first two
+    // histogram words, cleared by the scan, serve as the counter pair)
+    if (threadIdx.x == 0) {
+      unsigned long long* ctr = reinterpret_cast<unsigned long long*>(ws.hist + (size_t)r * kBins);
+      const unsigned long long old =
+          atomicAdd(ctr, ((unsigned long long)(tot >> 16) << 32) | (unsigned long long)(tot & 0xFFFFu));
+      before[0] = (uint32_t)old;
+      before[1] = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+  }
   uint32_t ow = before[0] + (pre & 0xFFFF);
   uint32_t oc = before[1] + (pre >> 16);
   // threshold-bin members first (their keys are then dead), then the
@@ -558,9 +650,27 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   int2* cand = ws.cand + (size_t)r * a.max_len;
   uint32_t om = better + oc;        // output slot of this workgroup's first member
   if (!members_out) {
+    int32_t* crow = ws.crow + (size_t)r * a.max_len;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if ((eq >> j) & 1u) cand[oc++] = make_int2(chunk_pos<VW>(begin, j), (int)key[j]);
+    for (int j = 0; j < PER; ++j) {
+      if ((eq >> j) & 1u) {
+        const int pos = chunk_pos<VW>(begin, j);
+        if (a.defer) {
+          // the member's physical row, for the attention that resolves it
+          int row;
+          if (lds_pages) {
+            int pg, po;
+            split_pos(pos, a.page_size, pg, po);
+            const int page = pages[pg - pg0];
+            row = (unsigned)page < (unsigned)a.num_pages ? page * a.page_size + po : -1;
+          } else {
+            row = phys_of(a, r, pos);
+          }
+          crow[oc] = row;
+        }
+        cand[oc++] = make_int2(pos, (int)key[j]);
+      }
+    }
   }
   // the members' next 12 key bits go into the row's second histogram, so the
   // refinement starts from it: counted in LDS first (the level-1 histogram
@@ -939,14 +1049,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
 
 size_t topk_ws_bytes(int num_req, int max_len) {
   const size_t R = (size_t)num_req;
-  return align_up(2 * R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (3 * R * max_len + 4 * R) * 4, 256);
+  return align_up(2 * R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (4 * R * max_len + 4 * R) * 4, 256);
 }
 
 int64_t topk_zero_words(int num_req) { return (int64_t)num_req * 2 * kBins; }
 
 hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t s) {
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, kBlock * 4), 1024));
-  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(kBlock), 0, s, p, n);
+  launch(zero_kernel, dim3(blocks), dim3(kBlock), 0, s, "zero_kernel", p, n);
   return hipGetLastError();
 }
 
@@ -955,9 +1065,9 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   // row is enough parallelism and needs no hand-over between workgroups
   if (a.num_req >= num_cus() || a.max_len <= 32768) {
     if (a.map != nullptr || a.phys != nullptr)
-      hipLaunchKernelGGL((topk_row_kernel<1, true>), dim3(a.num_req), dim3(kRowThreads), 0, s, a);
+      launch((topk_row_kernel<1, true>), dim3(a.num_req), dim3(kRowThreads), 0, s, "topk_row_kernel", a);
     else
-      hipLaunchKernelGGL((topk_row_kernel<1, false>), dim3(a.num_req), dim3(kRowThreads), 0, s, a);
+      launch((topk_row_kernel<1, false>), dim3(a.num_req), dim3(kRowThreads), 0, s, "topk_row_kernel", a);
     return hipGetLastError();
   }
   if (ws_state == 0) {
@@ -978,9 +1088,11 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   switch (per * (vec ? 1 : -1)) {
 #define LSI_TOPK_PER(P, VW)                                                                           \
   case (VW == 1 ? -P : P):                                                                            \
-    hipLaunchKernelGGL((topk_hist_kernel<P, VW>), grid, dim3(kBlock), 0, s, a);                       \
-    if (mapped) hipLaunchKernelGGL((topk_select_kernel<P, true, VW>), grid, dim3(kBlock), 0, s, a);   \
-    else hipLaunchKernelGGL((topk_select_kernel<P, false, VW>), grid, dim3(kBlock), 0, s, a);         \
+    if (a.hist_rep == nullptr) {                                                                      \
+      launch((topk_hist_kernel<P, VW>), grid, dim3(kBlock), 0, s, "topk_hist_kernel", a);                                                               \
+    }                                                                                                 \
+    if (mapped) launch((topk_select_kernel<P, true, VW>), grid, dim3(kBlock), 0, s, "topk_select_kernel", a); \
+    else launch((topk_select_kernel<P, false, VW>), grid, dim3(kBlock), 0, s, "topk_select_kernel", a);                                                               \
     break;
     LSI_TOPK_PER(2, 2)
     LSI_TOPK_PER(4, 4)
@@ -993,7 +1105,9 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
 #undef LSI_TOPK_PER
     default: return hipErrorInvalidValue;
   }
-  if (!a.defer) hipLaunchKernelGGL(topk_refine_kernel, dim3(a.num_req), dim3(kRefThreads), 0, s, a);
+  if (!a.defer) {
+    launch(topk_refine_kernel, dim3(a.num_req), dim3(kRefThreads), 0, s, "topk_refine_kernel", a);
+  }
   return hipGetLastError();
 }
 

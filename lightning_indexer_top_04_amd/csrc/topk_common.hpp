@@ -21,10 +21,13 @@ struct Ws {
   int2* cand;        // [R][max_len] threshold-bin members (slot, key), in chunk order
   int32_t* list;     // [R][max_len] their slots, compacted (when too many for LDS)
   uint32_t* rec;     // [R][4] threshold bin, count above it, count in it
+  int32_t* crow;     // [R][max_len] physical row of each candidate (deferred selections only)
   int nchunk;        // chunks per row at the smallest chunk size
 };
 
-__host__ __device__ inline int max_chunks(int max_len) { return (max_len + kMinChunk - 1) / kMinChunk; }
+__host__ __device__ inline int max_chunks(int max_len) {
+  return (int)(((int64_t)max_len + kMinChunk - 1) / kMinChunk);
+}
 
 __host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   Ws w;
@@ -35,6 +38,7 @@ __host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   w.cand = reinterpret_cast<int2*>(w.suf + (size_t)R * w.nchunk * kBins);
   w.list = reinterpret_cast<int32_t*>(w.cand + (size_t)R * max_len);
   w.rec = reinterpret_cast<uint32_t*>(w.list + (size_t)R * max_len);
+  w.crow = reinterpret_cast<int32_t*>(w.rec + (size_t)R * 4);
   return w;
 }
 
@@ -120,8 +124,9 @@ __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uin
 // third, then, among exact ties, the lowest positions: the same set as the
 // one-workgroup refinement keeps.  The i-th kept member takes output slot
 // better + i.  Every workgroup that calls this computes the same thresholds
-// and the same order; put(slot, position) is called for the slots in
-// [lo, hi).  NT threads; hist (kBins words) and tmp (32 words) are LDS.
+// and the same order; put(slot, position, physical row) is called for the
+// slots in [lo, hi).  NT threads; hist (kBins words) and tmp (32 words) are
+// LDS.
 // ---------------------------------------------------------------------------
 template <int NT, class Put>
 __device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_t* hist, uint32_t* tmp,
@@ -132,8 +137,19 @@ __device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_
   const uint32_t better = rec[1];
   const uint32_t members = rec[2];
   const int2* cand = ws.cand + (size_t)r * max_len;
+  const int32_t* crow = ws.crow + (size_t)r * max_len;
   const uint32_t* g2 = ws.h2 + (size_t)r * kBins;
   const uint32_t need = (uint32_t)k - better;
+  // the first batch of candidates (and their rows) comes in with the
+  // second histogram: one round trip for both
+  int2 e0[E];
+  int32_t w0[E];
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    const uint32_t i = tid * E + u;
+    e0[u] = i < members ? cand[i] : make_int2(-1, 0);
+    w0[u] = i < members ? crow[i] : -1;
+  }
   // f(pos, key) over every candidate, E consecutive ones per thread
   auto pass = [&](auto&& f) {
     for (uint32_t base = 0; base < members; base += NT * E) {
@@ -148,8 +164,16 @@ __device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_
         if (e[u].x >= 0) f(e[u].x, (uint32_t)e[u].y);
     }
   };
-  // level 2: key bits [19:8], histogram built by the select
-  for (int i = tid; i < kBins; i += NT) hist[i] = g2[i];
+  // level 2: key bits [19:8], histogram built by the select (every load
+  // issued before the first LDS store: one round trip, not one per load)
+  {
+    uint32_t hv[kBins / NT];
+#pragma unroll
+    for (int m = 0; m < kBins / NT; ++m) hv[m] = g2[tid + m * NT];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < kBins / NT; ++m) hist[tid + m * NT] = hv[m];
+  }
   __syncthreads();
   uint32_t better2;
   const uint32_t bin2 = (uint32_t)find_threshold<NT>(hist, need, true, tmp, &better2);
@@ -209,19 +233,28 @@ __device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_
   uint32_t run = 0;
   for (uint32_t base = 0; base < members && better + run < (uint32_t)hi; base += NT * E) {
     int2 e[E];
+    int32_t rw[E];
     uint32_t m = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       const uint32_t i = base + tid * E + u;
-      e[u] = i < members ? cand[i] : make_int2(-1, 0);
-      if (e[u].x >= 0 && kept(e[u].x, (uint32_t)e[u].y)) m |= 1u << u;
+      if (base == 0) {
+        e[u] = e0[u];
+        rw[u] = w0[u];
+      } else {
+        e[u] = i < members ? cand[i] : make_int2(-1, 0);
+        rw[u] = i < members ? crow[i] : -1;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < E; ++u)
+      if (e[u].x >= 0 && kept(e[u].x, (uint32_t)e[u].y)) m |= 1u << u;
     uint32_t tot;
     uint32_t o = run + block_excl_scan<NT>((uint32_t)__popc(m), tmp, &tot) + better;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       if ((m >> u) & 1u) {
-        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, e[u].x);
+        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, e[u].x, rw[u]);
         ++o;
       }
     }

@@ -25,11 +25,13 @@ DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int4": INT4}
 EXPORTS = [
     "lsi_index_scores", "lsi_topk_workspace_bytes", "lsi_topk",
     "lsi_sparse_mla_workspace_bytes", "lsi_sparse_mla_decode",
-    "lsi_decode_step_workspace_bytes", "lsi_decode_step", "lsi_decode_step_noalloc",
+    "lsi_decode_step_state_bytes", "lsi_decode_step_workspace_bytes", "lsi_decode_step",
+    "lsi_decode_step_noalloc",
     "lsi_multilayer_workspace_bytes", "lsi_multilayer_decode",
     "lsi_two_stage_workspace_bytes", "lsi_two_stage_topk",
     "lsi_prefill_workspace_bytes", "lsi_prefill_index_topk",
-    "lsi_status_string", "lsi_last_error", "lsi_version",
+    "lsi_workspace_bytes", "lsi_profile_events",
+    "lsi_status_string", "lsi_last_error_detail", "lsi_last_error", "lsi_version",
 ]
 
 
@@ -66,6 +68,7 @@ _SIGS = {
     "lsi_topk": (_I, [_P, _L, _PB, _I, _P, _P, _P, _S, _P]),
     "lsi_sparse_mla_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "lsi_sparse_mla_decode": (_I, [_PC, _PC, _PB, _P, _I, _I, _I, _P, _I, _F, _P, _P, _P, _S, _P]),
+    "lsi_decode_step_state_bytes": (_S, [_I]),
     "lsi_decode_step_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "lsi_decode_step": (_I, [_PC, _PC, _PC, _PB, _P, _I, _I, _P, _P, _I, _I, _I, _F, _I,
                              _P, _P, _P, _P, _P, _S, _P]),
@@ -79,7 +82,10 @@ _SIGS = {
     "lsi_prefill_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "lsi_prefill_index_topk": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _P, _I, _I, _P, _P,
                                     _P, _P, _S, _P, _P]),
+    "lsi_workspace_bytes": (_S, [_I, C.c_void_p]),
+    "lsi_profile_events": (_I, [C.c_void_p, C.c_void_p, _I]),
     "lsi_status_string": (C.c_char_p, [_I]),
+    "lsi_last_error_detail": (C.c_char_p, []),
     "lsi_last_error": (C.c_char_p, []),
     "lsi_version": (_I, []),
 }
@@ -105,8 +111,53 @@ def lib():
 
 def _check(status: int, what: str):
     if status != OK:
-        detail = lib().lsi_last_error().decode()
+        detail = lib().lsi_last_error_detail().decode()
         raise LsiError(status, what, detail)
+
+
+class WsQuery(C.Structure):
+    _fields_ = [("num_req", C.c_int32), ("max_seq_len", C.c_int32), ("k", C.c_int32),
+                ("n_heads", C.c_int32), ("dv", C.c_int32), ("n_cand", C.c_int32),
+                ("dim", C.c_int32), ("block_tokens", C.c_int32), ("scores_external", C.c_int32)]
+
+
+OP_TOPK, OP_SPARSE_MLA, OP_DECODE_STEP, OP_MULTILAYER, OP_TWO_STAGE, OP_PREFILL = 1, 2, 3, 4, 5, 6
+
+
+def workspace_bytes(op: int, **fields) -> int:
+    """lsi_workspace_bytes(op, query) with the query's fields by name."""
+    q = WsQuery(**fields)
+    return int(lib().lsi_workspace_bytes(op, C.byref(q)))
+
+
+class KernelTimer:
+    """lsi_profile_events around a block of calls: afterwards `intervals()`
+    lists (kernel name, milliseconds) for every kernel the library launched
+    in between, each timed by a start/stop event pair carried by its own
+    dispatch."""
+
+    def __init__(self, capacity: int = 4096):
+        capacity -= capacity % 2
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.events:          # create the underlying events
+            e.record()
+        torch.cuda.synchronize()
+        self._ev = (C.c_void_p * capacity)(*[e.cuda_event for e in self.events])
+        self._names = (C.c_char_p * (capacity // 2))()
+        self.n = 0
+
+    def __enter__(self):
+        lib().lsi_profile_events(self._ev, self._names, len(self.events))
+        return self
+
+    def __exit__(self, *exc):
+        self.n = lib().lsi_profile_events(None, None, 0)
+        return False
+
+    def intervals(self):
+        torch.cuda.synchronize()
+        return [(self._names[i].decode(), self.events[2 * i].elapsed_time(self.events[2 * i + 1]))
+                for i in range(self.n // 2)]
 
 
 def _ptr(t):
@@ -205,6 +256,13 @@ def decode_step_workspace_bytes(B, max_seq_len, k, n_heads, dv) -> int:
     return int(lib().lsi_decode_step_workspace_bytes(B, max_seq_len, k, n_heads, dv))
 
 
+def decode_step_workspace(B, max_seq_len, k, n_heads, dv, device) -> torch.Tensor:
+    """A workspace for lsi_decode_step: zero-filled, as its leading state
+    words must be on first use (each successful call leaves them zero)."""
+    return torch.zeros(max(decode_step_workspace_bytes(B, max_seq_len, k, n_heads, dv), 1),
+                       dtype=torch.uint8, device=device)
+
+
 def decode_step(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests, q_idx: torch.Tensor,
                 w: torch.Tensor, q_attn: torch.Tensor, k: int, sm_scale: float, dv: int,
                 out=None, lse=None, idx=None, count=None, ws=None, stream=None):
@@ -215,9 +273,8 @@ def decode_step(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests, q_idx: 
     count = torch.empty(B, dtype=torch.int32, device=dev) if count is None else count
     out = torch.empty(B, H, dv, dtype=q_attn.dtype, device=dev) if out is None else out
     lse = torch.empty(B, H, dtype=torch.float32, device=dev) if lse is None else lse
-    nb = decode_step_workspace_bytes(B, req.max_seq_len, k, H, dv)
     if ws is None:
-        ws = _ws(nb, dev)
+        ws = decode_step_workspace(B, req.max_seq_len, k, H, dv, dev)
     _check(lib().lsi_decode_step(ikeys.ref, kv.ref, None if v is None else v.ref, req.ref,
                                  _ptr(q_idx), HI, dI, _ptr(w), _ptr(q_attn), H, dk, dv, sm_scale,
                                  k, _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _ptr(ws),

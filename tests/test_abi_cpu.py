@@ -142,8 +142,9 @@ def test_multilayer_validation(L):
                                 for _ in range(n)])
     arr = lambda base, m=n: (C.c_void_p * m)(*[base + 0x100 * i for i in range(m)])
     need = L.lsi_multilayer_workspace_bytes(1, 256, 64, 128, 512)
-    # two buffers of selection rows: larger than one layer's step
-    assert need > L.lsi_decode_step_workspace_bytes(1, 256, 64, 128, 512)
+    # two buffers of selection rows: larger than one layer's step scratch
+    assert need > (L.lsi_decode_step_workspace_bytes(1, 256, 64, 128, 512)
+                   - L.lsi_decode_step_state_bytes(1))
 
     def call(n_layers=n, r=1, sched=lsi.SCHED_MLI, ikeys=ik, kvs=kv, idx=None, ws=0x100000,
              nb=need, q_idx=None):
@@ -196,3 +197,43 @@ def test_decode_step_noalloc_validation(L):
     assert L.lsi_decode_step_workspace_bytes(64, 300000, 2048, 128, 512) > lsi.NOALLOC_SCRATCH_BYTES
     assert call(big) == lsi.ERR_WORKSPACE
     assert b"scratch" in L.lsi_last_error()
+
+
+def test_host_validation_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The library's host code (argument validation, workspace sizing, error
+    strings) built with AddressSanitizer and UndefinedBehaviorSanitizer on the
+    host side only, driven by tests/abi_sanitize_driver.cpp: every entry point
+    with arguments it must reject before touching HIP, every size query with
+    ordinary and extreme shapes.  No GPU is used."""
+    import shutil
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    csrc = os.path.join(ROOT, "lightning_indexer_top_04_amd", "csrc")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+    objs, procs = [], []
+    for src in ("api.hip", "scan.hip", "topk.hip", "attn.hip", "prefill.hip"):
+        o = str(tmp_path / src.replace(".hip", ".o"))
+        procs.append(subprocess.Popen([hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
+                                       "-munsafe-fp-atomics", "-Wno-unused-result", *san, "-c",
+                                       os.path.join(csrc, src), "-o", o],
+                                      stdout=subprocess.PIPE, stderr=subprocess.PIPE))
+        objs.append(o)
+    drv = str(tmp_path / "drv.o")
+    procs.append(subprocess.Popen([hipcc, "-O1", "-g", "-std=c++17", "-x", "c++", *san, "-D__HIP_PLATFORM_AMD__",
+                                   "-I/opt/rocm/include", "-c",
+                                   os.path.join(ROOT, "tests", "abi_sanitize_driver.cpp"), "-o", drv],
+                                  stdout=subprocess.PIPE, stderr=subprocess.PIPE))
+    for p in procs:
+        _, err = p.communicate()
+        assert p.returncode == 0, err.decode()[-2000:]
+    exe = str(tmp_path / "abi_sanitize")
+    r = subprocess.run([hipcc, "--offload-arch=gfx950", *san, drv, *objs, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
+    assert "sanitized ABI checks passed" in r.stdout
+    shutil.rmtree(tmp_path, ignore_errors=True)

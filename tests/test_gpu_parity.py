@@ -496,18 +496,20 @@ def test_decode_step_unplanted():
     print(_check_step(di, 2048))
 
 
-def test_decode_step_graph_replays_match_eager():
+@pytest.mark.parametrize("lens", [(9000, 3000, 700), (70001,)])
+def test_decode_step_graph_replays_match_eager(lens):
     """The fused step captured in a HIP graph: every replay (with eager work
-    and synchronisations in between) reproduces the eager result."""
-    di = small_dsa([9000, 3000, 700], k=2048)
+    and synchronisations in between) reproduces the eager result.  One long
+    request takes the path whose scan builds the top-k histograms in the
+    workspace's state words, which every call must leave cleared."""
+    di = small_dsa(list(lens), k=2048)
     ik, req, kv, _ = objs(di)
-    B, k, H, dv = 3, 2048, 128, 512
+    B, k, H, dv = len(lens), 2048, 128, 512
     idx = torch.empty(B, k, dtype=torch.int32, device=DEV)
     cnt = torch.empty(B, dtype=torch.int32, device=DEV)
     out = torch.empty(B, H, dv, dtype=torch.bfloat16, device=DEV)
     lse = torch.empty(B, H, dtype=torch.float32, device=DEV)
-    ws = torch.empty(lsi.decode_step_workspace_bytes(B, req.max_seq_len, k, H, dv),
-                     dtype=torch.uint8, device=DEV)
+    ws = lsi.decode_step_workspace(B, req.max_seq_len, k, H, dv, DEV)
 
     def run():
         lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, k, di.wl.sm_scale, dv,
@@ -540,6 +542,8 @@ def test_decode_step_graph_replays_match_eager():
             check_attention(out[b].float().cpu().numpy(), e_out[b].cpu().numpy().astype(np.float64),
                             f"replay {rep} req {b}")
         assert torch.allclose(lse, e_lse, rtol=1e-5, atol=1e-5), rep
+    st = lsi.lib().lsi_decode_step_state_bytes(B)
+    assert torch.count_nonzero(ws[:st]).item() == 0
 
 
 # ----------------------------------------------------------------------------
