@@ -531,6 +531,8 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
         out["prefill_t4096_h65536"] = {
             "queries": T, "pairs": pairs, "ms_history_from_pinned_host": t_host,
             "ms_history_on_device": t_dev,
+            "workspace_bytes": int(lsi.workspace_bytes(lsi.OP_PREFILL, num_req=T, max_seq_len=Hh,
+                                                       k=2048, dim=128, block_tokens=8192)),
             "roofline": {"bound": "mfma", "useful_flops": flops, "dtype": "bf16",
                          "achieved_TFLOP_s": flops / (t_dev * 1e-3) / 1e12, "peak": 2500.0,
                          "frac": flops / (t_dev * 1e-3) / 1e12 / 2500.0,

@@ -810,14 +810,14 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
 
 size_t lsi_prefill_workspace_bytes(int32_t hist_len, int32_t T, int32_t dim, int32_t block_tokens,
                                    int32_t k, int32_t scores_external) {
-  (void)k;
-  if (hist_len < 0 || T < 1 || dim < 1 || block_tokens < 1) return 0;
-  const int64_t ld = (int64_t)hist_len + T;
+  (void)hist_len;
+  (void)scores_external;   // the scores are never stored in the workspace
+  if (hist_len < 0 || T < 1 || dim < 1 || block_tokens < 1 || k < 1 || k > 65536) return 0;
   const size_t bufk = align_up((size_t)block_tokens * dim, kWsAlign);
   const size_t bufs = align_up((size_t)block_tokens * 4, kWsAlign);
-  const size_t sc = scores_external ? 0 : align_up((size_t)T * ld * 4, kWsAlign);
-  const size_t rg = align_up((size_t)T * 8, kWsAlign);
-  return 2 * (bufk + bufs) + sc + rg + topk_ws_bytes(T, (int)ld);
+  const size_t cand = align_up((size_t)T * prefill_cand_cap(k) * 8, kWsAlign);
+  const size_t state = align_up((size_t)T * 8, kWsAlign);
+  return 2 * (bufk + bufs) + cand + state;
 }
 
 int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale, int32_t hist_len,
@@ -851,14 +851,10 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
     bufs[i] = reinterpret_cast<float*>(ws);
     ws += align_up((size_t)block_tokens * 4, kWsAlign);
   }
-  float* sc = scores;
-  if (!sc) {
-    sc = reinterpret_cast<float*>(ws);
-    ws += align_up((size_t)T * ld * 4, kWsAlign);
-  }
-  uint32_t* range = reinterpret_cast<uint32_t*>(ws);   // [T][2] key range of each row
-  ws += align_up((size_t)T * 8, kWsAlign);
-  void* tws = ws;
+  const int cap = prefill_cand_cap(k);
+  uint2* cand = reinterpret_cast<uint2*>(ws);          // [T][cap] running candidates
+  ws += align_up((size_t)T * cap * 8, kWsAlign);
+  uint32_t* state = reinterpret_cast<uint32_t*>(ws);   // [T][2] count, entry threshold
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
@@ -881,7 +877,7 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
     if (_e != hipSuccess)                                                                 \
       return fail(LSI_ERR_HIP, std::string("lsi_prefill_index_topk: ") + hipGetErrorString(_e)); \
   } while (0)
-  LSI_HIP(launch_zero(range, 2 * (int64_t)T, s_compute));
+  LSI_HIP(launch_zero(state, 2 * (int64_t)T, s_compute));
   // the copy stream must not overwrite buffers a previous call still reads
   LSI_HIP(hipEventRecord(ev.start, s_compute));
   LSI_HIP(hipStreamWaitEvent(s_copy, ev.start, 0));
@@ -890,9 +886,14 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   pa.w = w;
   pa.T = T;
   pa.hist_len = hist_len;
-  pa.scores = sc;
+  pa.scores = scores;
   pa.ld = ld;
-  pa.range = range;
+  pa.cand = cand;
+  pa.state = state;
+  pa.cap = cap;
+  pa.k = k;
+  pa.idx = idx;
+  pa.count = count;
   const int nblk = (int)ceil_div(hist_len, block_tokens);
   for (int blk = 0; blk < nblk; ++blk) {
     const int j = blk & 1;
@@ -914,20 +915,8 @@ int32_t lsi_prefill_index_topk(const uint8_t* hist_keys, const float* hist_scale
   pa.kscale = chunk_scale;
   pa.tok0 = hist_len;
   pa.n_tok = T;
+  pa.final_block = 1;   // the chunk's own keys come last: selection written here
   LSI_HIP(launch_prefill_scan(pa, s_compute));
-
-  TopkArgs t;
-  t.scores = sc;
-  t.ld = ld;
-  t.causal_base = hist_len;
-  t.range = range;
-  t.num_req = T;
-  t.max_len = (int)ld;
-  t.k = k;
-  t.idx = idx;
-  t.count = count;
-  t.ws = tws;
-  LSI_HIP(launch_topk(t, 0, s_compute));
 #undef LSI_HIP
   return check_launch("lsi_prefill_index_topk");
 }

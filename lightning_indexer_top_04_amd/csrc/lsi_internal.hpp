@@ -141,12 +141,21 @@ struct PrefillScanArgs {
   const float* w = nullptr;        // [T][64]
   int T = 0;
   int hist_len = 0;                // query i sits at hist_len + i
-  float* scores = nullptr;         // [T][ld]
+  float* scores = nullptr;         // optional [T][ld]: every visible score as well
   int64_t ld = 0;
-  // optional [T][2]: per query row, atomic maxima of ~key and key over the
-  // scores written (zero before the first block), i.e. the row's key range
-  uint32_t* range = nullptr;
+  // the running selection: per query a candidate buffer [T][cap] of (score
+  // key, position) and a state [T][2] (count, entry threshold key; zero
+  // before the first block); the last block writes idx [T][k] and count [T]
+  uint2* cand = nullptr;
+  uint32_t* state = nullptr;
+  int cap = 0;
+  int k = 0;
+  int final_block = 0;
+  int32_t* idx = nullptr;
+  int32_t* count = nullptr;
 };
+// candidate capacity per query for a selection of k (>= 2k + 8 tiles of 64)
+inline int prefill_cand_cap(int k) { return (int)(((int64_t)2 * k + 512 + 63) / 64 * 64); }
 hipError_t launch_prefill_scan(const PrefillScanArgs& a, hipStream_t s);
 
 }  // namespace lsi

@@ -7,6 +7,7 @@ LsiError is raised if it is missing or a call fails; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 
@@ -213,6 +214,13 @@ def _ws(nbytes: int, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _on(stream):
+    """Allocate on the stream the library will use: the caching allocator
+    then orders the reuse of these buffers after that stream's work, also
+    when it is not the current stream."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 # ----------------------------------------------------------------------------
 # Entry points
 # ----------------------------------------------------------------------------
@@ -221,7 +229,8 @@ def index_scores(ikeys: Cache, req: Requests, q: torch.Tensor, w: torch.Tensor,
                  scores: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     B, H, d = q.shape
     if scores is None:
-        scores = torch.empty(B, max(req.max_seq_len, 1), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            scores = torch.empty(B, max(req.max_seq_len, 1), dtype=torch.float32, device=q.device)
     _check(lib().lsi_index_scores(ikeys.ref, req.ref, _ptr(q), H, d, _ptr(w), _ptr(scores),
                                   scores.stride(0), _stream(stream)), "lsi_index_scores")
     return scores
@@ -229,10 +238,11 @@ def index_scores(ikeys: Cache, req: Requests, q: torch.Tensor, w: torch.Tensor,
 
 def topk(scores: torch.Tensor, req: Requests, k: int, stream=None):
     B = req.num_req
-    idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
-    cnt = torch.empty(B, dtype=torch.int32, device=scores.device)
     nb = lib().lsi_topk_workspace_bytes(B, req.max_seq_len, k)
-    ws = _ws(nb, scores.device)
+    with _on(stream):
+        idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
+        cnt = torch.empty(B, dtype=torch.int32, device=scores.device)
+        ws = _ws(nb, scores.device)
     _check(lib().lsi_topk(_ptr(scores), scores.stride(0), req.ref, k, _ptr(idx), _ptr(cnt),
                           _ptr(ws), nb, _stream(stream)), "lsi_topk")
     return idx, cnt
@@ -242,10 +252,11 @@ def sparse_mla_decode(kv: Cache, v: Cache | None, req: Requests, q: torch.Tensor
                       idx: torch.Tensor, sm_scale: float, dv: int, stream=None):
     B, H, dk = q.shape
     k = idx.shape[1]
-    out = torch.empty(B, H, dv, dtype=q.dtype, device=q.device)
-    lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
     nb = lib().lsi_sparse_mla_workspace_bytes(B, H, dv, k)
-    ws = _ws(nb, q.device)
+    with _on(stream):
+        out = torch.empty(B, H, dv, dtype=q.dtype, device=q.device)
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+        ws = _ws(nb, q.device)
     _check(lib().lsi_sparse_mla_decode(kv.ref, None if v is None else v.ref, req.ref, _ptr(q),
                                        H, dk, dv, _ptr(idx), k, sm_scale, _ptr(out), _ptr(lse),
                                        _ptr(ws), nb, _stream(stream)), "lsi_sparse_mla_decode")
@@ -269,12 +280,13 @@ def decode_step(ikeys: Cache, kv: Cache, v: Cache | None, req: Requests, q_idx: 
     B, HI, dI = q_idx.shape
     _, H, dk = q_attn.shape
     dev = q_attn.device
-    idx = torch.empty(B, k, dtype=torch.int32, device=dev) if idx is None else idx
-    count = torch.empty(B, dtype=torch.int32, device=dev) if count is None else count
-    out = torch.empty(B, H, dv, dtype=q_attn.dtype, device=dev) if out is None else out
-    lse = torch.empty(B, H, dtype=torch.float32, device=dev) if lse is None else lse
-    if ws is None:
-        ws = decode_step_workspace(B, req.max_seq_len, k, H, dv, dev)
+    with _on(stream):
+        idx = torch.empty(B, k, dtype=torch.int32, device=dev) if idx is None else idx
+        count = torch.empty(B, dtype=torch.int32, device=dev) if count is None else count
+        out = torch.empty(B, H, dv, dtype=q_attn.dtype, device=dev) if out is None else out
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev) if lse is None else lse
+        if ws is None:
+            ws = decode_step_workspace(B, req.max_seq_len, k, H, dv, dev)
     _check(lib().lsi_decode_step(ikeys.ref, kv.ref, None if v is None else v.ref, req.ref,
                                  _ptr(q_idx), HI, dI, _ptr(w), _ptr(q_attn), H, dk, dv, sm_scale,
                                  k, _ptr(idx), _ptr(count), _ptr(out), _ptr(lse), _ptr(ws),
@@ -360,11 +372,12 @@ def two_stage_topk(ikeys4: Cache, ikeys8: Cache, req: Requests, q: torch.Tensor,
                    w: torch.Tensor, n_cand: int, k: int, want_cand: bool = False, stream=None):
     B, H, d = q.shape
     dev = q.device
-    idx = torch.empty(B, k, dtype=torch.int32, device=dev)
-    cnt = torch.empty(B, dtype=torch.int32, device=dev)
-    cand = torch.empty(B, n_cand, dtype=torch.int32, device=dev) if want_cand else None
     nb = lib().lsi_two_stage_workspace_bytes(B, req.max_seq_len, n_cand, k)
-    ws = _ws(nb, dev)
+    with _on(stream):
+        idx = torch.empty(B, k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, dtype=torch.int32, device=dev)
+        cand = torch.empty(B, n_cand, dtype=torch.int32, device=dev) if want_cand else None
+        ws = _ws(nb, dev)
     _check(lib().lsi_two_stage_topk(ikeys4.ref, ikeys8.ref, req.ref, _ptr(q), H, d, _ptr(w),
                                     n_cand, k, _ptr(idx), _ptr(cnt), _ptr(cand), _ptr(ws), nb,
                                     _stream(stream)), "lsi_two_stage_topk")
@@ -378,13 +391,14 @@ def prefill_index_topk(hist_keys: torch.Tensor, hist_scale: torch.Tensor,
     T, H, d = q.shape
     hist_len = hist_keys.shape[0]
     dev = q.device
-    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
-    cnt = torch.empty(T, dtype=torch.int32, device=dev)
-    scores = (torch.empty(T, hist_len + T, dtype=torch.float32, device=dev)
-              if want_scores else None)
     nb = lib().lsi_prefill_workspace_bytes(hist_len, T, d, block_tokens, k,
                                            1 if want_scores else 0)
-    ws = _ws(nb, dev)
+    with _on(stream):
+        idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(T, dtype=torch.int32, device=dev)
+        scores = (torch.empty(T, hist_len + T, dtype=torch.float32, device=dev)
+                  if want_scores else None)
+        ws = _ws(nb, dev)
     s_comp = _stream(stream)
     s_copy = _stream(copy_stream) if copy_stream is not None else s_comp
     _check(lib().lsi_prefill_index_topk(_ptr(hist_keys), _ptr(hist_scale), hist_len,

@@ -57,6 +57,17 @@ def check_topk(gpu_idx, gpu_count, ref_scores, k, what=""):
     return {"band": int(bnd.size), "diff": int(diff.size)}
 
 
+def exact_topk_f32(scores, k):
+    """Positions of the k best of float32 scores (fewer when there are fewer),
+    ranked as the kernels rank them: by the order-preserving integer key of
+    the float (so -0 < +0), equal keys by position ascending.  Sorted."""
+    s = np.ascontiguousarray(np.asarray(scores, dtype=np.float32))
+    b = s.view(np.uint32).astype(np.uint64)
+    key = np.where(b >> 31 == 1, b ^ 0xFFFFFFFF, b | 0x80000000)
+    order = np.lexsort((np.arange(s.size), -key.astype(np.int64)))
+    return np.sort(order[:min(k, s.size)])
+
+
 def check_attention(out, ref, what=""):
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

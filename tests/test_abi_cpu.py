@@ -111,6 +111,23 @@ def test_attention_validation(L):
     assert call(kf, H=8, dk=64, dv=64) == lsi.ERR_INVALID_ARG   # f32 needs a value cache
 
 
+def test_prefill_workspace_is_linear_in_queries_times_k(L):
+    """The prefill selection keeps a candidate buffer of 2k + 512 (rounded up
+    to 64) entries of 8 bytes per query and no score matrix: 4096 queries
+    over 65536 history tokens with k = 2048 and 8192-token copy blocks need
+    about 151 MB, whatever the history length."""
+    a = L.lsi_prefill_workspace_bytes(65536, 4096, 128, 8192, 2048, 0)
+    assert 0 < a <= 160_000_000, a
+    assert a == L.lsi_prefill_workspace_bytes(1 << 20, 4096, 128, 8192, 2048, 0)
+    assert a == L.lsi_prefill_workspace_bytes(65536, 4096, 128, 8192, 2048, 1)
+    cap = (2 * 2048 + 512 + 63) // 64 * 64
+    assert a >= 4096 * cap * 8
+    assert L.lsi_prefill_workspace_bytes(65536, 4096, 128, 8192, 4096, 0) > a
+    assert L.lsi_prefill_workspace_bytes(65536, 4096, 128, 8192, 0, 0) == 0
+    q = lsi.WsQuery(num_req=4096, max_seq_len=65536, k=2048, dim=128, block_tokens=8192)
+    assert L.lsi_workspace_bytes(lsi.OP_PREFILL, C.byref(q)) == a
+
+
 def test_prefill_and_two_stage_validation(L):
     assert L.lsi_prefill_index_topk(None, None, 10, 0x1000, 0x2000, 4, 0x3000, 64, 128,
                                     0x4000, 16, 32, 0x5000, 0x6000, None, 0x100000, 1 << 30,

@@ -606,3 +606,29 @@ def test_decode_step_threshold_bin_resolved_by_attention(case):
         ro, _ = ov.attention(b, idx_h[b, :n])
         st.update(check_attention(out[b].float().cpu().numpy(), ro, f"{case} attn {b}"))
         print(case, b, st)
+
+
+def test_calls_on_a_side_stream_match_the_current_stream():
+    """Entry points given a stream that is not the current one allocate their
+    outputs and scratch on that stream and give the same results."""
+    di = small_dsa([9000, 40000], k=2048)
+    ik, req, kv, _ = objs(di)
+    ref = lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, 2048, di.wl.sm_scale, 512)
+    ref_sc = lsi.index_scores(ik, req, di.q_idx, di.w)
+    ref_tk = lsi.topk(ref_sc, req, 2048)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    got = lsi.decode_step(ik, kv, None, req, di.q_idx, di.w, di.q_attn, 2048, di.wl.sm_scale, 512,
+                          stream=s)
+    sc = lsi.index_scores(ik, req, di.q_idx, di.w, stream=s)
+    tk = lsi.topk(sc, req, 2048, stream=s)
+    s.synchronize()
+    for b, n in enumerate((9000, 40000)):   # positions past a row's length are not written
+        assert torch.equal(sc[b, :n], ref_sc[b, :n])
+    assert torch.equal(got[1], ref[1]) and torch.equal(tk[1], ref_tk[1])
+    assert torch.equal(torch.sort(got[0], 1).values, torch.sort(ref[0], 1).values)
+    assert torch.equal(torch.sort(tk[0], 1).values, torch.sort(ref_tk[0], 1).values)
+    for b in range(2):
+        check_attention(got[2][b].float().cpu().numpy(), ref[2][b].float().cpu().numpy().astype(np.float64),
+                        f"side stream {b}")
