@@ -301,15 +301,15 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4,
  *              pinned host memory (or device memory).
  *   chunk_keys [T][dim] uint8, chunk_scale [T] float: device.
  *   q [T][n_heads][dim] bf16 (n_heads 64, dim 128), w [T][n_heads] float.
- *   idx [T][k] int32 positions (the k best in no particular order, then -1
- *   padding), count [T] int32 = min(k, hist_len + i + 1).
+ *   idx [T][k] int32 positions (the k best in ascending position order,
+ *   then -1 padding), count [T] int32 = min(k, hist_len + i + 1).
  *   scores (optional, may be NULL) [T][hist_len+T] float receives the scores
  *   of visible positions (a debugging aid: the selection never needs them).
  * Ranking: score descending, equal scores by position ascending.  No score
  * matrix is kept: each query holds a running candidate buffer of
- * 2k + 512 (rounded up to 64) entries of 8 bytes, pruned to its k best
- * whenever it could fill up, so the workspace is O(T k) plus the two copy
- * buffers; scores_external no longer changes the size.
+ * 2k + 512 (rounded up to 64) entries of 8 bytes, pruned to about its k
+ * best whenever it could fill up, so the workspace is O(T k) plus the two
+ * copy buffers; scores_external no longer changes the size.
  * s_copy may equal s_compute (then nothing overlaps).  The call returns once
  * everything is enqueued; s_compute carries the final dependency. */
 size_t lsi_prefill_workspace_bytes(int32_t hist_len, int32_t T, int32_t dim,

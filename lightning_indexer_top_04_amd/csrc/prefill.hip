@@ -17,20 +17,19 @@
 //
 // No score matrix: each query keeps a buffer of candidates (order-preserving
 // score key, position) of capacity cap >= 2k + 512 and an entry threshold.
-// A score enters only if its key exceeds the threshold.  The threshold is
-// the key of the k-th best candidate after the last compaction, a lower
-// bound of the final k-th score, and a later token equal to it ranks below
-// every kept candidate (ties keep the lower positions, and every later token
-// has a higher position), so nothing that could still be selected is
-// dropped.  Every 8 tiles the workgroup compacts the buffers that could
-// overflow before the next check: an exact top-k of the buffer (key bits
-// 31..20, 19..8, 7..0, then positions ascending, by LDS histograms) keeps k
-// candidates and raises the threshold.  A query belongs to the same wave and
-// workgroup index in every launch, so its buffer and state are never shared.
-// The launch over the last block reduces each buffer to its k best and
-// writes the selection.  Workspace: T x cap x 8 bytes, O(T k).
+// A score enters only if its key exceeds the threshold.  Every 8 tiles a
+// wave whose buffer could overflow before the next check prunes it on its
+// own (radix digits of the keys over the buffer's key range, in a private
+// LDS histogram), keeping at least k and at most k + 64 candidates in
+// position order, and raises the threshold to the smallest kept key.  At
+// least k kept candidates beat any later token whose key is at or below it
+// (equal keys rank by position, and a later token has a higher one), so
+// nothing that could still be selected is dropped.  A query belongs to the
+// same wave and workgroup index in every launch, so its buffer and state are
+// never shared.  The launch over the last block reduces each buffer to
+// exactly its k best and writes their positions in ascending order.
+// Workspace: T x cap x 8 bytes, O(T k).
 #include "lsi_internal.hpp"
-#include "topk_common.hpp"
 
 namespace lsi {
 namespace {
@@ -43,130 +42,174 @@ constexpr int kQPerWg = 8;     // queries per workgroup, one per wave
 constexpr int kThreads = 64 * kQPerWg;
 static_assert(kTile * kDim == 16 * kThreads, "one 16-byte piece of a tile per thread");
 constexpr int kCheckTiles = 8;  // tiles between capacity checks of the candidate buffers
-constexpr int kCE = 8;          // candidates per thread and batch in a compaction
 
-// Exact top-k of the candidate buffer of query qi (n = st[0] entries, ranked
-// by key descending, position ascending) by the whole workgroup.  Non-final:
-// the k best stay at the front of the buffer, st = {k, key of the k-th};
-// final: their positions go to idx (padded with -1) and count.  hist (4096
-// words) and tmp (32 words) are LDS; st is LDS.
-__device__ void compact_candidates(const PrefillScanArgs& a, int qi, uint32_t* st, uint32_t* hist,
-                                   uint32_t* tmp, bool final_pass) {
-  using namespace topk;
-  const int tid = threadIdx.x;
-  const uint32_t n = st[0];
-  const uint32_t k = (uint32_t)a.k;
-  uint2* buf = a.cand + (size_t)qi * a.cap;
-  if (n <= k && !final_pass) return;
-  // The kept set, narrowed level by level: a candidate is kept when its
-  // digit at the deciding level beats the threshold bin, or it sits in every
-  // threshold bin down to a level where the whole bin is kept.
-  // lv 0..2: key bits [31:20], [19:8], [7:0] (descending); lv 3..5: position
-  // bits [30:20], [19:9], [8:0] (ascending).
-  int deciding = -1;          // level whose threshold bin is kept whole (-1: all kept)
-  uint32_t bins[6] = {0, 0, 0, 0, 0, 0};
-  auto digit = [](int lv, uint32_t key, uint32_t pos) -> uint32_t {
-    switch (lv) {
-      case 0: return key >> 20;
-      case 1: return (key >> 8) & 4095u;
-      case 2: return key & 255u;
-      case 3: return (pos >> 20) & 2047u;
-      case 4: return (pos >> 9) & 2047u;
-      default: return pos & 511u;
-    }
-  };
-  auto in_bins = [&](int upto, uint32_t key, uint32_t pos) {   // in the threshold bin of levels < upto
-    for (int l = 0; l < upto; ++l)
-      if (digit(l, key, pos) != bins[l]) return false;
-    return true;
-  };
-  auto kept = [&](uint32_t key, uint32_t pos) -> bool {
-    if (deciding < 0) return true;
-    for (int l = 0; l <= deciding; ++l) {
-      const uint32_t d = digit(l, key, pos);
-      if (d != bins[l]) return l < 3 ? d > bins[l] : d < bins[l];
-    }
-    return true;   // in every threshold bin down to the deciding level
-  };
+constexpr int kWBins = 2048;    // bins of a wave's private LDS histogram (11-bit digits)
+constexpr uint32_t kSlack = 64; // entries a pruning may keep beyond k
+constexpr int kGroup = 8;       // 128-entry chunks a pruning pass loads at once
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Over the wave's histogram h (kWBins words) in descending bin order, the
+// bin where the running count first reaches need (1 <= need <= total), the
+// count of the bins above it and its own count.  Lane l sums bins
+// 2047 - 32 l - 31 .. 2047 - 32 l; the lane where the count is reached then
+// splits its 32 bins over 32 lanes.
+__device__ __forceinline__ void wave_threshold(const uint32_t* h, uint32_t need, int lane, uint32_t& bin,
+                                               uint32_t& above, uint32_t& members) {
+  const uint4* p = reinterpret_cast<const uint4*>(h + kWBins - 32 - 32 * lane);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = p[i];
+    sum += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t incl = wave_incl_scan(sum, lane);
+  const int L = min((int)__builtin_ctzll(__ballot(incl >= need)), 63);
+  const uint32_t before = (uint32_t)__shfl((int)(incl - sum), L);
+  const uint32_t c = lane < 32 ? h[kWBins - 1 - 32 * L - lane] : 0u;
+  const uint32_t ci = wave_incl_scan(c, lane) + before;
+  const int j = min((int)__builtin_ctzll(__ballot(lane < 32 && ci >= need)), 31);
+  bin = (uint32_t)(kWBins - 1 - 32 * L - j);
+  members = (uint32_t)__shfl((int)c, j);
+  above = (uint32_t)__shfl((int)ci, j) - members;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Pruning of one query's candidate buffer by its own wave (no workgroup
+// barrier; the other waves keep scanning).  buf holds n entries (key,
+// position) in position order (capacity cap, even); every pass reads them
+// 1024 at a time, two consecutive entries per lane and chunk of 128.  The rank order is key descending, then
+// position ascending.  The bound is found digit by digit: 11-bit digits of
+// key - (smallest key) over the buffer's own key range, in the wave's LDS
+// histogram wh.  A level ends the search when its threshold bin can be kept
+// whole: exactly (the k-th entry closes the bin), or, when not final, with
+// at most `limit` entries in all (k <= limit); a single key value left over keeps its
+// lowest positions, which come first in the buffer.  The kept entries are
+// packed in order: into buf (returns their count; tau receives their
+// smallest key, the next entry threshold, since at least k entries beat
+// anything at or below it that comes later) or, when final, their positions
+// into idx_row followed by -1 up to k (returns the count).
+__device__ uint32_t wave_prune(uint2* buf, uint32_t n, uint32_t cap, uint32_t k, uint32_t limit, bool final_pass,
+                               uint32_t* wh, int lane, int32_t* idx_row, uint32_t& tau) {
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // f(e0, e1) for entries i, i + 1 (i even; position kNone past the end),
+  // every lane's pair of a chunk of 128 in order, kGroup chunks loaded
+  // before any is used (addresses clamped into the buffer, which holds cap
+  // entries; values past n are ignored)
   auto pass = [&](auto&& f) {
-    for (uint32_t base = 0; base < n; base += kThreads * kCE) {
-      uint2 e[kCE];
+    for (uint32_t g0 = 0; g0 < n; g0 += 128 * kGroup) {
+      uint4 v[kGroup];
 #pragma unroll
-      for (int u = 0; u < kCE; ++u) {
-        const uint32_t i = base + u * kThreads + tid;
-        e[u] = i < n ? buf[i] : make_uint2(0u, 0xFFFFFFFFu);
+      for (int c = 0; c < kGroup; ++c) {
+        const uint32_t i = min(g0 + 128 * c + 2 * lane, cap - 2);
+        v[c] = *reinterpret_cast<const uint4*>(buf + i);
       }
 #pragma unroll
-      for (int u = 0; u < kCE; ++u)
-        if (e[u].y != 0xFFFFFFFFu) f(e[u].x, e[u].y);
+      for (int c = 0; c < kGroup; ++c) {
+        const uint32_t i = g0 + 128 * c + 2 * lane;
+        f(make_uint2(v[c].x, i < n ? v[c].y : kNone), make_uint2(v[c].z, i + 1 < n ? v[c].w : kNone));
+      }
     }
   };
+  // kept: key > K, or key == K and among the first need_tie such entries
+  uint32_t K = 0u, need_tie = kNone;
   if (n > k) {
-    uint32_t need = k;
-    for (int lv = 0; lv < 6; ++lv) {
-      __syncthreads();
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
-      __syncthreads();
-      pass([&](uint32_t key, uint32_t pos) {
-        if (in_bins(lv, key, pos)) atomicAdd(&hist[digit(lv, key, pos)], 1u);
+    uint32_t mn = kNone, mx = 0u;
+    pass([&](uint2 e0, uint2 e1) {
+      if (e0.y != kNone) { mn = min(mn, e0.x); mx = max(mx, e0.x); }
+      if (e1.y != kNone) { mn = min(mn, e1.x); mx = max(mx, e1.x); }
+    });
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    const uint32_t span = (mx - mn) >> 11;
+    int sh = span ? 32 - __clz((int)span) : 0;      // (mx - mn) >> sh < kWBins
+    int w = 32;                                       // the current bin: keys base .. base + 2^w - 1
+    uint32_t base = mn;
+    uint32_t kept_above = 0;                          // entries above the current bin
+    for (;;) {
+      uint4* z = reinterpret_cast<uint4*>(wh);
+#pragma unroll
+      for (int i = 0; i < kWBins / 256; ++i) z[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
+      pass([&](uint2 e0, uint2 e1) {
+        const uint32_t d0 = e0.x - base, d1 = e1.x - base;
+        if (e0.y != kNone && e0.x >= base && ((uint64_t)d0 >> w) == 0) atomicAdd(&wh[d0 >> sh], 1u);
+        if (e1.y != kNone && e1.x >= base && ((uint64_t)d1 >> w) == 0) atomicAdd(&wh[d1 >> sh], 1u);
       });
-      __syncthreads();
-      uint32_t before;
-      bins[lv] = (uint32_t)find_threshold<kThreads>(hist, need, lv < 3, tmp, &before);
-      const uint32_t members = hist[bins[lv]];
-      need -= before;
-      deciding = lv;
-      if (members == need) break;   // the whole threshold bin is kept
-    }
-  }
-  // write-back (or the selection): the kept candidates, packed in place
-  // (a batch is read whole before any of it is written, and its outputs go
-  // below its end); the smallest kept key becomes the new entry threshold
-  if (tid == 0) tmp[30] = 0xFFFFFFFFu;
-  __syncthreads();
-  uint32_t out = 0;
-  uint32_t kmin = 0xFFFFFFFFu;
-  for (uint32_t base = 0; base < n; base += kThreads * kCE) {
-    uint2 e[kCE];
-    uint32_t m = 0;
-#pragma unroll
-    for (int u = 0; u < kCE; ++u) {
-      const uint32_t i = base + u * kThreads + tid;
-      e[u] = i < n ? buf[i] : make_uint2(0u, 0xFFFFFFFFu);
-      if (e[u].y != 0xFFFFFFFFu && kept(e[u].x, e[u].y)) m |= 1u << u;
-    }
-    uint32_t tot;
-    uint32_t o = out + block_excl_scan<kThreads>((uint32_t)__popc(m), tmp, &tot);
-#pragma unroll
-    for (int u = 0; u < kCE; ++u) {
-      if ((m >> u) & 1u) {
-        if (final_pass) a.idx[(int64_t)qi * a.k + o] = (int32_t)e[u].y;
-        else buf[o] = e[u];
-        kmin = min(kmin, e[u].x);
-        ++o;
+      uint32_t b, above, members;
+      wave_threshold(wh, k - kept_above, lane, b, above, members);
+      kept_above += above;
+      const uint32_t lo = base + (b << sh);
+      const uint32_t need = k - kept_above;
+      if (members == need || (!final_pass && kept_above + members <= limit)) {
+        K = lo - 1u;   // every key >= lo (lo > the entry threshold >= 0)
+        need_tie = 0u;
+        break;
       }
+      if (sh == 0) {   // one key value: its first `need` entries
+        K = lo;
+        need_tie = need;
+        break;
+      }
+      base = lo;
+      w = sh;
+      sh = sh > 11 ? sh - 11 : 0;
     }
-    out += tot;
   }
-  atomicMin(&tmp[30], kmin);
-  __syncthreads();
-  if (final_pass) {
-    for (uint32_t i = out + tid; i < k; i += kThreads) a.idx[(int64_t)qi * a.k + i] = -1;
-    if (tid == 0) a.count[qi] = (int32_t)out;
-  } else if (tid == 0) {
-    st[0] = out;
-    st[1] = tmp[30];
-  }
-  __syncthreads();
+  uint32_t out = 0, seen_tie = 0, kmin = kNone;
+  // in place: a chunk's kept entries go below its end, and every chunk of
+  // a group is read before any of them is written
+  pass([&](uint2 e0, uint2 e1) {
+    const bool v0 = e0.y != kNone, v1 = e1.y != kNone;
+    const bool t0 = v0 && e0.x == K, t1 = v1 && e1.x == K;
+    const uint64_t bt0 = __ballot(t0), bt1 = __ballot(t1);
+    const uint32_t r0 = seen_tie + (uint32_t)(__popcll(bt0 & below) + __popcll(bt1 & below));
+    const uint32_t r1 = r0 + (t0 ? 1u : 0u);
+    seen_tie += (uint32_t)(__popcll(bt0) + __popcll(bt1));
+    const bool k0 = v0 && (e0.x > K || (t0 && r0 < need_tie));
+    const bool k1 = v1 && (e1.x > K || (t1 && r1 < need_tie));
+    const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
+    const uint32_t o0 = out + (uint32_t)(__popcll(m0 & below) + __popcll(m1 & below));
+    const uint32_t o1 = o0 + (k0 ? 1u : 0u);
+    if (k0) {
+      if (final_pass) idx_row[o0] = (int32_t)e0.y;
+      else buf[o0] = e0;
+      kmin = min(kmin, e0.x);
+    }
+    if (k1) {
+      if (final_pass) idx_row[o1] = (int32_t)e1.y;
+      else buf[o1] = e1;
+      kmin = min(kmin, e1.x);
+    }
+    out += (uint32_t)(__popcll(m0) + __popcll(m1));
+  });
+  if (final_pass)
+    for (uint32_t i = out + lane; i < k; i += 64) idx_row[i] = -1;
+  tau = wave_min(kmin);
+  return out;
 }
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 kt[2][kTile * kStride];
   __shared__ float ksc[2][kTile];
-  __shared__ uint32_t hist[topk::kBins];
-  __shared__ uint32_t tmp[32];
-  __shared__ uint32_t qst[kQPerWg][2];    // count and entry threshold of each wave's query
-  __shared__ int qflag[kQPerWg];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[kQPerWg][kWBins];   // one per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -236,31 +279,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanAr
   if (ntile > 1) fetch(1, raw, sc);
   __syncthreads();
 
-  // The workgroup compacts the buffers of its queries listed in qflag.
-  auto compact_flagged = [&](bool final_pass) {
-    for (int j = 0; j < kQPerWg; ++j) {
-      if (qflag[j] == 0) continue;                 // uniform (LDS after a barrier)
-      if (wave == j && lane == 0) {
-        qst[j][0] = cnt_r;
-        qst[j][1] = tau_r;
-      }
-      __syncthreads();
-      compact_candidates(a, q0 + j, qst[j], hist, tmp, final_pass);
-      if (wave == j) {
-        cnt_r = qst[j][0];
-        tau_r = qst[j][1];
-      }
-    }
-  };
+  int32_t* idx_row = a.idx ? a.idx + (int64_t)(active ? qi : 0) * a.k : nullptr;
+  // a pruning may keep a few more than k, as long as the next 8 tiles fit
+  const uint32_t keep_limit = min((uint32_t)a.k + kSlack, (uint32_t)(a.cap - kCheckTiles * kTile));
 
   for (int tile = 0; tile < ntile; ++tile) {
     const int cur = tile & 1;
-    if (tile % kCheckTiles == 0) {
-      // could a buffer fill up before the next check (64 entries per tile)?
-      if (lane == 0) qflag[wave] = active && cnt_r + kCheckTiles * kTile > (uint32_t)a.cap;
-      __syncthreads();
-      compact_flagged(false);
-    }
+    // could the buffer fill up before the next check (64 entries per tile)?
+    if (tile % kCheckTiles == 0 && active && cnt_r + kCheckTiles * kTile > (uint32_t)a.cap)
+      cnt_r = wave_prune(cbuf, cnt_r, (uint32_t)a.cap, (uint32_t)a.k, keep_limit, false, whist[wave], lane, idx_row, tau_r);
     // the next tile into the other buffer (its readers passed the last
     // barrier), then the one after it from memory
     if (tile + 1 < ntile) {
@@ -304,10 +331,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(PrefillScanAr
     __syncthreads();
   }
   if (a.final_block) {
-    // every query's k best (all of its candidates when it has fewer)
-    if (lane == 0) qflag[wave] = active;
-    __syncthreads();
-    compact_flagged(true);
+    // the query's k best (all of its candidates when it has fewer)
+    if (active) {
+      uint32_t t;
+      const uint32_t c = wave_prune(cbuf, cnt_r, (uint32_t)a.cap, (uint32_t)a.k, (uint32_t)a.k, true, whist[wave], lane, idx_row, t);
+      if (lane == 0) a.count[qi] = (int32_t)c;
+    }
   } else if (active && lane == 0) {
     a.state[2 * (int64_t)qi] = cnt_r;
     a.state[2 * (int64_t)qi + 1] = tau_r;

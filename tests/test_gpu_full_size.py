@@ -194,8 +194,9 @@ def test_prefill_small_history_and_partial_blocks():
         assert np.array_equal(np.sort(got[:n]), exact_topk_f32(sc[i, :vis].cpu().numpy(), k))
 
 
-@pytest.mark.parametrize("pattern", ["equal", "rising", "falling"])
-def test_prefill_running_selection_under_ties_and_monotone_scores(pattern):
+@pytest.mark.parametrize("pattern,k", [("equal", 700), ("rising", 700), ("falling", 700),
+                                       ("equal", 1), ("rising", 1), ("rising", 37), ("falling", 37)])
+def test_prefill_running_selection_under_ties_and_monotone_scores(pattern, k):
     """Every key the same code: a query's scores are one constant times the
     token scale.  equal: all scores tie, the first positions win and after
     the first pruning nothing enters; rising / falling: the scale grows or
@@ -210,7 +211,6 @@ def test_prefill_running_selection_under_ties_and_monotone_scores(pattern):
     scale = {"equal": torch.full((n,), 0.5, dtype=torch.float64, device=DEV),
              "rising": 0.25 + pos * 1e-4,
              "falling": 2.0 - pos * 1e-4}[pattern].float()
-    k = 700
     idx, cnt, sc = lsi.prefill_index_topk(keys[:H], scale[:H].contiguous(), keys[H:],
                                           scale[H:].contiguous(), pi.q, pi.w, k, 1024,
                                           want_scores=True)
@@ -220,6 +220,7 @@ def test_prefill_running_selection_under_ties_and_monotone_scores(pattern):
         row = sc[i, :vis].cpu().numpy()
         got = idx[i].cpu().numpy()
         assert cnt[i].item() == k and np.all(got[k:] == -1)
-        assert np.array_equal(np.sort(got[:k]), exact_topk_f32(row, k)), f"{pattern} row {i}"
+        assert np.all(np.diff(got[:k]) > 0), "positions in ascending order"
+        assert np.array_equal(got[:k], exact_topk_f32(row, k)), f"{pattern} row {i}"
         if pattern == "equal":
-            assert np.array_equal(np.sort(got[:k]), np.arange(k))
+            assert np.array_equal(got[:k], np.arange(k))
