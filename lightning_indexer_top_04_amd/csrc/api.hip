@@ -718,12 +718,13 @@ size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32
   if (num_req < 1 || max_seq_len < 0 || n_cand < 1 || k < 1) return 0;
   (void)k;
   const size_t s4 = align_up((size_t)num_req * scores_ld(max_seq_len) * 4, kWsAlign);
+  const size_t rg = align_up((size_t)kMaxRangeSlots * 16, kWsAlign);
   const size_t t1 = topk_ws_bytes(num_req, max_seq_len);
   const size_t cand = align_up((size_t)num_req * n_cand * 4, kWsAlign);
   const size_t ccount = align_up((size_t)num_req * 4, kWsAlign);
   const size_t s8 = align_up((size_t)num_req * n_cand * 4, kWsAlign);
   const size_t t2 = topk_ws_bytes(num_req, n_cand);
-  return s4 + t1 + cand + ccount + s8 + t2;
+  return s4 + rg + t1 + cand + ccount + s8 + t2;
 }
 
 int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache* ikeys8,
@@ -754,6 +755,8 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   char* ws = static_cast<char*>(workspace);
   float* s4 = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * ld * 4, kWsAlign);
+  uint4* rslots = reinterpret_cast<uint4*>(ws);   // the int4 scan's per-workgroup key ranges
+  ws += align_up((size_t)kMaxRangeSlots * 16, kWsAlign);
   void* t1 = ws;
   ws += topk_ws_bytes(B, batch->max_seq_len);
   int32_t* cl = reinterpret_cast<int32_t*>(ws);
@@ -764,13 +767,20 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ws += align_up((size_t)B * n_cand * 4, kWsAlign);
   void* t2 = ws;
 
-  // stage 1: compact keys over every token, keep n_cand
+  // stage 1: compact keys over every token, keep n_cand.  The scan records
+  // each workgroup's key range, so that the top-k's first digit spans the
+  // row's range (the compact scores crowd into a few binades), and clears
+  // the top-k's counters.
   ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
   a4.zero_ptr = static_cast<uint32_t*>(t1);
   a4.zero_words = topk_zero_words(B);
-  LSI_LAUNCH(launch_scan_int4(a4, stream), "lsi_two_stage_topk (compact scan)");
+  a4.range_slots = rslots;
+  int nslots = 0;
+  LSI_LAUNCH(launch_scan_int4(a4, stream, &nslots), "lsi_two_stage_topk (compact scan)");
   TopkArgs ta;
   ta.scores = s4;
+  ta.range_slots = nslots > 0 ? rslots : nullptr;
+  ta.range_nslots = nslots;
   ta.ld = ld;
   ta.seq_lens = batch->seq_lens;
   ta.num_req = B;

@@ -37,14 +37,21 @@ struct ScanArgs {
   // blockIdx % kHistReps of the row's replicated histogram, which must be
   // zero when the scan starts ([num_req][kHistReps][kHistWords] words)
   uint32_t* hist_rep = nullptr;
+  // optional (contiguous walk): every workgroup stores {request, ~lowest
+  // key, highest key, 0} of the scores it wrote (request ~0u when it wrote
+  // none) at range_slots[its linear index] (the key ranges for the top-k's
+  // digits, TopkArgs::range_slots); plain stores, nothing to clear
+  uint4* range_slots = nullptr;
 };
+// most workgroups a scan that records key ranges may use (its slots)
+constexpr int kMaxRangeSlots = 8192;
 constexpr int kHistReps = 8;
 constexpr int kHistWords = 4096 + 64;     // 12-bit digits, then 6-bit digits
 // whether a scan of this shape can build the replicated histogram
 bool scan_builds_hist(int num_req, int max_seq_len, int page_size);
 
 hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s);
-hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s, int* nslots = nullptr);
 hipError_t launch_scan_f32(const ScanArgs& a, hipStream_t s);
 
 // ---- top-k ----------------------------------------------------------------
@@ -54,7 +61,14 @@ struct TopkArgs {
   const int32_t* seq_lens = nullptr;  // per-row length (clamped to max_len)
   int lens_const = -1;             // if >= 0: every row has this length
   int causal_base = -1;            // if >= 0: row r has length causal_base+r+1
-  const uint32_t* range = nullptr; // optional [R][2]: ~(min key), max key of row r
+  // optional [R][2]: ~(min key), max key of row r, recorded by the producer
+  // of the scores; the one-workgroup path's first digit then spans it
+  const uint32_t* range = nullptr;
+  // optional: the scan's per-workgroup key ranges (ScanArgs::range_slots,
+  // range_nslots of them); the multi-workgroup path's histogram launch
+  // reduces a row's slots and its digits span the row's key range
+  const uint4* range_slots = nullptr;
+  int range_nslots = 0;
   int num_req = 0;
   int max_len = 0;
   int k = 0;

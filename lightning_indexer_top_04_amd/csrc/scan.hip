@@ -579,6 +579,8 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     }
     if (b < 0) {             // no slice for this workgroup
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (a.range_slots != nullptr && tid == 0)
+        a.range_slots[blockIdx.y * gridDim.x + blockIdx.x] = make_uint4(~0u, 0u, 0u, 0u);
       return;
     }
     if (b != gb || begin != gbegin || span != bal_sp) {
@@ -595,6 +597,8 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   if (begin > 0 && begin >= L) {
     // nothing of this request here; no DMA may still be writing the LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (a.range_slots != nullptr && tid == 0)
+      a.range_slots[blockIdx.y * gridDim.x + blockIdx.x] = make_uint4(~0u, 0u, 0u, 0u);
     return;
   }
   if (tid < npg_max) pages[tid] = page_in0;
@@ -824,8 +828,16 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   // own DRAM row, slows the key stream far beyond the bytes it adds.
   float* out = a.scores + (int64_t)b * a.ld + begin;
   float* stage = sbuf[wv];
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;   // key range of this lane's scores (range_slots)
   auto stage_score = [&](int j, float v) {
-    if (h == 0) stage[(j % kFlushTiles) * kTile + m] = v;
+    if (h == 0) {
+      stage[(j % kFlushTiles) * kTile + m] = v;
+      if (a.range_slots != nullptr && (my0 + j) * kTile + m < end - begin) {
+        const uint32_t kk = float_key(v);
+        kmn = min(kmn, kk);
+        kmx = max(kmx, kk);
+      }
+    }
   };
   auto flush = [&](int j) {                  // after tile j, the last of its group
     const int first = j - j % kFlushTiles;
@@ -864,6 +876,27 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   }
   // no DMA may still be writing this workgroup's LDS when it retires
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (a.range_slots != nullptr) {
+    // the workgroup's key range (waves combined in LDS) into its slot: plain
+    // stores (atomics from every workgroup on one row's pair of words
+    // serialise, several microseconds at 512 workgroups)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
+    }
+    uint32_t* lr = reinterpret_cast<uint32_t*>(&ring[0][0]);
+    __syncthreads();
+    if (tid < 2) lr[tid] = 0u;
+    __syncthreads();
+    if (lane == 0 && kmx >= kmn) {
+      atomicMax(&lr[0], ~kmn);
+      atomicMax(&lr[1], kmx);
+    }
+    __syncthreads();
+    if (tid == 0)
+      a.range_slots[blockIdx.y * gridDim.x + blockIdx.x] = make_uint4(lr[1] != 0u ? (uint32_t)b : ~0u, lr[0], lr[1], 0u);
+  }
   if (a.hist_rep != nullptr) {
     // The histogram of this workgroup's scores for the top-k that follows:
     // 12-bit and 6-bit top key digits, counted in the ring's LDS (no DMA is
@@ -951,7 +984,13 @@ bool scan_builds_hist(int num_req, int max_seq_len, int page_size) {
 namespace {
 
 template <int KIND>
-hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
+hipError_t launch_mfma_scan(const ScanArgs& a_in, hipStream_t s, int* nslots) {
+  // key ranges only when every workgroup has a slot
+  ScanArgs a = a_in;
+  auto slots = [&](int64_t g) {
+    if (a.range_slots != nullptr && g > kMaxRangeSlots) a.range_slots = nullptr;
+    if (nslots) *nslots = a.range_slots != nullptr ? (int)g : 0;
+  };
   const bool gather = a.positions != nullptr;
   const int max_items = gather ? a.n_pos : a.max_seq_len;
   constexpr int kRingTiles = 2;
@@ -982,6 +1021,7 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
             break;
           }
         }
+        slots(G);
         launch((scan_dma_kernel<KIND, kRingTiles>), dim3((unsigned)G), dim3(kThreads), 0, s, KIND == KIND_FP8 ? "scan_dma_kernel<fp8>" : "scan_dma_kernel<int4>", a,
                            (int)unit, ps, (int)n_u, (int)sp_u);
         return hipGetLastError();
@@ -992,6 +1032,8 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
   // the DMA scan stages a slice's page ids, two per thread
   if (!gather && (chunk + a.page_size - 1) / a.page_size > kMaxChunkPages) return hipErrorInvalidValue;
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(max_items, chunk)), (unsigned)a.num_req);
+  if (gather) a.range_slots = nullptr;   // the contiguous walk only
+  slots((int64_t)grid.x * grid.y);
   if (!gather) {
     launch((scan_dma_kernel<KIND, kRingTiles>), grid, dim3(kThreads), 0, s, KIND == KIND_FP8 ? "scan_dma_kernel<fp8>" : "scan_dma_kernel<int4>", a, chunk, ps, 0, 0);
   } else {
@@ -1002,8 +1044,10 @@ hipError_t launch_mfma_scan(const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s) { return launch_mfma_scan<KIND_FP8>(a, s); }
-hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s) { return launch_mfma_scan<KIND_INT4>(a, s); }
+hipError_t launch_scan_fp8(const ScanArgs& a, hipStream_t s) { return launch_mfma_scan<KIND_FP8>(a, s, nullptr); }
+hipError_t launch_scan_int4(const ScanArgs& a, hipStream_t s, int* nslots) {
+  return launch_mfma_scan<KIND_INT4>(a, s, nslots);
+}
 
 hipError_t launch_scan_f32(const ScanArgs& a, hipStream_t s) {
   dim3 grid((unsigned)std::max<int64_t>(1, ceil_div(a.max_seq_len, 256)), (unsigned)a.num_req);

@@ -192,6 +192,7 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
   __shared__ __attribute__((aligned(16))) uint32_t hist[kReps * kBins / 2];
   __shared__ uint32_t tmp[32];
+  __shared__ uint32_t rr[2];
   const int r = blockIdx.x;   // rows fastest: every row's early (full) chunks
   const int c = blockIdx.y;   // are dispatched before the empty tails
   const int L = row_len(a, r);
@@ -200,20 +201,49 @@ __global__ __launch_bounds__(kBlock) void topk_hist_kernel(TopkArgs a) {
   if (begin >= L) return;
   const int end = min(begin + kChunk, L);
   const float* row = a.scores + (int64_t)r * a.ld;
+  // the row's key range from the scan's per-workgroup slots (when it
+  // recorded them), reduced by every workgroup and stored by the first for
+  // the launches that follow
+  uint32_t nlo = 0u, hi = 0u;
+  if (a.range_slots != nullptr) {
+    if (threadIdx.x < 2) rr[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < a.range_nslots; i += kBlock) {
+      const uint4 v = a.range_slots[i];
+      if (v.x == (uint32_t)r) {
+        nlo = max(nlo, v.y);
+        hi = max(hi, v.z);
+      }
+    }
+  }
   // the chunk's loads go out first, so they cost one round trip
   uint32_t d[PER];
   load_keys<PER, VW>(row, begin, end, d);
   for (int i = threadIdx.x; i < kReps * kBins / 2; i += kBlock) hist[i] = 0u;
   __syncthreads();
+  Digits dg = row_digits(a.range, r);
+  const Ws ws = carve(a.ws, a.num_req, a.max_len);
+  if (a.range_slots != nullptr) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      nlo = max(nlo, (uint32_t)__shfl_xor((int)nlo, o));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicMax(&rr[0], nlo);
+      atomicMax(&rr[1], hi);
+    }
+    __syncthreads();
+    dg = row_digits(rr, 0);
+    if (c == 0 && threadIdx.x < 2) ws.rng[2 * (size_t)r + threadIdx.x] = rr[threadIdx.x];
+  }
   const int rep = threadIdx.x & (kReps - 1);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const uint32_t bin = d[j] >> 20;
+    const uint32_t bin = dg.d1(d[j]);
     const uint32_t one = chunk_pos<VW>(begin, j) < end ? 1u : 0u;
     atomicAdd(&hist[kReps * (bin & 2047) + rep], one << (16 * (bin >> 11)));
   }
   __syncthreads();
-  const Ws ws = carve(a.ws, a.num_req, a.max_len);
   // the chunk's suffix counts: thread t owns bins 4095-8t down to 4088-8t
   uint32_t v[8], run = 0;
 #pragma unroll
@@ -255,6 +285,35 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
   // to 24 bits), then position bits [31:20], [19:8], [7:0] ascending
   const int kb_hi = key_bits > 12 ? 12 : key_bits;
   const int kb_lo = key_bits > 12 ? key_bits - 12 : 0;
+  if (need > 0 && n > need && n <= 64) {
+    // few candidates: the first wave ranks each one against all of them (key
+    // descending, then position ascending) and writes the `need` best; no
+    // histogram stages and no workgroup barriers
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      uint32_t key = 0u;
+      int pos = 0x7FFFFFFF;
+      if (lane < (int)n) {
+        const int slot = in_lds ? lslot[lane] : list[lane];
+        key = in_lds ? lkey[lane] : float_key(row[slot]) - kbase;
+        pos = out_value(a, r, slot);
+      }
+      uint32_t rank = 0;
+      for (int j = 0; j < (int)n; ++j) {
+        const uint32_t kj = (uint32_t)__shfl((int)key, j);
+        const int pj = __shfl(pos, j);
+        rank += (kj > key || (kj == key && pj < pos)) ? 1u : 0u;
+      }
+      const bool take = lane < (int)n && rank < need;
+      const uint64_t m = __ballot(take);
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      const uint32_t o = out_pos + (uint32_t)__popcll(m & below);
+      if (take && o < (uint32_t)a.k) emit(a, r, (int)o, pos);
+    }
+    out_pos += need;
+    need = 0;
+    n = 0;
+  }
   for (int stage = 0; stage < 5 && need > 0 && n > 0; ++stage) {
     if (n <= need) break;
     const bool by_key = stage < 2;
@@ -487,6 +546,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   // entries (so winners leave with their physical rows; with a slot map the
   // pages are only known per winner)
   uint32_t key[PER];
+  const Digits dg = row_digits(a.range_slots ? ws.rng : a.range, r);
   load_keys<PER, VW>(row, begin, end, key);
   const uint32_t* gh = ws.hist + (size_t)r * kBins;
   // scan-built histograms: kHistReps replicas of [4096 12-bit | 64 6-bit] bins
@@ -622,7 +682,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (chunk_pos<VW>(begin, j) < end) {
-      const uint32_t dj = key[j] >> 20;
+      const uint32_t dj = dg.d1(key[j]);
       win |= (uint32_t)(dj > digit) << j;
       eq |= (uint32_t)(dj == digit) << j;
     }
@@ -681,7 +741,7 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if ((eq >> j) & 1u) atomicAdd(&hist[(key[j] >> 8) & (kBins - 1)], 1u);
+      if ((eq >> j) & 1u) atomicAdd(&hist[dg.d2(key[j])], 1u);
     __syncthreads();
     uint32_t* g2 = ws.h2 + (size_t)r * kBins;
     for (int i = threadIdx.x; i < kBins; i += kBlock) {
@@ -744,8 +804,9 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
   const int L = row_len(a, r);
   if (L <= a.k) return;
   const Ws ws = carve(a.ws, a.num_req, a.max_len);
+  const Digits dg = row_digits(a.range_slots ? ws.rng : a.range, r);
   // the threshold bin's members are the candidates (everything above it has
-  // been written already); their second histogram (key bits [19:8]) was
+  // been written already); their second histogram (level-2 digits) was
   // built by the select, so one ordered pass over them settles 12 more bits.
   // The histogram, the record and the first batch of members are loaded
   // together.
@@ -810,7 +871,7 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (base + tid + u * kRefThreads < n) {
-        const uint32_t d = ((uint32_t)e[u].y >> 8) & (kBins - 1);
+        const uint32_t d = dg.d2((uint32_t)e[u].y);
         win |= (uint32_t)(d > bin2 || (take_eq && d == bin2)) << u;
         eq |= (uint32_t)(!take_eq && d == bin2) << u;
       }
@@ -837,7 +898,7 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
       if ((eq >> u) & 1u) {
         if (in_lds) {
           lslot[q] = e[u].x;
-          lkey[q] = (uint32_t)e[u].y;
+          lkey[q] = (uint32_t)e[u].y - dg.base;
         } else {
           list[q] = e[u].x;
         }
@@ -852,9 +913,10 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
     return;
   }
   wg_sync(in_lds);
-  // the members that share the level-2 digit: key bits [7:0], then position
+  // the members that share the level-2 digit: the key bits below it, then
+  // positions
   refine_cands<kRefThreads, kLdsCand>(a, r, n2, need - better2, better + better2, list, in_lds, hist,
-                                      tmp, lkey, lslot, 8, 0u);
+                                      tmp, lkey, lslot, dg.sh2, dg.base);
 }
 
 // ---------------------------------------------------------------------------
@@ -1049,7 +1111,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
 
 size_t topk_ws_bytes(int num_req, int max_len) {
   const size_t R = (size_t)num_req;
-  return align_up(2 * R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (4 * R * max_len + 4 * R) * 4, 256);
+  return align_up(2 * R * kBins * 4 + R * max_chunks(max_len) * kBins * 2 + (4 * R * max_len + 6 * R) * 4, 256);
 }
 
 int64_t topk_zero_words(int num_req) { return (int64_t)num_req * 2 * kBins; }

@@ -22,6 +22,7 @@ struct Ws {
   int32_t* list;     // [R][max_len] their slots, compacted (when too many for LDS)
   uint32_t* rec;     // [R][4] threshold bin, count above it, count in it
   int32_t* crow;     // [R][max_len] physical row of each candidate (deferred selections only)
+  uint32_t* rng;     // [R][2] the row's key range as reduced by the histogram launch
   int nchunk;        // chunks per row at the smallest chunk size
 };
 
@@ -39,7 +40,42 @@ __host__ __device__ inline Ws carve(void* ws, int R, int max_len) {
   w.list = reinterpret_cast<int32_t*>(w.cand + (size_t)R * max_len);
   w.rec = reinterpret_cast<uint32_t*>(w.list + (size_t)R * max_len);
   w.crow = reinterpret_cast<int32_t*>(w.rec + (size_t)R * 4);
+  w.rng = reinterpret_cast<uint32_t*>(w.crow + (size_t)R * max_len);
   return w;
+}
+
+// The multi-workgroup top-k's digits of a row's keys: level 1 is
+// (key - base) >> sh1 (12 bits), level 2 ((key - base) >> sh2) & 4095 over
+// the level-1 bin's members, and the sh2 bits below it come last.  Without
+// a recorded key range these are the top 12, the next 12 and the last 8 key
+// bits.  With one ([~lowest key, highest key] of the row, written by the
+// producer of the scores) the range fills the 4096 level-1 bins, so scores
+// crowded into a few binades still spread over many bins and the threshold
+// bin keeps few members.  Keys outside a recorded range (none, when the
+// producer is right) are clamped into the end bins, never out of bounds.
+struct Digits {
+  uint32_t base = 0u;
+  int sh1 = 20;
+  int sh2 = 8;
+  __device__ uint32_t d1(uint32_t key) const {
+    return key < base ? 0u : min((key - base) >> sh1, (uint32_t)kBins - 1u);
+  }
+  __device__ uint32_t d2(uint32_t key) const { return ((key - base) >> sh2) & (uint32_t)(kBins - 1); }
+};
+__device__ inline Digits row_digits(const uint32_t* range, int r) {
+  Digits g;
+  if (range != nullptr) {
+    const uint32_t lo = ~range[2 * (size_t)r];
+    const uint32_t hi = range[2 * (size_t)r + 1];
+    if (hi >= lo) {
+      const uint32_t span = hi - lo;
+      const int bits = span ? 32 - __clz((int)span) : 0;
+      g.base = lo;
+      g.sh1 = bits > 12 ? bits - 12 : 0;
+      g.sh2 = g.sh1 > 12 ? g.sh1 - 12 : 0;
+    }
+  }
+  return g;
 }
 
 // Workgroup barrier.  With lds_only it orders LDS traffic only: a plain
