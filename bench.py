@@ -567,45 +567,58 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
 
 
 def multilayer(lsi, synth, torch, dev, graph_ms, n_layers=61):
-    """Several layers of one decode step over one 131072-token request, each
-    layer with its own indexer keys and latent cache (one page table): an
-    indexer in every layer, each finishing before its layer attends
-    (unmodified), the MLI schedule (each layer attends the previous indexer
-    layer's selection while its own indexer runs on a second stream), and
-    IndexCache retention 1/2 and 1/4 with and without MLI.  One graph replay
-    per multi-layer step."""
-    wl = synth.DSA_128K
-    L, k, H, dv = 131072, 2048, 128, 512
-    dis = [synth.make_decode_inputs(wl, device=dev, planted=False, layer=l)
-           for l in range(n_layers)]
-    req = lsi.Requests(dis[0].seq_lens, dis[0].page_table, L)
+    """Several layers of one decode step over one request, each layer with
+    its own indexer keys and latent cache (one page table): an indexer in
+    every layer, each finishing before its layer attends (serial), and the
+    MLI schedule (each layer attends the previous indexer layer's selection
+    while its own indexer runs on a second stream); IndexCache retention 1/r
+    keeps an indexer in every r-th layer.  Swept over r = 1 .. 32 at 131072
+    tokens, and over contexts of 10240 .. 199680 tokens at r = 1 and 4.  One
+    graph replay per multi-layer step."""
+    k, H, dv = 2048, 128, 512
     side = torch.cuda.Stream()
-    kv = [lsi.Cache(d.kv, None, "bf16", 576) for d in dis]
     attn_bytes = k * 576 * 2 + H * 576 * 2 + H * dv * 2
-    us, frac = {}, {}
-    for r in (1, 2, 4):
-        has = [l % r == 0 for l in range(n_layers)]
-        layers = lsi.Layers([lsi.Cache(d.ikeys, d.iscale, "fp8", 128) if h else None
-                             for d, h in zip(dis, has)], kv, req,
-                            [d.q_idx if h else None for d, h in zip(dis, has)],
-                            [d.w if h else None for d, h in zip(dis, has)],
-                            [d.q_attn for d in dis], k, dv, r)
-        byts = sum(has) * L * BYTES_PER_TOKEN + n_layers * attn_bytes
-        for sched in ("serial", "mli"):
-            t = graph_ms(lambda sched=sched: lsi.multilayer_decode(
-                layers, wl.sm_scale, sched, index_stream=side), n=1, reps=10)
-            key = f"r{r}_{sched}"
-            us[key] = t * 1e3
-            frac[key] = byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS
-        del layers
-    base = us["r1_serial"]
-    return {"layers": n_layers, "tokens_per_layer": L,
-            "us_per_step": us, "us_per_layer": {kk: v / n_layers for kk, v in us.items()},
-            "speedup_vs_unmodified": {kk: base / v for kk, v in us.items()},
-            "hbm_roofline_frac": frac,
-            "note": "r = retention (one indexer every r layers); serial = each indexer "
-                    "finishes before its layer attends; mli = the indexer of layer l runs "
-                    "beside layer l's attention on a second stream, after layer l-1"}
+
+    def sweep(L, retentions):
+        wl = synth.scaled(synth.DSA_128K, seq_lens=(L,))
+        dis = [synth.make_decode_inputs(wl, device=dev, planted=False, layer=l)
+               for l in range(n_layers)]
+        req = lsi.Requests(dis[0].seq_lens, dis[0].page_table, L)
+        kv = [lsi.Cache(d.kv, None, "bf16", 576) for d in dis]
+        us, frac = {}, {}
+        for r in retentions:
+            has = [l % r == 0 for l in range(n_layers)]
+            layers = lsi.Layers([lsi.Cache(d.ikeys, d.iscale, "fp8", 128) if h else None
+                                 for d, h in zip(dis, has)], kv, req,
+                                [d.q_idx if h else None for d, h in zip(dis, has)],
+                                [d.w if h else None for d, h in zip(dis, has)],
+                                [d.q_attn for d in dis], k, dv, r)
+            byts = sum(has) * L * BYTES_PER_TOKEN + n_layers * attn_bytes
+            for sched in ("serial", "mli"):
+                t = graph_ms(lambda sched=sched: lsi.multilayer_decode(
+                    layers, wl.sm_scale, sched, index_stream=side), n=1, reps=10)
+                key = f"r{r}_{sched}"
+                us[key] = t * 1e3
+                frac[key] = byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS
+            del layers
+            print(f"# multilayer L={L} r={r}: serial {us[f'r{r}_serial']:.0f} us, "
+                  f"mli {us[f'r{r}_mli']:.0f} us", file=sys.stderr, flush=True)
+        del dis, kv, req
+        torch.cuda.empty_cache()
+        base = us["r1_serial"]
+        return {"tokens_per_layer": L, "us_per_step": us,
+                "us_per_layer": {kk: v / n_layers for kk, v in us.items()},
+                "speedup_vs_unmodified": {kk: base / v for kk, v in us.items()},
+                "hbm_roofline_frac": frac}
+
+    res = sweep(131072, (1, 2, 4, 8, 16, 32))
+    res["layers"] = n_layers
+    res["by_context"] = {f"L{L}": sweep(L, (1, 4)) for L in (10240, 65536, 199680)}
+    res["note"] = ("r = retention (one indexer every r layers); serial = each indexer finishes "
+                   "before its layer attends; mli = the indexer of layer l runs beside layer l's "
+                   "attention on a second stream, after layer l-1; speedups against r1_serial "
+                   "of the same context")
+    return res
 
 
 def measured_traffic(kernel):

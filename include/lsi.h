@@ -248,7 +248,12 @@ int32_t lsi_decode_step_noalloc(const lsi_paged_cache* ikeys,
  * carries the final dependency.  With s_index NULL or equal to `stream`
  * LSI_SCHED_MLI runs the same work in order on `stream`.  Calls on one
  * device are serialised by a lock while they enqueue (they share two
- * events).  1 <= retention <= n_layers <= 4096. */
+ * events).  1 <= retention <= n_layers <= 4096.
+ * Each indexer layer runs the launches of lsi_decode_step (the scan builds
+ * the top-k's histograms, the attention resolves the threshold bin), with
+ * two sets of that state alternating between selection slots.  Workspace
+ * state: its first 2 * lsi_decode_step_state_bytes(num_req) bytes must be
+ * zero the first time it is used; every successful call leaves them zero. */
 enum { LSI_SCHED_SERIAL = 0, LSI_SCHED_MLI = 1 };
 size_t lsi_multilayer_workspace_bytes(int32_t num_req, int32_t max_seq_len,
                                       int32_t k, int32_t n_heads, int32_t dv);

@@ -346,6 +346,7 @@ int32_t enqueue_attend(const lsi_paged_cache* kv, const lsi_paged_cache* v, cons
   a.tk_ws = deferred_topk_ws;
   a.tk_max_len = batch->max_seq_len;
   a.idx_out = idx_out;
+  a.phys_out = deferred_topk_ws ? const_cast<int32_t*>(phys) : nullptr;
   a.zero_ptr = zero_ptr;
   a.zero_words = zero_words;
   LSI_LAUNCH(run_attn(kv->dtype, a, stream), std::string(what) + " (attention)");
@@ -593,11 +594,12 @@ int32_t lsi_decode_step_noalloc(const lsi_paged_cache* ikeys, const lsi_paged_ca
 size_t lsi_multilayer_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32_t k,
                                       int32_t n_heads, int32_t dv) {
   if (num_req < 1 || max_seq_len < 0 || k < 1 || n_heads < 1) return 0;
+  const size_t st = lsi_decode_step_state_bytes(num_req);
   const size_t sc = align_up((size_t)num_req * scores_ld(max_seq_len) * sizeof(float), kWsAlign);
   const size_t tk = topk_ws_bytes(num_req, max_seq_len);
   const size_t ph = align_up((size_t)num_req * k * sizeof(int32_t), kWsAlign);
   const size_t at = (n_heads % 16 == 0 && dv == 512) ? mla_ws_bytes(num_req, n_heads, dv, k) : 0;
-  return sc + tk + 2 * ph + at;
+  return 2 * st + sc + 2 * tk + 2 * ph + at;
 }
 
 int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t schedule,
@@ -639,17 +641,39 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t sched
   const size_t need = lsi_multilayer_workspace_bytes(batch->num_req, batch->max_seq_len, k, n_heads, dv);
   LSI_TRY(check_ws(workspace, ws_bytes, need));
 
+  // Per selection slot parity: the scan-built histograms (state kept between
+  // calls, zero on entry and on return), the top-k workspace and the
+  // physical rows, so that the attention reading slot s - 1 (and resolving
+  // its threshold bin) never shares them with the indexer filling slot s.
   char* ws = static_cast<char*>(workspace);
+  uint32_t* state[2];
+  const size_t st_bytes = lsi_decode_step_state_bytes(batch->num_req);
+  for (int i = 0; i < 2; ++i) {
+    state[i] = reinterpret_cast<uint32_t*>(ws);
+    ws += st_bytes;
+  }
   float* scores = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)batch->num_req * ld * sizeof(float), kWsAlign);
-  void* topk_ws = ws;
-  ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
+  void* topk_ws[2];
+  for (int i = 0; i < 2; ++i) {
+    topk_ws[i] = ws;
+    ws += topk_ws_bytes(batch->num_req, batch->max_seq_len);
+  }
   int32_t* phys[2];
   for (int i = 0; i < 2; ++i) {
     phys[i] = reinterpret_cast<int32_t*>(ws);
     ws += align_up((size_t)batch->num_req * k * sizeof(int32_t), kWsAlign);
   }
   void* attn_wsp = ws;
+  // the one-layer step's launches: the threshold bin left to the attention,
+  // and (fp8 keys, one request) the histograms built by the scan
+  const bool defer = mla_resolves(batch->num_req, n_heads, k) &&
+                     topk_can_defer(batch->num_req, batch->max_seq_len);
+  bool scan_hist = defer;
+  for (int l = 0; l < n_layers && scan_hist; l += retention)
+    scan_hist = ikeys[l].dtype == LSI_FP8_E4M3 &&
+                scan_builds_hist(batch->num_req, batch->max_seq_len, ikeys[l].page_size);
+  const int64_t st_words = (int64_t)batch->num_req * kHistReps * kHistWords;
 
   const bool mli = schedule == LSI_SCHED_MLI;
   const bool split = mli && s_index != nullptr && s_index != stream;
@@ -674,10 +698,16 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t sched
   // `pending`: a selection made on si that `stream` has not waited for yet.
   // There is at most one: the next layer that reads it waits before the next
   // indexer records the event again.
+  // MLI: when the last layer has an indexer, no attention of this call reads
+  // the last selection, so nothing would resolve a threshold bin left open:
+  // that selection is finished by the top-k itself
+  const int last_slot = (n_layers - 1) / retention;
+  const bool last_unread = mli && (n_layers - 1) % retention == 0 && last_slot >= 1;
   bool pending = false;
   for (int l = 0; l < n_layers; ++l) {
     const int slot = l / retention;
     const bool indexer = l % retention == 0;
+    const bool fin = last_unread && slot == last_slot;
     if (pending) {
       LSI_HIP(hipStreamWaitEvent(stream, ev.selected, 0));
       pending = false;
@@ -693,22 +723,35 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention, int32_t sched
         LSI_HIP(hipStreamWaitEvent(si, ev.attn_done, 0));
       }
       LSI_TRY(enqueue_select(&ikeys[l], &kv[l], batch, q_idx[l], n_idx_heads, idx_dim, w[l], k,
-                             idx[slot], count[slot], scores, ld, topk_ws, phys[slot & 1], si,
-                             "lsi_multilayer_decode"));
+                             idx[slot], count[slot], scores, ld, topk_ws[slot & 1], phys[slot & 1], si,
+                             "lsi_multilayer_decode", defer && !fin,
+                             scan_hist && !fin ? state[slot & 1] : nullptr));
       if (split) {
         LSI_HIP(hipEventRecord(ev.selected, si));
         pending = true;   // the next layer waits for it; this one does not
       }
     } else if (indexer) {
       LSI_TRY(enqueue_select(&ikeys[l], &kv[l], batch, q_idx[l], n_idx_heads, idx_dim, w[l], k,
-                             idx[slot], count[slot], scores, ld, topk_ws, phys[slot & 1], stream,
-                             "lsi_multilayer_decode"));
+                             idx[slot], count[slot], scores, ld, topk_ws[slot & 1], phys[slot & 1],
+                             stream, "lsi_multilayer_decode", defer,
+                             scan_hist ? state[slot & 1] : nullptr));
     }
+    // The first attention after a selection was made clears that
+    // selection's histograms (its top-k has read them): the layer's own
+    // (serial, and layer 0) or the previous slot's (an MLI indexer layer,
+    // whose own top-k may still be reading its own).
+    uint32_t* clear = nullptr;
+    if (scan_hist && indexer) clear = state[src & 1];
     LSI_TRY(enqueue_attend(&kv[l], nullptr, batch, q_attn[l], n_heads, dk, dv, idx[src], k,
                            sm_scale, out[l], lse[l], attn_wsp, phys[src & 1], stream,
-                           "lsi_multilayer_decode"));
+                           "lsi_multilayer_decode", defer ? topk_ws[src & 1] : nullptr,
+                           defer ? idx[src] : nullptr, clear, clear ? st_words : 0));
   }
   if (pending) LSI_HIP(hipStreamWaitEvent(stream, ev.selected, 0));
+  // MLI: the last selection's histograms (when the scan built them) were
+  // read by its top-k but cleared by no attention
+  if (scan_hist && mli && last_slot >= 1 && !last_unread)
+    LSI_HIP(launch_zero(state[last_slot & 1], st_words, stream));
 #undef LSI_HIP
   return check_launch("lsi_multilayer_decode");
 }

@@ -220,7 +220,10 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
     topk::resolve_members<kMThreads>(tw, b, a.tk_max_len, a.k, reinterpret_cast<uint32_t*>(kvs), rtmp, r0, r1,
                                      [&](int slot, int pos, int row) {
                                        rows_all[slot - r0] = (row < 0 || row >= n_rows_pool) ? -1 : row;
-                                       if (hg == 0) a.idx_out[(int64_t)b * a.k + slot] = pos;
+                                       if (hg == 0) {
+                                         a.idx_out[(int64_t)b * a.k + slot] = pos;
+                                         if (a.phys_out) a.phys_out[(int64_t)b * a.k + slot] = row;
+                                       }
                                      });
   }
   __syncthreads();

@@ -133,6 +133,10 @@ struct AttnArgs {
   void* tk_ws = nullptr;
   int tk_max_len = 0;
   int32_t* idx_out = nullptr;      // [num_req][k], receives the resolved positions
+  // optional [num_req][k] (the phys array itself): receives the resolved
+  // physical rows, so that later attentions over the same selection find no
+  // slot left to resolve
+  int32_t* phys_out = nullptr;
   // optional: clear this many uint32 words at zero_ptr (grid-stride; the
   // scan-built histograms, once the selection has read them)
   uint32_t* zero_ptr = nullptr;

@@ -350,7 +350,9 @@ class Layers:
         self.c_idx, self.c_count = _ptr_array(self.idx), _ptr_array(self.count)
         self.c_out, self.c_lse = _ptr_array(self.out), _ptr_array(self.lse)
         nb = multilayer_workspace_bytes(B, req.max_seq_len, k, H, dv)
-        self.ws = _ws(nb, dev)
+        # zero-filled: its leading state words must be on first use (each
+        # successful call leaves them zero)
+        self.ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
 
 
 def multilayer_decode(layers: Layers, sm_scale: float, schedule: str = "mli", stream=None,

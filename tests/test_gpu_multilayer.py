@@ -135,3 +135,60 @@ def test_multilayer_mli_graph_replays_match_eager():
                 check_attention(t[b].float().cpu().numpy(), a[b].cpu().numpy().astype(np.float64),
                                 f"replay {rep} layer {l} req {b}")
     _check(dis, layers, 2, "mli", "graph")
+
+
+def _state_is_zero(layers):
+    n = 2 * lsi.lib().lsi_decode_step_state_bytes(1)
+    return int(torch.count_nonzero(layers.ws[:n]).item()) == 0
+
+
+@pytest.mark.parametrize("retention,sched", [(1, "serial"), (1, "mli"), (2, "mli"), (3, "serial")])
+def test_multilayer_long_request_takes_the_one_step_launches(retention, sched):
+    """One request longer than 32768 positions: every indexer layer runs the
+    one-layer step's launches (the scan builds the top-k histograms, the
+    attention resolves the threshold bin), with two sets of that state
+    alternating between selection slots; every selection and output is
+    checked against the oracle and the state words are zero afterwards."""
+    wl = _wl([70001], 2048)
+    dis, layers = _build(wl, 4, retention)
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        lsi.multilayer_decode(layers, wl.sm_scale, sched, index_stream=side)
+        torch.cuda.synchronize()
+        assert _state_is_zero(layers), rep
+    _check(dis, layers, retention, sched, f"long r={retention} {sched}")
+
+
+def test_multilayer_long_request_graph_replays_match_eager():
+    wl = _wl([70001], 2048)
+    dis, layers = _build(wl, 4, 1)
+    side = torch.cuda.Stream()
+
+    def run():
+        lsi.multilayer_decode(layers, wl.sm_scale, "mli", index_stream=side)
+
+    run()
+    torch.cuda.synchronize()
+    e_idx = [torch.sort(t, dim=1).values.clone() for t in layers.idx]
+    e_out = [t.float().clone() for t in layers.out]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in layers.idx:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _state_is_zero(layers), rep
+        for a, t in zip(e_idx, layers.idx):
+            assert torch.equal(a, torch.sort(t, dim=1).values), rep
+        for l, (a, t) in enumerate(zip(e_out, layers.out)):
+            check_attention(t[0].float().cpu().numpy(), a[0].cpu().numpy().astype(np.float64),
+                            f"replay {rep} layer {l}")
+    _check(dis, layers, 1, "mli", "long graph")
