@@ -102,8 +102,10 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     if args.only_extra:
-        print(json.dumps({"other_workloads": other_workloads(lsi, synth, torch, dev,
-                                                             tuple(args.extra.split(",")))}))
+        res = {"other_workloads": other_workloads(lsi, synth, torch, dev, tuple(args.extra.split(",")))}
+        if args.calib_copy:
+            res["calib_copy_bytes"] = calib_copy(torch, dev)
+        print(json.dumps(res))
         return
     R = args.sets
     L = 131072
@@ -369,17 +371,22 @@ def main():
         res["other_workloads"] = other_workloads(lsi, synth, torch, dev, tuple(args.extra.split(",")))
 
     if args.calib_copy:
-        # a plain elementwise copy of known size (512 MiB read, 512 MiB
-        # written per launch) for scaling the FETCH_SIZE / WRITE_SIZE counters
-        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)      # 512 MiB written (and read)
-            src.sum()                         # 512 MiB read, nothing written
-        torch.cuda.synchronize()
-        res["calib_copy_bytes"] = 512 << 20
+        res["calib_copy_bytes"] = calib_copy(torch, dev)
 
     print(json.dumps(res))
+
+
+def calib_copy(torch, dev):
+    """A plain elementwise copy of known size (512 MiB read, 512 MiB written
+    per launch) and a plain sum (512 MiB read), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters of the same run."""
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)      # 512 MiB written (and read)
+        src.sum()                         # 512 MiB read, nothing written
+    torch.cuda.synchronize()
+    return 512 << 20
 
 
 def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
