@@ -391,7 +391,18 @@ __device__ __forceinline__ void lds_read_tile2_scale(u32x4 (&kr)[2], float& sc, 
 }
 
 // Wait until the tile issued RING - 1 refills ago has landed: every refill
-// is OPS vector-memory operations.
+// is OPS vector-memory operations.  Why a count suffices (AMD's CDNA3
+// Instruction Set Architecture reference guide, "Data Dependency
+// Resolution" and the s_waitcnt description; the CDNA4 guide keeps the
+// rule): VM_CNT counts the wave's vector-memory instructions that have not
+// completed, and vector-memory loads complete in the order they were
+// issued, so waiting until VM_CNT <= n means every load but the last n has
+// completed.  A global load with the LDS modifier (global_load_lds_dwordx4,
+// the "load to LDS" form of the buffer/global instructions) is such a load:
+// it increments VM_CNT at issue and decrements it once its data are
+// written to LDS.  The score stores a wave issues between refills are
+// vector-memory operations too; they only add to the count behind the
+// tile's loads, which makes the wait stricter, never looser.
 template <int RING, int OPS>
 __device__ __forceinline__ void wait_ring_tile() {
   static_assert(RING == 2 && (OPS == 5 || OPS == 3), "two-slot ring of fp8 or int4 tiles");
