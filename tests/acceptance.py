@@ -60,10 +60,13 @@ def check_topk(gpu_idx, gpu_count, ref_scores, k, what=""):
 def exact_topk_f32(scores, k):
     """Positions of the k best of float32 scores (fewer when there are fewer),
     ranked as the kernels rank them: by the order-preserving integer key of
-    the float (so -0 < +0), equal keys by position ascending.  Sorted."""
+    the float (-0 folded onto +0, NaN below -inf), equal keys by position
+    ascending.  Sorted."""
     s = np.ascontiguousarray(np.asarray(scores, dtype=np.float32))
     b = s.view(np.uint32).astype(np.uint64)
+    b = np.where(b == 0x80000000, 0, b)
     key = np.where(b >> 31 == 1, b ^ 0xFFFFFFFF, b | 0x80000000)
+    key = np.where(np.isnan(s), 0, key)
     order = np.lexsort((np.arange(s.size), -key.astype(np.int64)))
     return np.sort(order[:min(k, s.size)])
 
