@@ -485,7 +485,7 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
         res = {"tokens": L, "n_cand": 8192, "k": 2048}
         for planted in (True, False):
             wl = synth.TWO_STAGE_512K
-            di = synth.make_decode_inputs(wl, device=dev, with_int4=True, with_attn=False,
+            di = synth.make_decode_inputs(wl, device=dev, with_int4=True, with_attn=planted,
                                           planted=planted)
             ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
             ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
@@ -505,6 +505,21 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
                              "achieved_GB_s": byts / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                              "frac": byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}}
             if planted:
+                # the sparse MLA over the selection (128 heads), alone and
+                # after the search in one graph: the decode step over 524288
+                # tokens with the compact search as its indexer
+                kv = lsi.Cache(di.kv, None, "bf16", 576)
+                t_mla = graph_ms(lambda: lsi.sparse_mla_decode(kv, None, req, di.q_attn, idx,
+                                                               wl.sm_scale, 512), n=8)
+
+                def step():
+                    sel, _ = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048)
+                    lsi.sparse_mla_decode(kv, None, req, di.q_attn, sel, wl.sm_scale, 512)
+
+                t_step = graph_ms(step, n=4)
+                rec["mla_over_selection_us"] = t_mla * 1e3
+                rec["search_plus_mla_us"] = t_step * 1e3
+                del kv
                 # the original fp8 keys in pinned host memory: only the compact
                 # keys (68 B/token) occupy GPU memory; the rescoring reads the
                 # 8192 candidates' rows across the host bus

@@ -120,6 +120,13 @@ def test_two_stage_512k(planted):
     assert rec >= rec4 - 1e-9
     if planted:
         assert rec == 1.0
+    # the sparse attention over the two-stage selection
+    kv = lsi.Cache(di.kv, None, "bf16", 576)
+    out, lse = lsi.sparse_mla_decode(kv, None, req, di.q_attn, idx, wl.sm_scale, 512)
+    torch.cuda.synchronize()
+    ro, rl = ov.attention(0, fin)
+    check_attention(out[0].float().cpu().numpy(), ro, "attention over the two-stage selection")
+    assert np.allclose(lse[0].cpu().numpy(), rl, rtol=1e-4, atol=1e-4)
 
 
 def test_prefill_chunk_4096_over_65536():
