@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle as O
-from acceptance import OracleView, check_attention, check_scores, check_topk
+from acceptance import OracleView, check_attention, check_scores, check_topk, exact_topk_f32
 from lightning_indexer_top_04_amd import lsi, synth
 
 pytestmark = pytest.mark.gpu
@@ -321,6 +321,63 @@ def test_two_stage_ragged_against_oracle(host):
         pos = np.full(k, -1)
         pos[:len(fin)] = np.searchsorted(c_sorted, fin)
         check_topk(pos, cnt[b], I8, k, f"stage 2 req {b}")
+
+
+def test_two_stage_long_ragged_rows_against_oracle():
+    """Rows longer than 32768 take the multi-workgroup first top-k with
+    digits over each row's key range (reduced from the int4 scan's
+    per-workgroup slots, here from the balanced multi-request grid); a row
+    shorter than n_cand keeps everything.  Stage 1 equals the exact top
+    n_cand of the scan's own int4 scores; both stages against the oracle."""
+    lens, n_cand, k = [70000, 40000, 5000], 8192, 2048
+    di, idx, cnt, cand = _two_stage_case(False, lens, n_cand, k, 23)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, max(lens))
+    s4 = lsi.index_scores(ik4, req, di.q_idx, di.w).cpu().numpy()
+    ov = OracleView(di)
+    for b, L in enumerate(lens):
+        nc = min(n_cand, L)
+        assert np.array_equal(np.sort(cand[b, :nc]), exact_topk_f32(s4[b, :L], n_cand)), b
+        K4, sc4 = ov.keys4(b)
+        I4 = O.index_scores(ov.q_idx[b], ov.w[b], K4, sc4)
+        check_topk(cand[b], nc, I4, n_cand, f"stage 1 req {b}")
+        c_sorted = np.sort(cand[b, :nc])
+        K8, s8 = ov.keys(b)
+        I8 = O.index_scores(ov.q_idx[b], ov.w[b], K8[c_sorted], s8[c_sorted])
+        fin = idx[b, :cnt[b]]
+        assert set(fin.tolist()) <= set(c_sorted.tolist())
+        pos = np.full(k, -1)
+        pos[:len(fin)] = np.searchsorted(c_sorted, fin)
+        check_topk(pos, cnt[b], I8, k, f"stage 2 req {b}")
+
+
+def test_two_stage_key_range_digits_with_a_tie_across_the_threshold():
+    """20000 tokens share one compact key (and scale) whose score ranks near
+    the 4000th: the threshold of the 8192 candidates falls inside that tie,
+    which the key-range digits cannot split, so positions decide (the lowest
+    kept).  Stage 1 must equal the exact top-8192 of the scan's own scores."""
+    wl = synth.scaled(synth.TWO_STAGE_512K, seq_lens=(70001,), num_req=1, n_planted=0, seed=29)
+    di = synth.make_decode_inputs(wl, device=DEV, with_int4=True, with_attn=False, planted=False)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    req = lsi.Requests(di.seq_lens, di.page_table, 70001)
+    s4 = lsi.index_scores(ik4, req, di.q_idx, di.w)[0, :70001].cpu().numpy()
+    src = int(np.argsort(-s4.astype(np.float64), kind="stable")[4000])
+    pt = di.page_table[0].cpu().numpy()
+    pos = np.arange(10000, 30000)
+    pages = torch.from_numpy(pt[pos // synth.PAGE].astype(np.int64)).to(DEV)
+    slots = torch.from_numpy(pos % synth.PAGE).to(DEV)
+    sp, ss = int(pt[src // synth.PAGE]), src % synth.PAGE
+    di.ikeys4[pages, slots] = di.ikeys4[sp, ss].clone()
+    di.iscale4[pages, slots] = di.iscale4[sp, ss].clone()
+    s4 = lsi.index_scores(ik4, req, di.q_idx, di.w)[0, :70001].cpu().numpy()
+    idx, cnt, cand = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, 8192, 2048, want_cand=True)
+    torch.cuda.synchronize()
+    got = np.sort(cand[0].cpu().numpy())
+    want = exact_topk_f32(s4, 8192)
+    assert np.array_equal(got, want)
+    tied = np.isin(want, pos)
+    assert 0 < tied.sum() < 20000   # the threshold lies inside the tie
 
 
 def test_two_stage_host_originals_equal_device_and_pageable_is_rejected():
