@@ -201,6 +201,31 @@ def test_prefill_small_history_and_partial_blocks():
         assert np.array_equal(np.sort(got[:n]), exact_topk_f32(sc[i, :vis].cpu().numpy(), k))
 
 
+def test_prefill_chunk_without_history():
+    """hist_len = 0: only the chunk's own keys, causal; every row's selection
+    against the oracle and exactly the top-k of the kernel's own scores."""
+    wl = synth.scaled(synth.PREFILL_CHUNK, seq_lens=(0,), chunk=100, block_tokens=256, seed=17)
+    pi = synth.make_prefill_inputs(wl, device=DEV)
+    k = 64
+    empty_k = pi.keys[:0]
+    empty_s = pi.scale[:0]
+    idx, cnt, sc = lsi.prefill_index_topk(empty_k, empty_s, pi.keys, pi.scale, pi.q, pi.w, k, 256,
+                                          want_scores=True)
+    torch.cuda.synchronize()
+    keys = O.decode_e4m3fn(synth.u8_bits(pi.keys))
+    scale = pi.scale.cpu().double().numpy()
+    q = O.decode_bf16(synth.bf16_bits(pi.q))
+    w = pi.w.cpu().double().numpy()
+    res = O.prefill_index_topk(q, w, keys, scale, 0, k)
+    for i in range(100):
+        sel_ref, tau, s_ref = res[i]
+        vis = i + 1
+        got = idx[i].cpu().numpy()
+        check_topk(got, cnt[i].item(), s_ref, k, f"row {i}")
+        n = min(k, vis)
+        assert np.array_equal(got[:n], exact_topk_f32(sc[i, :vis].cpu().numpy(), k))
+
+
 @pytest.mark.parametrize("pattern,k", [("equal", 700), ("rising", 700), ("falling", 700),
                                        ("equal", 1), ("rising", 1), ("rising", 37), ("falling", 37)])
 def test_prefill_running_selection_under_ties_and_monotone_scores(pattern, k):
