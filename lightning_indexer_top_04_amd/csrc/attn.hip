@@ -17,10 +17,12 @@
 //                      V read with ds_read_b64_tr_b16, which hands each lane
 //                      four rows of one value dim straight from the row-major
 //                      rows in LDS
+// Every LDS operand of a block is read before the block's first MFMA (an
+// MFMA waiting on its own read pays the LDS latency once per MFMA).
 // The workgroups of one slice (all head groups) are given block ids that are
 // equal modulo 8, so they run on one XCD and share its L2 for the rows.
 // Splits of the selection are merged with their log-sum-exp by a small
-// combine kernel.
+// combine kernel, from bf16 partials of the normalised outputs.
 #include "lsi_internal.hpp"
 #include "topk_common.hpp"
 
@@ -134,24 +136,25 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 }
 
 __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int rows_per_split,
-                                                                int nsplit, int units, float* part_o,
+                                                                int nsplit, int units, __bf16* part_o,
                                                                 float* part_lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t kvs[kKvBytes];
   __shared__ __attribute__((aligned(16))) __bf16 Pl[kMH * kPStride];
   __shared__ float red_m[4][kMH];
   __shared__ float red_l[4][kMH];
   __shared__ float alpha_s[kMH];
-  __shared__ int rows_all[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) int rows_all[kMaxSplitRows];
   // the 16 heads' query rows (16 x 1152 bytes), moved in once per workgroup:
   // chunk j (16 bytes) of head n at position 72 n + ((j & ~7) | ((j ^ n) & 7)),
   // so that the 16 heads' reads of one chunk spread over the banks
   __shared__ __attribute__((aligned(1024))) uint8_t qlds[kMH * kD * 2];
   __shared__ uint32_t rtmp[32];
 
-  // Block ids map to XCDs round-robin (bid % 8).  Every split of one head
-  // group of one request runs on one XCD, so the combine of that group (placed
-  // on the same XCD) reads their partials from that XCD's L2; the selected
-  // rows, shared by all head groups, are what crosses XCDs instead.
+  // Block ids map to XCDs round-robin (bid % 8).  Every head group of one
+  // (request, slice) unit runs on the XCD of that unit, so each selected row
+  // is fetched from memory into one L2 and read there by the 8 head groups;
+  // the partials, 16 KB of bf16 per workgroup, are what crosses XCDs instead
+  // (written through to memory, sc1).
   if (a.zero_ptr) {
     // clear the scan-built histograms the selection has read (they must be
     // zero when the next scan starts)
@@ -161,19 +164,17 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   }
   const int n_hg = a.n_heads / kMH;
   const int bid = blockIdx.x;
-  const int jx = bid >> 3;
-  const int inst = 8 * (jx / nsplit) + (bid & 7);     // (request, head group) instance
-  const int split = jx % nsplit;
-  if (inst >= a.num_req * n_hg) return;
-  const int b = inst / n_hg;
-  const int hg = inst % n_hg;
-  (void)units;
+  // unit u = (request, split) on XCD u % 8 with all its head groups
+  const int u = (bid / (8 * n_hg)) * 8 + (bid & 7);
+  const int hg = (bid >> 3) % n_hg;
+  if (u >= units) return;
+  const int b = u / nsplit;
+  const int split = u % nsplit;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int head = hg * kMH + n;               // this lane's head in the S layout
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int r0 = split * rows_per_split;
   const int r1 = min(r0 + rows_per_split, a.k);
@@ -228,10 +229,10 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   }
   __syncthreads();
 
-  // query operand of S^T = K Q^T: lane (n, g) holds Q[head][32t + 8g .. +7],
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head n][32t + 8g .. +7],
   // read from qlds after the first block's wait (every wave needs all 16
-  // heads; one DMA of the group's rows per workgroup instead of a load per
-  // wave, which had the workgroups of one XCD queue on the same L2 lines)
+  // heads: one DMA of the group's rows per workgroup instead of a load per
+  // wave, which doubled the gather's L2 requests)
   const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
                                                        ((int64_t)b * a.n_heads + hg * kMH) * kD);
   bf16x8 qr[kD / 32];
@@ -283,30 +284,42 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
       }
     }
 
-    // ---- S^T for rows 16w + (0..15): A = K rows from LDS, B = Q^T
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T for rows 16w + (0..15): A = K rows from LDS, B = Q^T.  Every
+    // LDS read is issued before the first MFMA (an MFMA waiting on its own
+    // read pays the LDS latency 18 times), two accumulators halve the chain.
+    f32x4 sacc;
     {
       const int row = 16 * w + n;                  // A-operand row of this lane
       const uint8_t* vrow = kvs + row * kVRow;
       const uint8_t* rrow = kvs + kRopeOff + (row >> 3) * 1024 + (row & 7) * 128;
+      bf16x8 av[kD / 32];
 #pragma unroll
       for (int t = 0; t < kD / 32; ++t) {
-        bf16x8 av;
         if (t < 16) {
-          av = *reinterpret_cast<const bf16x8*>(vrow + 16 * ((4 * t + g) ^ (row & 15)));
+          av[t] = *reinterpret_cast<const bf16x8*>(vrow + 16 * ((4 * t + g) ^ (row & 15)));
         } else {
-          av = *reinterpret_cast<const bf16x8*>(rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7)));
+          av[t] = *reinterpret_cast<const bf16x8*>(rrow + 16 * ((4 * (t - 16) + g) ^ (row & 7)));
         }
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qr[t], sacc, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kD / 32; t += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], qr[t], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t + 1], qr[t + 1], s1, 0, 0, 0);
+      }
+      sacc = s0 + s1;
     }
     // lane (n, g) holds S^T[row 16w + 4g + r][head n]
     float x[4];
+    {
+      const int4 rv = *reinterpret_cast<const int4*>(&rows_all[base + 16 * w + 4 * g]);
+      const int rr[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = 16 * w + 4 * g + r;
-      const bool ok = rl < nb && rows_all[base + rl] >= 0;
-      x[r] = ok ? sacc[r] * c : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 16 * w + 4 * g + r < nb && rr[r] >= 0;
+        x[r] = ok ? sacc[r] * c : -INFINITY;
+      }
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max4rows(mx);
@@ -346,38 +359,47 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
     const int s16 = lane & 15;                 // source lane of the transpose reads
     const int ja = s16 >> 2;                   // row offset within the group of 4
     const int aa = s16 & 3;                    // 4-dim column group
-#pragma unroll 1
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pl[n * kPStride + 32 * kk + 8 * g]);
-      const int ra = 32 * kk + 8 * g + ja;     // rows ra and ra + 4
+    {
+      // all LDS reads of the block first, then the 16 MFMAs
+      bf16x8 pa[2];
+      s16x4 v0[2][8], v1[2][8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ch = (128 * w + 16 * t + 4 * aa) >> 3;    // 16-byte chunk of the dim group
-        const int hb = 8 * (aa & 1);
-        const s16x4 v0 = lds_read_tr16(kvs + ra * kVRow + 16 * (ch ^ (ra & 15)) + hb);
-        const s16x4 v1 = lds_read_tr16(kvs + (ra + 4) * kVRow + 16 * (ch ^ ((ra + 4) & 15)) + hb);
-        const short vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        bf16x8 vb;
+      for (int kk = 0; kk < 2; ++kk) {
+        pa[kk] = *reinterpret_cast<const bf16x8*>(&Pl[n * kPStride + 32 * kk + 8 * g]);
+        const int ra = 32 * kk + 8 * g + ja;     // rows ra and ra + 4
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vb[e] = __builtin_bit_cast(__bf16, vv[e]);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+        for (int t = 0; t < 8; ++t) {
+          const int ch = (128 * w + 16 * t + 4 * aa) >> 3;    // 16-byte chunk of the dim group
+          const int hb = 8 * (aa & 1);
+          v0[kk][t] = lds_read_tr16(kvs + ra * kVRow + 16 * (ch ^ (ra & 15)) + hb);
+          v1[kk][t] = lds_read_tr16(kvs + (ra + 4) * kVRow + 16 * (ch ^ ((ra + 4) & 15)) + hb);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const short vv[8] = {v0[kk][t][0], v0[kk][t][1], v0[kk][t][2], v0[kk][t][3],
+                               v1[kk][t][0], v1[kk][t][1], v1[kk][t][2], v1[kk][t][3]};
+          bf16x8 vb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vb[e] = __builtin_bit_cast(__bf16, vv[e]);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk], vb, o[t], 0, 0, 0);
+        }
       }
     }
     __syncthreads();   // the block's LDS is refilled next
   }
 
-  // ---- results: per-head statistics to the output layout through LDS
-  if (w == 0 && g == 0) {
-    red_m[0][n] = m_run;
-    red_l[0][n] = l_run;
-  }
-  __syncthreads();
+  // ---- results: the per-head statistics (every wave holds head n's in
+  // lanes n, n + 16, ...) moved to the output layout by lane shuffles
   const int dim0 = 128 * w + n;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int hl = 4 * g + r;
-    const float lr = red_l[0][hl];
-    const float mr = red_m[0][hl];
+    const float lr = __shfl(l_run, hl);
+    const float mr = __shfl(m_run, hl);
     const float inv = lr > 0.f ? 1.f / lr : 0.f;
     const float lse2 = lr > 0.f ? mr + log2f(lr) : -INFINITY;
     const int64_t bh = (int64_t)b * a.n_heads + hg * kMH + hl;
@@ -387,9 +409,14 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
       for (int t = 0; t < 8; ++t) ob[16 * t] = (__bf16)(o[t][r] * inv);
       if (w == 0 && n == 0) a.lse[bh] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
     } else {
-      float* po = part_o + (bh * nsplit + split) * kDV + dim0;
+      // bf16 partial, dims in lane order (dim 128w + 16t + n at 128w + 8n + t):
+      // one 16-byte store per head, written through to memory for the
+      // combine, which reads it from another XCD
+      u32x4 v;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) po[16 * t] = o[t][r] * inv;
+      for (int t = 0; t < 4; ++t) v[t] = pack_bf16x2(o[2 * t][r] * inv, o[2 * t + 1][r] * inv);
+      __bf16* po = part_o + (bh * nsplit + split) * kDV + 128 * w + 8 * n;
+      asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(po), "v"(v) : "memory");
       if (w == 0 && n == 0) part_lse[bh * nsplit + split] = lse2;
     }
   }
@@ -721,6 +748,58 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
   if (threadIdx.x == 0) a.lse[bh] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
+// Merge of the 16-head kernel's bf16 partials (dims in lane order: dim
+// 128w + 16t + n stored at 128w + 8n + t): out = sum_s 2^(lse_s - M) o_s /
+// sum_s 2^(lse_s - M).  One workgroup of two waves per (request, head), four
+// stored dims per thread; every wave works out the split weights itself and
+// broadcasts them from the lanes that hold them.
+__global__ __launch_bounds__(128) void mla_combine_bf16_kernel(AttnArgs a, int nsplit,
+                                                                const __bf16* part_o,
+                                                                const float* part_lse) {
+  constexpr int kBatch = 32;     // splits loaded before any is used
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const float* pl = part_lse + bh * nsplit;
+  const __bf16* pb = part_o + bh * nsplit * kDV + 4 * tid;
+  // nsplit <= 64: lane s holds split s's log-sum-exp
+  const float ls = lane < nsplit ? pl[lane] : -INFINITY;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, wgt = 0.f, wsum = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    const int nb = min(kBatch, nsplit - s0);
+    u32x2 v[kBatch];
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s) v[s] = *reinterpret_cast<const u32x2*>(pb + (int64_t)(s0 + min(s, nb - 1)) * kDV);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s0 == 0) {
+      M = ls;
+      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      wgt = (M == -INFINITY || ls == -INFINITY) ? 0.f : exp2f(ls - M);
+      wsum = wgt;
+      for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
+    }
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s) {
+      if (s < nb) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s0 + s));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[2 * j] += ws * __uint_as_float(v[s][j] << 16);
+          acc[2 * j + 1] += ws * __uint_as_float(v[s][j] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  // stored dims 4 tid .. 4 tid + 3 = 128w + 8n + t0 + i hold dims 128w + 16 (t0 + i) + n
+  const int w = tid >> 5, n = (tid & 31) >> 1, t0 = 4 * (tid & 1);
+  __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV + 128 * w + 16 * t0 + n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ob[16 * i] = (__bf16)(acc[i] * inv);
+  if (tid == 0) a.lse[bh] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------
 // fp32 generic path: separate K and V caches, one K/V head, any head count.
 // One workgroup per (request, head); rows in blocks of 256, online softmax.
@@ -832,6 +911,8 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
   const MlaPlan p = plan_mla(a.num_req, a.n_heads, a.k);
   const int nsplit = p.nsplit;
   const int rows_per_split = p.rows_per_split;
+  // partials: [num_req * n_heads][nsplit][dv] (fp32 for the 32-head kernel,
+  // bf16 for the 16-head one), then the [num_req * n_heads][nsplit] log-sum-exps
   float* part_o = static_cast<float*>(a.ws);
   float* part_lse = part_o ? part_o + (size_t)a.num_req * a.n_heads * nsplit * kDV : nullptr;
   const int units = a.num_req * nsplit;
@@ -839,19 +920,23 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
     const int grid = (int)ceil_div(units, 8) * 8 * (a.n_heads / kWH);
     launch(mla_bf16_wide_kernel, dim3(grid), dim3(kWThreads), 0, s, "mla_bf16_wide_kernel", a, rows_per_split, nsplit,
                        units, part_o, part_lse);
+    if (nsplit > 1) {
+      // one block per (request, head), laid out so that head group instance
+      // i (16 heads) lands on XCD i % 8
+      const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
+      launch(mla_combine_kernel, dim3((unsigned)(8 * 16 * ceil_div(inst, 8))), dim3(kDV / 4), 0, s,
+             "mla_combine_kernel", a, nsplit, part_o, part_lse);
+    }
   } else {
-    // 8 XCDs x (head group instances per XCD) x splits
-    const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
-    const int grid = (int)(8 * ceil_div(inst, 8) * nsplit);
-    launch(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, "mla_bf16_kernel", a, rows_per_split, nsplit,
-                       units, part_o, part_lse);
-  }
-  if (nsplit > 1) {
-    // one block per (request, head), laid out so that head group instance i
-    // (16 heads) lands on XCD i % 8 like its partials
-    const int64_t inst = (int64_t)a.num_req * (a.n_heads / kMH);
-    launch(mla_combine_kernel, dim3((unsigned)(8 * 16 * ceil_div(inst, 8))), dim3(kDV / 4), 0, s, "mla_combine_kernel",
-                       a, nsplit, part_o, part_lse);
+    // 8 XCDs x (units per XCD) x head groups: unit u with all its head groups
+    // on XCD u % 8
+    const int grid = (int)(8 * ceil_div(units, 8) * (a.n_heads / kMH));
+    __bf16* part_b = reinterpret_cast<__bf16*>(part_o);
+    launch(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, "mla_bf16_kernel", a, rows_per_split, nsplit, units,
+           part_b, part_lse);
+    if (nsplit > 1)
+      launch(mla_combine_bf16_kernel, dim3((unsigned)(a.num_req * a.n_heads)), dim3(128), 0, s,
+             "mla_combine_bf16_kernel", a, nsplit, part_b, part_lse);
   }
   return hipGetLastError();
 }
