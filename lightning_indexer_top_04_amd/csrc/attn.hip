@@ -184,6 +184,16 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   // looked up through the page table); -1 = skip
   constexpr int kRowsPerThread = kMaxSplitRows / kMThreads;
   const int n_rows_pool = a.num_pages * a.page_size;
+  // a deferred selection's record (count above the threshold bin, members),
+  // loaded by the last thread together with the row ids (one round trip for
+  // both; a load by one lane is not made uniform and waited for at once)
+  // and handed over through LDS
+  uint32_t rec_v[2] = {0u, 0u};
+  if (a.tk_ws != nullptr && tid == kMThreads - 1) {
+    const uint32_t* rec = topk::carve(a.tk_ws, a.num_req, a.tk_max_len).rec + (size_t)b * 4;
+    rec_v[0] = rec[1];
+    rec_v[1] = rec[2];
+  }
   int prow[kRowsPerThread];
   if (a.phys) {
 #pragma unroll
@@ -212,13 +222,20 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
     if (e < nr) rows_all[e] = (prow[i] < 0 || prow[i] >= n_rows_pool) ? -1 : prow[i];
     unresolved |= e < nr && prow[i] == kUnresolvedRow;
   }
+  if (tid == kMThreads - 1) {
+    rtmp[30] = rec_v[0];
+    rtmp[31] = rec_v[1];
+  }
   if (a.tk_ws != nullptr && __syncthreads_or(unresolved)) {
     // Part of this slice lies in a threshold bin that the top-k left open:
     // work out the kept members (every workgroup that needs them reaches the
     // same set and order) and take the rows of this slice's slots.  The
     // block buffer is free until the gather below.
     const topk::Ws tw = topk::carve(a.tk_ws, a.num_req, a.tk_max_len);
-    topk::resolve_members<kMThreads>(tw, b, a.tk_max_len, a.k, reinterpret_cast<uint32_t*>(kvs), rtmp, r0, r1,
+    const uint32_t rec_better = rtmp[30], rec_members = rtmp[31];
+    lds_barrier();   // rtmp is the resolve's scratch from here on
+    topk::resolve_members<kMThreads>(tw, b, a.tk_max_len, a.k, rec_better, rec_members,
+                                     reinterpret_cast<uint32_t*>(kvs), rtmp, r0, r1,
                                      [&](int slot, int pos, int row) {
                                        rows_all[slot - r0] = (row < 0 || row >= n_rows_pool) ? -1 : row;
                                        if (hg == 0) {

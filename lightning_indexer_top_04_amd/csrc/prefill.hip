@@ -47,14 +47,7 @@ constexpr int kWBins = 2048;    // bins of a wave's private LDS histogram (11-bi
 constexpr uint32_t kSlack = 64; // entries a pruning may keep beyond k
 constexpr int kGroup = 8;       // 128-entry chunks a pruning pass loads at once
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) { return wave_incl_sum(v); }
 
 // Over the wave's histogram h (kWBins words) in descending bin order, the
 // bin where the running count first reaches need (1 <= need <= total), the

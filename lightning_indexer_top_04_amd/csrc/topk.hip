@@ -501,13 +501,7 @@ __device__ void refine_cands(const TopkArgs& a, int r, uint32_t n, uint32_t need
 // (1 <= need <= total) and, in *before, the count of the positions ahead of
 // it; every lane gets both.
 __device__ __forceinline__ int wave_threshold64(uint32_t cnt, uint32_t need, uint32_t* before) {
-  const int lane = threadIdx.x & 63;
-  uint32_t inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const uint32_t inc = wave_incl_sum(cnt);
   const uint64_t m = __ballot(inc >= need);
   const int p = m ? __ffsll((unsigned long long)m) - 1 : 63;
   *before = __shfl(inc - cnt, p);

@@ -94,11 +94,16 @@ template <int NT, class T>
 __device__ T block_excl_scan(T v, T* tmp, T* total, bool lds_only = false) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  T inc = v;
+  T inc;
+  if constexpr (sizeof(T) == 4) {
+    inc = (T)wave_incl_sum((uint32_t)v);
+  } else {
+    inc = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
+    for (int o = 1; o < 64; o <<= 1) {
+      const T t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
   }
   if (lane == 63) tmp[wave] = inc;
   wg_sync(lds_only);
@@ -161,65 +166,133 @@ __device__ int find_threshold(const uint32_t* cnt, uint32_t need, bool desc, uin
 // one-workgroup refinement keeps.  The i-th kept member takes output slot
 // better + i.  Every workgroup that calls this computes the same thresholds
 // and the same order; put(slot, position, physical row) is called for the
-// slots in [lo, hi).  NT threads; hist (kBins words) and tmp (32 words) are
-// LDS.
+// slots in [lo, hi).  better and members are the record's (read by the
+// caller with its other first loads).  NT threads; hist (kBins words) and tmp
+// (32 words) are LDS.
 // ---------------------------------------------------------------------------
 template <int NT, class Put>
-__device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_t* hist, uint32_t* tmp,
-                                int lo, int hi, Put&& put) {
+__device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_t better, uint32_t members,
+                                uint32_t* hist, uint32_t* tmp, int lo, int hi, Put&& put) {
   constexpr int E = 8;                       // candidates per thread and batch
+  constexpr int NB = 2;                      // batches held in registers
+  constexpr int kHeld = NB * NT * E;         // candidates held (the rest streamed)
+  constexpr int per = kBins / NT;            // level-2 bins per thread
+  static_assert(per % 4 == 0 && kHeld < 65536, "register layout");
   const int tid = threadIdx.x;
-  const uint32_t* rec = ws.rec + (size_t)r * 4;
-  const uint32_t better = rec[1];
-  const uint32_t members = rec[2];
   const int2* cand = ws.cand + (size_t)r * max_len;
   const int32_t* crow = ws.crow + (size_t)r * max_len;
   const uint32_t* g2 = ws.h2 + (size_t)r * kBins;
   const uint32_t need = (uint32_t)k - better;
-  // the first batch of candidates (and their rows) comes in with the
-  // second histogram: one round trip for both
-  int2 e0[E];
-  int32_t w0[E];
+  // one round trip: the first kHeld candidates with their rows (thread t
+  // holds E consecutive ones per batch) and the second histogram (thread t
+  // the per bins kBins - per (t + 1) .. kBins - per t - 1, which it takes in
+  // descending order)
+  int2 e[NB][E];
+  int32_t rw[NB][E];
+  uint4 hq[per / 4];
 #pragma unroll
-  for (int u = 0; u < E; ++u) {
-    const uint32_t i = tid * E + u;
-    e0[u] = i < members ? cand[i] : make_int2(-1, 0);
-    w0[u] = i < members ? crow[i] : -1;
+  for (int b = 0; b < NB; ++b) {
+    const uint32_t i0 = b * NT * E + tid * E;
+    if (i0 + E <= (uint32_t)max_len && ((reinterpret_cast<uintptr_t>(cand) | reinterpret_cast<uintptr_t>(crow)) & 15) == 0) {
+      // whole 16-byte loads (inside the row's lists, aligned), masked below
+      const int4* c4 = reinterpret_cast<const int4*>(cand + i0);
+      const int4* r4 = reinterpret_cast<const int4*>(crow + i0);
+#pragma unroll
+      for (int u = 0; u < E / 2; ++u) {
+        const int4 x = c4[u];
+        e[b][2 * u] = make_int2(x.x, x.y);
+        e[b][2 * u + 1] = make_int2(x.z, x.w);
+      }
+#pragma unroll
+      for (int u = 0; u < E / 4; ++u) {
+        const int4 x = r4[u];
+        rw[b][4 * u] = x.x;
+        rw[b][4 * u + 1] = x.y;
+        rw[b][4 * u + 2] = x.z;
+        rw[b][4 * u + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const uint32_t i = i0 + u;
+        e[b][u] = i < members ? cand[i] : make_int2(-1, 0);
+        rw[b][u] = i < members ? crow[i] : -1;
+      }
+    }
   }
-  // f(pos, key) over every candidate, E consecutive ones per thread
+#pragma unroll
+  for (int j = 0; j < per / 4; ++j) hq[j] = reinterpret_cast<const uint4*>(g2 + kBins - per * (tid + 1))[j];
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t hv[per];    // hv[i]: count of bin kBins - 1 - (per t + i)
+#pragma unroll
+  for (int j = 0; j < per / 4; ++j) {
+    hv[per - 1 - 4 * j] = hq[j].x;
+    hv[per - 2 - 4 * j] = hq[j].y;
+    hv[per - 3 - 4 * j] = hq[j].z;
+    hv[per - 4 - 4 * j] = hq[j].w;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int u = 0; u < E; ++u)
+      if (b * NT * E + tid * E + u >= members) e[b][u] = make_int2(-1, 0);
+  // f(pos, key) over every candidate: the held batches, then the rest
   auto pass = [&](auto&& f) {
-    for (uint32_t base = 0; base < members; base += NT * E) {
-      int2 e[E];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int u = 0; u < E; ++u)
+        if (e[b][u].x >= 0) f(e[b][u].x, (uint32_t)e[b][u].y);
+    for (uint32_t base = kHeld; base < members; base += NT * E) {
+      int2 x[E];
 #pragma unroll
       for (int u = 0; u < E; ++u) {
         const uint32_t i = base + tid * E + u;
-        e[u] = i < members ? cand[i] : make_int2(-1, 0);
+        x[u] = i < members ? cand[i] : make_int2(-1, 0);
       }
 #pragma unroll
       for (int u = 0; u < E; ++u)
-        if (e[u].x >= 0) f(e[u].x, (uint32_t)e[u].y);
+        if (x[u].x >= 0) f(x[u].x, (uint32_t)x[u].y);
     }
   };
-  // level 2: key bits [19:8], histogram built by the select (every load
-  // issued before the first LDS store: one round trip, not one per load)
+  // level 2: key bits [19:8], histogram built by the select; the threshold
+  // bin (descending) from the per-thread sums, then in registers
+  uint32_t bin2, better2, n2;
   {
-    uint32_t hv[kBins / NT];
+    uint32_t local = 0;
 #pragma unroll
-    for (int m = 0; m < kBins / NT; ++m) hv[m] = g2[tid + m * NT];
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < per; ++i) local += hv[i];
+    uint32_t tot;
+    const uint32_t excl = block_excl_scan<NT>(local, tmp, &tot);
+    // branch-free walk of the thread's bins: the first whose running count
+    // reaches need
+    uint32_t acc = excl;
+    int fi = -1;
+    uint32_t fb = 0, fn = 0;
 #pragma unroll
-    for (int m = 0; m < kBins / NT; ++m) hist[tid + m * NT] = hv[m];
+    for (int i = 0; i < per; ++i) {
+      const bool hit = fi < 0 && acc + hv[i] >= need;
+      fi = hit ? i : fi;
+      fb = hit ? acc : fb;
+      fn = hit ? hv[i] : fn;
+      acc += hv[i];
+    }
+    if (excl < need && fi >= 0) {
+      tmp[24] = (uint32_t)(kBins - 1 - (per * tid + fi));
+      tmp[25] = fb;
+      tmp[26] = fn;
+    }
+    __syncthreads();
+    bin2 = tmp[24];
+    better2 = tmp[25];
+    n2 = tmp[26];
+    __syncthreads();
   }
-  __syncthreads();
-  uint32_t better2;
-  const uint32_t bin2 = (uint32_t)find_threshold<NT>(hist, need, true, tmp, &better2);
-  const uint32_t n2 = hist[bin2];
   const bool take2 = n2 <= need - better2;
   // level 3: key bits [7:0] of the members in bin2
   uint32_t bin3 = 0, take3 = 1, pos_t = 0;
   if (!take2) {
     const uint32_t need_b = need - better2;
-    __syncthreads();
     for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
     pass([&](int, uint32_t key) {
@@ -258,43 +331,58 @@ __device__ void resolve_members(const Ws& ws, int r, int max_len, int k, uint32_
     }
   }
   // the ordered pass: kept members in list order, slots better + running index
+  // (branch-free: a branchy test costs more than the loads it follows)
   auto kept = [&](int pos, uint32_t key) -> bool {
     const uint32_t d2 = (key >> 8) & (kBins - 1);
-    if (d2 != bin2) return d2 > bin2;
-    if (take2) return true;
     const uint32_t d3 = key & 255u;
-    if (d3 != bin3) return d3 > bin3;
-    return take3 || (uint32_t)pos <= pos_t;
+    const bool in3 = (d3 > bin3) | ((d3 == bin3) & ((take3 != 0u) | ((uint32_t)pos <= pos_t)));
+    return (d2 > bin2) | ((d2 == bin2) & (take2 | in3));
   };
-  uint32_t run = 0;
-  for (uint32_t base = 0; base < members && better + run < (uint32_t)hi; base += NT * E) {
-    int2 e[E];
-    int32_t rw[E];
-    uint32_t m = 0;
+  // the held batches: one scan of both counts (16 bits each)
+  uint32_t m[NB] = {0u, 0u};
 #pragma unroll
-    for (int u = 0; u < E; ++u) {
-      const uint32_t i = base + tid * E + u;
-      if (base == 0) {
-        e[u] = e0[u];
-        rw[u] = w0[u];
-      } else {
-        e[u] = i < members ? cand[i] : make_int2(-1, 0);
-        rw[u] = i < members ? crow[i] : -1;
-      }
-    }
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int u = 0; u < E; ++u)
-      if (e[u].x >= 0 && kept(e[u].x, (uint32_t)e[u].y)) m |= 1u << u;
-    uint32_t tot;
-    uint32_t o = run + block_excl_scan<NT>((uint32_t)__popc(m), tmp, &tot) + better;
+      m[b] |= (uint32_t)((e[b][u].x >= 0) & kept(e[b][u].x, (uint32_t)e[b][u].y)) << u;
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<NT>((uint32_t)__popc(m[0]) | ((uint32_t)__popc(m[1]) << 16), tmp, &tot);
+  const uint32_t tot0 = tot & 0xFFFFu;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    uint32_t o = better + (b == 0 ? (ex & 0xFFFFu) : tot0 + (ex >> 16));
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-      if ((m >> u) & 1u) {
-        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, e[u].x, rw[u]);
+      if ((m[b] >> u) & 1u) {
+        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, e[b][u].x, rw[b][u]);
         ++o;
       }
     }
-    run += tot;
+  }
+  uint32_t run = tot0 + (tot >> 16);
+  for (uint32_t base = kHeld; base < members && better + run < (uint32_t)hi; base += NT * E) {
+    int2 x[E];
+    int32_t xr[E];
+    uint32_t mm = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const uint32_t i = base + tid * E + u;
+      x[u] = i < members ? cand[i] : make_int2(-1, 0);
+      xr[u] = i < members ? crow[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < E; ++u)
+      if (x[u].x >= 0 && kept(x[u].x, (uint32_t)x[u].y)) mm |= 1u << u;
+    uint32_t t2;
+    uint32_t o = run + block_excl_scan<NT>((uint32_t)__popc(mm), tmp, &t2) + better;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      if ((mm >> u) & 1u) {
+        if (o >= (uint32_t)lo && o < (uint32_t)hi) put((int)o, x[u].x, xr[u]);
+        ++o;
+      }
+    }
+    run += t2;
   }
 }
 
