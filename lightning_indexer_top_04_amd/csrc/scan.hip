@@ -103,6 +103,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_gather_kernel(ScanArgs a, in
   const int begin = blockIdx.x * chunk;
   const int end = min(begin + chunk, n_items);
   const int ntile = max(0, (end - begin + kTile - 1) / kTile);
+  // the slice item of lane m in tile tile_in (clamped to the slice)
+  auto tile_item = [&](int tile_in) {
+    const int tile = min(tile_in, ntile - 1);
+    return min(begin + tile * kTile + m, end - 1);
+  };
+  // the positions of the wave's first two tiles are loaded before the query
+  // is prepared (their round trip overlaps that work); ntile >= 1 here, so
+  // the loads are unconditional and in bounds
+  const int pos_first0 = a.positions[(int64_t)b * a.n_pos + tile_item(wave)];
+  const int pos_first1 = a.positions[(int64_t)b * a.n_pos + tile_item(wave + kWaves)];
 
   // query operand: lane (m, h) holds head 32*mt+m, dims 64h+8t .. 64h+8t+7
   const __bf16* qb = static_cast<const __bf16*>(a.q) + (int64_t)b * kHeads * kDim;
@@ -208,11 +218,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_gather_kernel(ScanArgs a, in
   // clamped to the last tile of the slice, an out-of-range page or position
   // reads row 0 of the pool and is reported as -inf, and tokens past the end of
   // a request still lie inside their allocated page and are never stored.
-  auto fetch = [&](int tile_in) {
+  auto fetch_at = [&](int pos) {
     TileFetch f;
-    const int tile = min(tile_in, ntile - 1);
-    const int it = min(begin + tile * kTile + m, end - 1);
-    const int pos = a.positions[(int64_t)b * a.n_pos + it];
     const bool in = pos >= 0 && pos < L;
     const int page = a.page_table[(int64_t)b * a.max_pages + ((in ? pos : 0) >> page_shift)];
     const bool ok = in && page >= 0 && page < a.num_pages;
@@ -225,6 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_gather_kernel(ScanArgs a, in
     f.scale = ok ? sc : __uint_as_float(kAbsent);
     return f;
   };
+  auto fetch = [&](int tile_in) { return fetch_at(a.positions[(int64_t)b * a.n_pos + tile_item(tile_in)]); };
 
   // Consume tile `tile` held in f, refill f with the tile two wave-steps
   // ahead, then compute and store.  Two TileFetch registers form a ring that
@@ -283,8 +291,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_gather_kernel(ScanArgs a, in
   };
 
   if (wave < ntile) {
-    TileFetch f0 = fetch(wave);
-    TileFetch f1 = fetch(wave + kWaves);
+    TileFetch f0 = fetch_at(pos_first0);
+    TileFetch f1 = fetch_at(pos_first1);
     for (int tile = wave; tile < ntile; tile += 2 * kWaves) {
       consume(f0, tile);
       if (tile + kWaves >= ntile) break;

@@ -964,24 +964,32 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   constexpr int kStride = kRowThreads * kBatch;
   const int nbat = (L + kStride - 1) / kStride;
   uint32_t kr[NB][kBatch];
+  // the resident batches' slot-map entries come in with their scores (a
+  // winner's output value is then in a register, not one more round trip)
+  int mv[NB][kBatch];
+  const bool pre_map = LOOKUP && a.map != nullptr;
   {
     float x[NB][kBatch];
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        x[bi][j] = bi < nbat ? row[min(tid + bi * kStride + j * kRowThreads, L - 1)] : 0.f;
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = min(tid + bi * kStride + j * kRowThreads, L - 1);
+        x[bi][j] = bi < nbat ? row[i] : 0.f;
+        mv[bi][j] = pre_map && bi < nbat ? a.map[(int64_t)r * a.map_ld + i] : 0;
+      }
     issue_fence();
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) kr[bi][j] = bi < nbat ? float_key(x[bi][j]) : 0u;
   }
-  // f(b, keys) for every batch b of this thread, the resident ones first
+  // f(b, keys, map entries or nullptr) for every batch b of this thread, the
+  // resident ones first
   auto for_batches = [&](auto&& f) {
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
-      if (bi < nbat) f(tid + bi * kStride, kr[bi]);
+      if (bi < nbat) f(tid + bi * kStride, kr[bi], pre_map ? mv[bi] : nullptr);
     for (int b = tid + NB * kStride; b < L; b += kStride) {
       float x[kBatch];
 #pragma unroll
@@ -990,7 +998,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
       uint32_t kk[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) kk[j] = float_key(x[j]);
-      f(b, kk);
+      f(b, kk, static_cast<const int*>(nullptr));
     }
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -999,7 +1007,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     kmin = ~a.range[2 * (int64_t)r];
     kmax = a.range[2 * (int64_t)r + 1];
   } else {
-    for_batches([&](int, const uint32_t (&kk)[kBatch]) {
+    for_batches([&](int, const uint32_t (&kk)[kBatch], const int*) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         kmin = min(kmin, kk[j]);
@@ -1027,7 +1035,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   const int span = range ? 32 - __clz(range) : 0;      // bits of the range
   const int shift = span > 12 ? span - 12 : 0;
   // pass 1
-  for_batches([&](int b, const uint32_t (&kk)[kBatch]) {
+  for_batches([&](int b, const uint32_t (&kk)[kBatch], const int*) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) atomicAdd(&hist[(kk[j] - kmin) >> shift], b + j * kRowThreads < L ? 1u : 0u);
   });
@@ -1035,9 +1043,78 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
   uint32_t better;
   const uint32_t digit = (uint32_t)find_threshold<kRowThreads>(hist, (uint32_t)a.k, true, tmp, &better);
   int32_t* list = carve(a.ws, a.num_req, a.max_len).list + (size_t)r * a.max_len;
-  // pass 2
+  // pass 2.  Resident batches (a uniform loop): flags per thread, one block
+  // scan of the winner and member counts, then every thread writes its own
+  // (a ballot pair per element, as below, is about 3 us of issue at 1024
+  // threads).  Streamed batches: per-wave ballots and LDS counters.
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi < nbat) {
+      const int b = tid + bi * kStride;
+      uint32_t win = 0, eq = 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const bool in = b + j * kRowThreads < L;
+        const uint32_t d = (kr[bi][j] - kmin) >> shift;
+        win |= (uint32_t)(in && d > digit) << j;
+        eq |= (uint32_t)(in && d == digit) << j;
+      }
+      const uint32_t base_w = cnt[0], base_e = cnt[1];   // read before the scan's barriers
+      uint32_t tot;
+      const uint32_t pre =
+          block_excl_scan<kRowThreads>((uint32_t)__popc(win) | ((uint32_t)__popc(eq) << 16), tmp, &tot, true);
+      uint32_t ow = base_w + (pre & 0xFFFFu), oe = base_e + (pre >> 16);
+      int wv[kBatch], wp[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = b + j * kRowThreads;
+        wv[j] = ((win >> j) & 1u) ? (LOOKUP ? (pre_map ? mv[bi][j] : out_value(a, r, i)) : i) : -1;
+      }
+      if constexpr (LOOKUP) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) wp[j] = a.phys ? phys_of(a, r, wv[j]) : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if ((win >> j) & 1u) {
+          a.idx[(int64_t)r * a.k + ow] = wv[j];
+          if (LOOKUP && a.phys) a.phys[(int64_t)r * a.k + ow] = wp[j];
+          ++ow;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if ((eq >> j) & 1u) {
+          const int i = b + j * kRowThreads;
+          if (oe < (uint32_t)kRowCap) {
+            lkey[oe] = kr[bi][j] - kmin;
+            lslot[oe] = i;
+          }
+          if (oe < (uint32_t)a.max_len) list[oe] = i;
+          ++oe;
+        }
+      }
+      if (tid == 0) {
+        cnt[0] = base_w + (tot & 0xFFFFu);
+        cnt[1] = base_e + (tot >> 16);
+      }
+      wg_sync(true);
+    }
+  }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for_batches([&](int b, const uint32_t (&kk)[kBatch]) {
+  auto for_streamed = [&](auto&& f) {
+    for (int b = tid + NB * kStride; b < L; b += kStride) {
+      float x[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) x[j] = row[min(b + j * kRowThreads, L - 1)];
+      issue_fence();
+      uint32_t kk[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) kk[j] = float_key(x[j]);
+      f(b, kk, static_cast<const int*>(nullptr));
+    }
+  };
+  for_streamed([&](int b, const uint32_t (&kk)[kBatch], const int* pm) {
     uint32_t rel[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) rel[j] = kk[j] - kmin;
@@ -1068,7 +1145,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
       wo[j] = wb + (uint32_t)__popcll(bw[j] & below);
       wb += (uint32_t)__popcll(bw[j]);
       const int i = b + j * kRowThreads;
-      wv[j] = ((bw[j] >> lane) & 1ull) ? (LOOKUP ? out_value(a, r, i) : i) : -1;
+      wv[j] = ((bw[j] >> lane) & 1ull) ? (LOOKUP ? (pm ? pm[j] : out_value(a, r, i)) : i) : -1;
     }
     if constexpr (LOOKUP) {
 #pragma unroll
