@@ -175,6 +175,18 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
+  // The 16 heads' query rows go into qlds by DMA first (18 DMAs of 1 KB;
+  // wave w issues numbers w, w + 4, ...): they arrive with the row ids, and
+  // the waves read them into registers while the first block's rows are on
+  // their way, so that S reads only the rows from LDS.
+  const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
+                                                       ((int64_t)b * a.n_heads + hg * kMH) * kD);
+  for (int i = w; i < kMH * kD * 2 / 1024; i += 4) {
+    const int p = 64 * i + lane;                        // 16-byte position in qlds
+    const int hn = p / 72, jj = p - 72 * hn;
+    const int j = (jj & ~7) | ((jj ^ hn) & 7);          // global chunk stored there
+    dma_row16<0>(qlds + 1024 * i, qg + hn * (kD * 2) + 16 * j);
+  }
   const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int r0 = split * rows_per_split;
   const int r1 = min(r0 + rows_per_split, a.k);
@@ -244,14 +256,14 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
                                        }
                                      });
   }
+  // every wave's query DMAs have landed (vmcnt counts loads to LDS) before
+  // the barrier after which any wave reads qlds
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // query operand of S^T = K Q^T: lane (n, g) holds Q[head n][32t + 8g .. +7],
-  // read from qlds after the first block's wait (every wave needs all 16
-  // heads: one DMA of the group's rows per workgroup instead of a load per
-  // wave, which doubled the gather's L2 requests)
-  const uint8_t* qg = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(a.q) +
-                                                       ((int64_t)b * a.n_heads + hg * kMH) * kD);
+  // query operand of S^T = K Q^T: lane (n, g) holds Q[head n][32t + 8g .. +7]
+  // (one DMA of the group's rows per workgroup instead of a load per wave,
+  // which doubled the gather's L2 requests)
   bf16x8 qr[kD / 32];
 
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv);
@@ -284,22 +296,15 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
       }
     }
     if (base == 0) {
-      // 18 DMAs of 1 KB fill qlds; wave w issues numbers w, w + 4, ...
-      for (int i = w; i < kMH * kD * 2 / 1024; i += 4) {
-        const int p = 64 * i + lane;                        // 16-byte position in qlds
-        const int hn = p / 72, jj = p - 72 * hn;
-        const int j = (jj & ~7) | ((jj ^ hn) & 7);          // global chunk stored there
-        dma_row16<0>(qlds + 1024 * i, qg + hn * (kD * 2) + 16 * j);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (base == 0) {
+      // the query rows landed before the barrier above: read them while this
+      // block's rows are on their way
 #pragma unroll
       for (int t = 0; t < kD / 32; ++t) {
         const int j = 4 * t + g;
         qr[t] = *reinterpret_cast<const bf16x8*>(qlds + 16 * (72 * n + ((j & ~7) | ((j ^ n) & 7))));
       }
     }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- S^T for rows 16w + (0..15): A = K rows from LDS, B = Q^T.  Every
     // LDS read is issued before the first MFMA (an MFMA waiting on its own
