@@ -772,10 +772,11 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs a, int nsplit
 
 // Merge of the 16-head kernel's bf16 partials (dims in lane order: dim
 // 128w + 16t + n stored at 128w + 8n + t): out = sum_s 2^(lse_s - M) o_s /
-// sum_s 2^(lse_s - M).  One workgroup of two waves per (request, head), four
-// stored dims per thread; every wave works out the split weights itself and
-// broadcasts them from the lanes that hold them.
-__global__ __launch_bounds__(128) void mla_combine_bf16_kernel(AttnArgs a, int nsplit,
+// sum_s 2^(lse_s - M).  One workgroup of four waves per (request, head), two
+// stored dims per thread (more loads in flight than two waves with four
+// dims); every wave works out the split weights itself and broadcasts them
+// from the lanes that hold them.
+__global__ __launch_bounds__(256) void mla_combine_bf16_kernel(AttnArgs a, int nsplit,
                                                                 const __bf16* part_o,
                                                                 const float* part_lse) {
   constexpr int kBatch = 32;     // splits loaded before any is used
@@ -783,16 +784,16 @@ __global__ __launch_bounds__(128) void mla_combine_bf16_kernel(AttnArgs a, int n
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const float* pl = part_lse + bh * nsplit;
-  const __bf16* pb = part_o + bh * nsplit * kDV + 4 * tid;
+  const __bf16* pb = part_o + bh * nsplit * kDV + 2 * tid;
   // nsplit <= 64: lane s holds split s's log-sum-exp
   const float ls = lane < nsplit ? pl[lane] : -INFINITY;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[2] = {0.f, 0.f};
   float M = -INFINITY, wgt = 0.f, wsum = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
     const int nb = min(kBatch, nsplit - s0);
-    u32x2 v[kBatch];
+    uint32_t v[kBatch];
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s) v[s] = *reinterpret_cast<const u32x2*>(pb + (int64_t)(s0 + min(s, nb - 1)) * kDV);
+    for (int s = 0; s < kBatch; ++s) v[s] = *reinterpret_cast<const uint32_t*>(pb + (int64_t)(s0 + min(s, nb - 1)) * kDV);
     __builtin_amdgcn_sched_barrier(0);
     if (s0 == 0) {
       M = ls;
@@ -805,20 +806,17 @@ __global__ __launch_bounds__(128) void mla_combine_bf16_kernel(AttnArgs a, int n
     for (int s = 0; s < kBatch; ++s) {
       if (s < nb) {
         const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s0 + s));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[2 * j] += ws * __uint_as_float(v[s][j] << 16);
-          acc[2 * j + 1] += ws * __uint_as_float(v[s][j] & 0xFFFF0000u);
-        }
+        acc[0] += ws * __uint_as_float(v[s] << 16);
+        acc[1] += ws * __uint_as_float(v[s] & 0xFFFF0000u);
       }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  // stored dims 4 tid .. 4 tid + 3 = 128w + 8n + t0 + i hold dims 128w + 16 (t0 + i) + n
-  const int w = tid >> 5, n = (tid & 31) >> 1, t0 = 4 * (tid & 1);
+  // stored dims 2 tid, 2 tid + 1 = 128w + 8n + t0 + i hold dims 128w + 16 (t0 + i) + n
+  const int w = tid >> 6, n = (tid & 63) >> 2, t0 = 2 * (tid & 3);
   __bf16* ob = static_cast<__bf16*>(a.out) + bh * kDV + 128 * w + 16 * t0 + n;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ob[16 * i] = (__bf16)(acc[i] * inv);
+  for (int i = 0; i < 2; ++i) ob[16 * i] = (__bf16)(acc[i] * inv);
   if (tid == 0) a.lse[bh] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
@@ -957,7 +955,7 @@ hipError_t launch_mla_bf16(const AttnArgs& a, hipStream_t s) {
     launch(mla_bf16_kernel, dim3(grid), dim3(kMThreads), 0, s, "mla_bf16_kernel", a, rows_per_split, nsplit, units,
            part_b, part_lse);
     if (nsplit > 1)
-      launch(mla_combine_bf16_kernel, dim3((unsigned)(a.num_req * a.n_heads)), dim3(128), 0, s,
+      launch(mla_combine_bf16_kernel, dim3((unsigned)(a.num_req * a.n_heads)), dim3(256), 0, s,
              "mla_combine_bf16_kernel", a, nsplit, part_b, part_lse);
   }
   return hipGetLastError();
