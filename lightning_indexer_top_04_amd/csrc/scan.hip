@@ -923,22 +923,39 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     // spread over kHistReps copies, so that the few hot bins take a sixteenth
     // of the atomics each).  Every score of the wave is still in its staging
     // buffer: the host enables this for slices of at most 32 tiles per wave.
+    // Cleared with 16-byte stores; the lane whose LDS add finds a bin empty
+    // adds that bin's final count to the replica (one global add per
+    // non-empty bin, no pass over all 4160 bins).
     uint32_t* lh = reinterpret_cast<uint32_t*>(&ring[0][0]);
-    static_assert(sizeof(ring) >= kHistWords * 4, "the ring holds the histogram");
+    static_assert(sizeof(ring) >= kHistWords * 4 && kHistWords % 4 == 0, "the ring holds the histogram");
     __syncthreads();
-    for (int i = tid; i < kHistWords; i += kThreads) lh[i] = 0u;
+    for (int i = tid; i < kHistWords / 4; i += kThreads) reinterpret_cast<u32x4*>(lh)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     const int nsc = myn > 0 ? min(myn * kTile, (end - begin) - my0 * kTile) : 0;
-    for (int i = lane; i < nsc; i += 64) {
-      const uint32_t key = float_key(stage[i]);
-      atomicAdd(&lh[key >> 20], 1u);
-      atomicAdd(&lh[4096 + (key >> 26)], 1u);
+    uint32_t* gh = a.hist_rep + ((size_t)b * kHistReps + blockIdx.x % kHistReps) * kHistWords;
+    constexpr int kMaxPer = kFlushTiles * kTile / 64;   // scores per lane at most (the staging buffer)
+    uint32_t first = 0u;                                 // bit 2u: 12-bit bin new, 2u + 1: 6-bit bin new
+    uint32_t bins[kMaxPer][2];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int i = lane + 64 * u;
+      bins[u][0] = bins[u][1] = 0u;
+      if (i < nsc) {
+        const uint32_t key = float_key(stage[i]);
+        bins[u][0] = key >> 20;
+        bins[u][1] = 4096 + (key >> 26);
+        first |= (atomicAdd(&lh[bins[u][0]], 1u) == 0u ? 1u : 0u) << (2 * u);
+        first |= (atomicAdd(&lh[bins[u][1]], 1u) == 0u ? 1u : 0u) << (2 * u + 1);
+      }
+      if (64 * (u + 1) >= nsc) break;
     }
     __syncthreads();
-    uint32_t* gh = a.hist_rep + ((size_t)b * kHistReps + blockIdx.x % kHistReps) * kHistWords;
-    for (int i = tid; i < kHistWords; i += kThreads) {
-      const uint32_t v = lh[i];
-      if (v) atomicAdd(&gh[i], v);
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if ((first >> (2 * u + e)) & 1u) atomicAdd(&gh[bins[u][e]], lh[bins[u][e]]);
+      if (64 * (u + 1) >= nsc) break;
     }
   }
 }
