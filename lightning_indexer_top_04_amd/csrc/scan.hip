@@ -57,13 +57,20 @@ struct TileFetch {
 // weight absorbs 2^-E_j.  Pairs are extracted as dims (0,4),(1,5),(2,6),(3,7)
 // of each 8-dim group; the query uses the same order.
 // ---------------------------------------------------------------------------
+// The second nibble of each byte is taken in place: (x & 0x00F000F0) |
+// 0x64006400 is the fp16 number 1024 + 16 n' (exact), and one packed fma
+// with 1/16 and -72 leaves n' - 8 = n exactly; the upper byte's nibbles
+// after one shift by 8.  Ten instructions per eight values instead of twelve.
 __device__ __forceinline__ f16x8 int4x8_to_f16x8(uint32_t d) {
   const uint32_t x = d ^ 0x88888888u;
+  const uint32_t y = x >> 8;
   const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
   f16x2 p0 = __builtin_bit_cast(f16x2, (x & 0x000F000Fu) | 0x64006400u) + bias;
-  f16x2 p1 = __builtin_bit_cast(f16x2, ((x >> 4) & 0x000F000Fu) | 0x64006400u) + bias;
-  f16x2 p2 = __builtin_bit_cast(f16x2, ((x >> 8) & 0x000F000Fu) | 0x64006400u) + bias;
-  f16x2 p3 = __builtin_bit_cast(f16x2, ((x >> 12) & 0x000F000Fu) | 0x64006400u) + bias;
+  f16x2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (x & 0x00F000F0u) | 0x64006400u), sixteenth, bias_hi);
+  f16x2 p2 = __builtin_bit_cast(f16x2, (y & 0x000F000Fu) | 0x64006400u) + bias;
+  f16x2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (y & 0x00F000F0u) | 0x64006400u), sixteenth, bias_hi);
   f16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   return r;
 }
