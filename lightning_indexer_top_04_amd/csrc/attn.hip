@@ -496,20 +496,35 @@ __global__ __launch_bounds__(kWThreads, 1) void mla_bf16_wide_kernel(AttnArgs a,
   bf16x8 qr[kD / 32];
 #pragma unroll
   for (int t = 0; t < kD / 32; ++t) qr[t] = *reinterpret_cast<const bf16x8*>(qh + 32 * t + 8 * g);
-  // physical rows of the slice (-1 = skip)
+  // physical rows of the slice (-1 = skip): every id load of the thread is
+  // issued before the first is used (then the page-table loads), so the
+  // slice costs one or two round trips, not one per 512 rows
   const int n_rows_pool = a.num_pages * a.page_size;
-  for (int e = tid; e < nr; e += kWThreads) {
-    int row = -1;
-    if (a.phys) {
-      row = a.phys[(int64_t)b * a.k + r0 + e];
-    } else {
-      const int pos = a.idx[(int64_t)b * a.k + r0 + e];
-      if (pos >= 0 && pos < L) {
-        const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-        if ((unsigned)page < (unsigned)a.num_pages) row = page * a.page_size + pos % a.page_size;
-      }
+  {
+    constexpr int kPer = kWMaxRows / kWThreads;
+    int v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * kWThreads;
+      v[i] = e < nr ? (a.phys ? a.phys[(int64_t)b * a.k + r0 + e] : a.idx[(int64_t)b * a.k + r0 + e]) : -1;
     }
-    rows_all[e] = (row < 0 || row >= n_rows_pool) ? -1 : row;
+    if (!a.phys) {
+      int pg[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const bool in = v[i] >= 0 && v[i] < L;
+        pg[i] = a.page_table[(int64_t)b * a.max_pages + (in ? v[i] / a.page_size : 0)];
+        pg[i] = in ? pg[i] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        v[i] = (unsigned)pg[i] < (unsigned)a.num_pages ? pg[i] * a.page_size + v[i] % a.page_size : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + i * kWThreads;
+      if (e < nr) rows_all[e] = (v[i] < 0 || v[i] >= n_rows_pool) ? -1 : v[i];
+    }
   }
   // the query and row loads are complete here (ordinary loads are not left
   // in flight under the block DMAs, whose waits are counted by hand below)
