@@ -872,7 +872,11 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     __builtin_amdgcn_wave_barrier();
     for (int i = 4 * lane; i < n; i += 4 * 64) {
       if (i + 4 <= n) {
-        *reinterpret_cast<f32x4*>(out + pos0 + i) = *reinterpret_cast<const f32x4*>(stage + i);
+        // written through to memory (sc1): the top-k that follows reads the
+        // scores from other XCDs, and lines left dirty in L2 would be
+        // written back at the end of the launch, after the last workgroup
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stage + i);
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(out + pos0 + i), "v"(v) : "memory");
       } else {
         for (int k = i; k < n; ++k) out[pos0 + k] = stage[k];
       }
