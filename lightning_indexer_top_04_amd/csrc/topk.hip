@@ -513,7 +513,7 @@ __device__ __forceinline__ int wave_threshold64(uint32_t cnt, uint32_t need, uin
 template <int PER, bool MAPPED, int VW>
 __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   constexpr int kChunk = PER * kBlock;
-  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t tmp[32];
   __shared__ uint32_t before[2];
   __shared__ uint32_t thr[4];
@@ -730,18 +730,23 @@ __global__ __launch_bounds__(kBlock, 8) void topk_select_kernel(TopkArgs a) {
   // refinement starts from it: counted in LDS first (the level-1 histogram
   // there is no longer read), then one global add per non-empty bin
   // (not needed when every member is kept)
+  // (the member whose LDS add opens a bin adds that bin's final count: no
+  // pass over the 4096 bins)
   if ((tot >> 16) != 0u && members > (uint32_t)a.k - better) {   // uniform
-    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
+    for (int i = threadIdx.x; i < kBins / 4; i += kBlock) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
+    uint32_t opened = 0u;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if ((eq >> j) & 1u) atomicAdd(&hist[dg.d2(key[j])], 1u);
+      if ((eq >> j) & 1u) opened |= (atomicAdd(&hist[dg.d2(key[j])], 1u) == 0u ? 1u : 0u) << j;
     __syncthreads();
     uint32_t* g2 = ws.h2 + (size_t)r * kBins;
-    for (int i = threadIdx.x; i < kBins; i += kBlock) {
-      const uint32_t n = hist[i];
-      if (n) atomicAdd(&g2[i], n);
-    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((opened >> j) & 1u) {
+        const uint32_t d2 = dg.d2(key[j]);
+        atomicAdd(&g2[d2], hist[d2]);
+      }
   }
   // with members_out the members are emitted like winners, at slots after
   // every winner of the row
