@@ -285,7 +285,13 @@ int32_t lsi_multilayer_decode(int32_t n_layers, int32_t retention,
  * of device memory (LeanSparse: only the compact keys need to stay in GPU
  * memory, the short list of originals is fetched from the host): stage 2
  * then reads the candidates' rows across the host bus.  Pageable host
- * memory returns LSI_ERR_INVALID_ARG. */
+ * memory returns LSI_ERR_INVALID_ARG.
+ * Workspace state (num_req == 1 only): the first
+ * lsi_decode_step_state_bytes(1) bytes carry state from one call to the
+ * next, with the rules of lsi_decode_step's: zero when a workspace is first
+ * used, left zero by every call that returns LSI_OK.  (The compact scan
+ * builds the first top-k's histograms there; the exact scan clears them.)
+ * With num_req > 1 the workspace holds no state. */
 size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len,
                                      int32_t n_cand, int32_t k);
 int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4,

@@ -760,6 +760,8 @@ size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32
                                      int32_t k) {
   if (num_req < 1 || max_seq_len < 0 || n_cand < 1 || k < 1) return 0;
   (void)k;
+  // one request: the state words of the compact scan's histograms first
+  const size_t st = num_req == 1 ? lsi_decode_step_state_bytes(1) : 0;
   const size_t s4 = align_up((size_t)num_req * scores_ld(max_seq_len) * 4, kWsAlign);
   const size_t rg = align_up((size_t)kMaxRangeSlots * 16, kWsAlign);
   const size_t t1 = topk_ws_bytes(num_req, max_seq_len);
@@ -767,7 +769,7 @@ size_t lsi_two_stage_workspace_bytes(int32_t num_req, int32_t max_seq_len, int32
   const size_t ccount = align_up((size_t)num_req * 4, kWsAlign);
   const size_t s8 = align_up((size_t)num_req * n_cand * 4, kWsAlign);
   const size_t t2 = topk_ws_bytes(num_req, n_cand);
-  return s4 + rg + t1 + cand + ccount + s8 + t2;
+  return st + s4 + rg + t1 + cand + ccount + s8 + t2;
 }
 
 int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache* ikeys8,
@@ -796,6 +798,14 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   k8.scale = static_cast<const float*>(sc8);
   const int B = batch->num_req;
   char* ws = static_cast<char*>(workspace);
+  // One request: the compact scan also builds the first top-k's histograms
+  // (fixed 12- and 6-bit key digits, no histogram launch) in the state words
+  // at the start of the workspace, which the exact scan clears again.
+  uint32_t* hist_rep = reinterpret_cast<uint32_t*>(ws);
+  const bool scan_hist = B == 1 && scan_builds_hist(1, batch->max_seq_len, ikeys4->page_size);
+  if (B == 1) ws += lsi_decode_step_state_bytes(1);
+  void* t2 = ws;               // the second top-k's workspace (counters first)
+  ws += topk_ws_bytes(B, n_cand);
   float* s4 = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * ld * 4, kWsAlign);
   uint4* rslots = reinterpret_cast<uint4*>(ws);   // the int4 scan's per-workgroup key ranges
@@ -807,23 +817,25 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   int32_t* cc = reinterpret_cast<int32_t*>(ws);
   ws += align_up((size_t)B * 4, kWsAlign);
   float* s8 = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)B * n_cand * 4, kWsAlign);
-  void* t2 = ws;
 
-  // stage 1: compact keys over every token, keep n_cand.  The scan records
-  // each workgroup's key range, so that the top-k's first digit spans the
-  // row's range (the compact scores crowd into a few binades), and clears
-  // the top-k's counters.
+  // stage 1: compact keys over every token, keep n_cand.  The scan clears
+  // the top-k's counters and either builds its histograms (one request) or
+  // records each workgroup's key range, so that the histogram launch's first
+  // digit spans the row's range (the compact scores crowd into a few
+  // binades: with the fixed digit the threshold bin holds ~2% of a row,
+  // which the refinement's second digit splits).
   ScanArgs a4 = scan_args(ikeys4, batch, q, n_heads, dim, w, s4, ld);
   a4.zero_ptr = static_cast<uint32_t*>(t1);
   a4.zero_words = topk_zero_words(B);
-  a4.range_slots = rslots;
+  a4.range_slots = scan_hist ? nullptr : rslots;
+  a4.hist_rep = scan_hist ? hist_rep : nullptr;
   int nslots = 0;
   LSI_LAUNCH(launch_scan_int4(a4, stream, &nslots), "lsi_two_stage_topk (compact scan)");
   TopkArgs ta;
   ta.scores = s4;
   ta.range_slots = nslots > 0 ? rslots : nullptr;
   ta.range_nslots = nslots;
+  ta.hist_rep = a4.hist_rep;
   ta.ld = ld;
   ta.seq_lens = batch->seq_lens;
   ta.num_req = B;
@@ -838,8 +850,10 @@ int32_t lsi_two_stage_topk(const lsi_paged_cache* ikeys4, const lsi_paged_cache*
   ScanArgs a8 = scan_args(&k8, batch, q, n_heads, dim, w, s8, n_cand);
   a8.positions = cl;
   a8.n_pos = n_cand;
-  a8.zero_ptr = static_cast<uint32_t*>(t2);
-  a8.zero_words = topk_zero_words(B);
+  // (it clears the second top-k's counters and, after the first top-k has
+  // read them, the histogram state words just before them)
+  a8.zero_ptr = scan_hist ? hist_rep : static_cast<uint32_t*>(t2);
+  a8.zero_words = topk_zero_words(B) + (scan_hist ? (int64_t)(static_cast<char*>(t2) - reinterpret_cast<char*>(hist_rep)) / 4 : 0);
   LSI_LAUNCH(launch_scan_fp8(a8, stream), "lsi_two_stage_topk (exact scan)");
   TopkArgs tb;
   tb.scores = s8;

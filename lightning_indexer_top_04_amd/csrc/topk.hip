@@ -1218,10 +1218,13 @@ hipError_t launch_topk(const TopkArgs& a, int ws_state, hipStream_t s) {
   // in the histogram launch, 4 us less in 128).  With scan-built histograms
   // every chunk places its output with one returning atomic on the row's
   // counter pair, and those serialise too (~12 ns each: 128 chunks of a
-  // 131072-score row spread their placements over 1.5 us): about one chunk
-  // per four compute units (64 chunks: 0.2 us faster; 32: 0.4 us slower).
-  const int64_t per_cu = a.hist_rep != nullptr ? std::max<int64_t>(num_cus() / 4, 1) : 2 * (int64_t)num_cus();
-  const int64_t want = ceil_div((int64_t)a.num_req * a.max_len, per_cu);
+  // 131072-score row spread their placements over 1.5 us): chunks of 2048
+  // scores (64 chunks of a 131072-score row: 0.2 us faster than 128; 32:
+  // 0.4 us slower), and for
+  // longer rows 128 chunks (a 524288-score row whose threshold bin holds
+  // ~10,000 members: 7.8 us in 128 chunks, 10.1 in 64).
+  const int64_t want = a.hist_rep != nullptr ? std::max<int64_t>(2048, ceil_div(a.max_len, 128))
+                                             : ceil_div((int64_t)a.num_req * a.max_len, 2 * (int64_t)num_cus());
   int per = kMinChunk / kBlock;
   while (per * kBlock < kMaxChunk && (per * kBlock < want || ceil_div(a.max_len, per * kBlock) > 256)) per *= 2;
   dim3 grid((unsigned)a.num_req, (unsigned)std::max<int64_t>(1, ceil_div(a.max_len, per * kBlock)));

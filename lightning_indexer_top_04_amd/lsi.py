@@ -370,19 +370,28 @@ def multilayer_decode(layers: Layers, sm_scale: float, schedule: str = "mli", st
     return L.idx, L.count, L.out, L.lse
 
 
+def two_stage_workspace(B, max_seq_len, n_cand, k, device) -> torch.Tensor:
+    """A workspace for lsi_two_stage_topk: zero-filled, as its leading state
+    words (one request) must be on first use (each successful call leaves
+    them zero)."""
+    nb = int(lib().lsi_two_stage_workspace_bytes(B, max_seq_len, n_cand, k))
+    return torch.zeros(max(nb, 1), dtype=torch.uint8, device=device)
+
+
 def two_stage_topk(ikeys4: Cache, ikeys8: Cache, req: Requests, q: torch.Tensor,
-                   w: torch.Tensor, n_cand: int, k: int, want_cand: bool = False, stream=None):
+                   w: torch.Tensor, n_cand: int, k: int, want_cand: bool = False, stream=None,
+                   ws=None):
     B, H, d = q.shape
     dev = q.device
-    nb = lib().lsi_two_stage_workspace_bytes(B, req.max_seq_len, n_cand, k)
     with _on(stream):
         idx = torch.empty(B, k, dtype=torch.int32, device=dev)
         cnt = torch.empty(B, dtype=torch.int32, device=dev)
         cand = torch.empty(B, n_cand, dtype=torch.int32, device=dev) if want_cand else None
-        ws = _ws(nb, dev)
+        if ws is None:
+            ws = two_stage_workspace(B, req.max_seq_len, n_cand, k, dev)
     _check(lib().lsi_two_stage_topk(ikeys4.ref, ikeys8.ref, req.ref, _ptr(q), H, d, _ptr(w),
-                                    n_cand, k, _ptr(idx), _ptr(cnt), _ptr(cand), _ptr(ws), nb,
-                                    _stream(stream)), "lsi_two_stage_topk")
+                                    n_cand, k, _ptr(idx), _ptr(cnt), _ptr(cand), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "lsi_two_stage_topk")
     return (idx, cnt, cand) if want_cand else (idx, cnt)
 
 

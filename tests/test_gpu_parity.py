@@ -380,6 +380,46 @@ def test_two_stage_key_range_digits_with_a_tie_across_the_threshold():
     assert 0 < tied.sum() < 20000   # the threshold lies inside the tie
 
 
+@pytest.mark.parametrize("planted", [True, False])
+def test_two_stage_one_request_reuses_its_workspace(planted):
+    """One long request: the compact scan builds the first top-k's histograms
+    in the workspace's state words (fixed key digits, the threshold bin then
+    holds a few percent of the row) and the exact scan clears them again.
+    Three calls on one workspace, the second over a shorter row: each stage
+    against the oracle, the state words zero after every call, and the
+    repeated call equal to the first."""
+    state = int(lsi.lib().lsi_decode_step_state_bytes(1))
+    wl = synth.scaled(synth.TWO_STAGE_512K, seq_lens=(100000,), n_planted=256, seed=23)
+    di = synth.make_decode_inputs(wl, device=DEV, with_int4=True, with_attn=False, planted=planted)
+    ov = OracleView(di)
+    ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
+    ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
+    n_cand, k = 4096, 1024
+    ws = lsi.two_stage_workspace(1, 100000, n_cand, k, DEV)
+    K4, s4 = ov.keys4(0)
+    I4 = O.index_scores(ov.q_idx[0], ov.w[0], K4, s4)
+    K8, s8 = ov.keys(0)
+    I8 = O.index_scores(ov.q_idx[0], ov.w[0], K8, s8)
+    first = None
+    for L in (100000, 60000, 100000):
+        req = lsi.Requests(di.seq_lens.clamp(max=L), di.page_table, 100000)
+        idx, cnt, cand = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, n_cand, k,
+                                            want_cand=True, ws=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:state])) == 0, "state words left non-zero"
+        cand_h = cand[0].cpu().numpy()
+        check_topk(cand_h, n_cand, I4[:L], n_cand, f"stage 1 L={L}")
+        c_sorted = np.sort(cand_h)
+        fin = idx[0, :cnt[0]].cpu().numpy()
+        assert cnt[0].item() == k and set(fin.tolist()) <= set(c_sorted.tolist())
+        pos = np.searchsorted(c_sorted, fin)
+        check_topk(pos, k, I8[c_sorted], k, f"stage 2 L={L}")
+        if first is None:
+            first = (np.sort(cand_h), np.sort(fin))
+        elif L == 100000:
+            assert np.array_equal(first[0], np.sort(cand_h)) and np.array_equal(first[1], np.sort(fin))
+
+
 def test_two_stage_host_originals_equal_device_and_pageable_is_rejected():
     lens = [70000, 20000]
     _, i_d, c_d, cd_d = _two_stage_case(False, lens, 8192, 2048, 19)
