@@ -861,51 +861,97 @@ __global__ __launch_bounds__(kRefThreads) void topk_refine_kernel(TopkArgs a) {
   const bool in_lds = n2 <= (uint32_t)kLdsCand;
   int32_t* list = ws.list + (size_t)r * a.max_len;
   uint32_t ow = better, oe = 0;
-  for (uint32_t base = 0; base < n; base += kRefBatch) {
-    if (base > 0) {
+  // The first batch (loaded with the histogram) is waited for here, by a
+  // wait the compiler can see: otherwise it counts those loads as pending
+  // inside the loop and waits for every store of the previous batch before
+  // reusing their registers.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  // Two copies of the pass: positions leaving as they are (no slot map, no
+  // physical rows), and with their lookups.  A lookup load that is issued
+  // and used only under a condition still counts as pending where the loop
+  // starts again, and the compiler then waits for every outstanding store
+  // before reusing its register: one loop with both cases ran its stores
+  // one round trip at a time.
+  auto pass = [&](auto plain_tag) {
+    constexpr bool kPlain = decltype(plain_tag)::value;
+    for (uint32_t base = 0; base < n; base += kRefBatch) {
+      if (base > 0) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) e[u] = cand[min(base + tid + u * kRefThreads, n - 1)];
-    }
-    uint32_t win = 0, eq = 0;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (base + tid + u * kRefThreads < n) {
-        const uint32_t d = dg.d2((uint32_t)e[u].y);
-        win |= (uint32_t)(d > bin2 || (take_eq && d == bin2)) << u;
-        eq |= (uint32_t)(!take_eq && d == bin2) << u;
+        for (int u = 0; u < kU; ++u) e[u] = cand[min(base + tid + u * kRefThreads, n - 1)];
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the batch, before any branch uses it
       }
-    }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan<kRefThreads>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot, true);
-    uint32_t o = ow + (pre & 0xFFFF);
-    uint32_t q = oe + (pre >> 16);
-    // winners: every output row (and its page) is looked up before any store
-    int wv[kU], wp[kU];
+      uint32_t win = 0, eq = 0;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) wv[u] = ((win >> u) & 1u) ? out_value(a, r, e[u].x) : -1;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) wp[u] = a.phys ? phys_of(a, r, wv[u]) : -1;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if ((win >> u) & 1u) {
-        if (o < (uint32_t)a.k) {
-          a.idx[(int64_t)r * a.k + o] = wv[u];
-          if (a.phys) a.phys[(int64_t)r * a.k + o] = wp[u];
+      for (int u = 0; u < kU; ++u) {
+        if (base + tid + u * kRefThreads < n) {
+          const uint32_t d = dg.d2((uint32_t)e[u].y);
+          win |= (uint32_t)(d > bin2 || (take_eq && d == bin2)) << u;
+          eq |= (uint32_t)(!take_eq && d == bin2) << u;
         }
-        ++o;
       }
-      if ((eq >> u) & 1u) {
-        if (in_lds) {
-          lslot[q] = e[u].x;
-          lkey[q] = (uint32_t)e[u].y - dg.base;
-        } else {
-          list[q] = e[u].x;
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan<kRefThreads>((uint32_t)(__popc(win) | (__popc(eq) << 16)), tmp, &tot, true);
+      uint32_t o = ow + (pre & 0xFFFF);
+      uint32_t q = oe + (pre >> 16);
+      // winners: every output row (and its page) is looked up before any store
+      // (the lookups load for every element, at clamped indexes, and are
+      // masked afterwards: loads under a per-element condition were each
+      // waited for on their own)
+      int wv[kU], wp[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        wv[u] = e[u].x;
+        wp[u] = -1;
+      }
+      if constexpr (!kPlain) {
+        if (a.map) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            wv[u] = a.map[(int64_t)r * a.map_ld + (((win >> u) & 1u) ? e[u].x : 0)];
         }
-        ++q;
+        // non-winners (possibly unwritten words past the row's members) look
+        // up position 0
+#pragma unroll
+        for (int u = 0; u < kU; ++u) wv[u] = ((win >> u) & 1u) ? wv[u] : -1;
+        if (a.phys) {
+          int pg[kU], off[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            split_pos(max(wv[u], 0), a.page_size, pg[u], off[u]);
+            wp[u] = a.page_table[(int64_t)r * a.max_pages + pg[u]];
+          }
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            wp[u] = wv[u] >= 0 && (unsigned)wp[u] < (unsigned)a.num_pages ? wp[u] * a.page_size + off[u] : -1;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if ((win >> u) & 1u) {
+          if (o < (uint32_t)a.k) {
+            a.idx[(int64_t)r * a.k + o] = wv[u];
+            if (!kPlain && a.phys) a.phys[(int64_t)r * a.k + o] = wp[u];
+          }
+          ++o;
+        }
+        if ((eq >> u) & 1u) {
+          if (in_lds) {
+            lslot[q] = e[u].x;
+            lkey[q] = (uint32_t)e[u].y - dg.base;
+          } else {
+            list[q] = e[u].x;
+          }
+          ++q;
+        }
+      }
+      ow += tot & 0xFFFF;
+      oe += tot >> 16;
     }
-    ow += tot & 0xFFFF;
-    oe += tot >> 16;
+  };
+  if (a.map == nullptr && a.phys == nullptr) {
+    pass(std::true_type{});
+  } else {
+    pass(std::false_type{});
   }
   if (take_eq) {
     if (tid == 0) a.count[r] = (int32_t)min(better + better2 + n2, (uint32_t)a.k);
