@@ -26,14 +26,16 @@
  *     every buffer; the library never allocates device memory.  Scratch comes
  *     in as `workspace` (256-byte aligned) of at least the size the matching
  *     *_workspace_bytes() function returns; its contents on entry do not
- *     matter and on return are unspecified.
+ *     matter and on return are unspecified, except for the leading state
+ *     words of lsi_decode_step, lsi_multilayer_decode and (one request)
+ *     lsi_two_stage_topk, whose rules are given with those calls.
  *   - Work is enqueued on the caller's stream; no call synchronises the host.
  *     Arguments are validated on the host BEFORE anything is enqueued:
  *     LSI_ERR_INVALID_ARG, LSI_ERR_UNSUPPORTED and LSI_ERR_WORKSPACE mean
  *     nothing was enqueued.  LSI_ERR_HIP (a launch or runtime call failed)
  *     can come after some of a call's kernels or copies were already
- *     enqueued: the call's outputs (and, for lsi_decode_step, its workspace
- *     state words) are then undefined.  lsi_last_error_detail() gives a
+ *     enqueued: the call's outputs (and the workspace state words of the
+ *     calls that keep them) are then undefined.  lsi_last_error_detail() gives a
  *     per-thread message.
  *   - Paged caches: token s of request b lives in physical page
  *     page_table[b][s / page_size], slot s % page_size.  Indexer keys and
