@@ -380,8 +380,8 @@ def test_two_stage_key_range_digits_with_a_tie_across_the_threshold():
     assert 0 < tied.sum() < 20000   # the threshold lies inside the tie
 
 
-@pytest.mark.parametrize("planted", [True, False])
-def test_two_stage_one_request_reuses_its_workspace(planted):
+@pytest.mark.parametrize("planted,L_max", [(True, 100000), (False, 100000), (False, 20000)])
+def test_two_stage_one_request_reuses_its_workspace(planted, L_max):
     """One long request: the compact scan builds the first top-k's histograms
     in the workspace's state words (fixed key digits, the threshold bin then
     holds a few percent of the row) and the exact scan clears them again.
@@ -389,20 +389,20 @@ def test_two_stage_one_request_reuses_its_workspace(planted):
     against the oracle, the state words zero after every call, and the
     repeated call equal to the first."""
     state = int(lsi.lib().lsi_decode_step_state_bytes(1))
-    wl = synth.scaled(synth.TWO_STAGE_512K, seq_lens=(100000,), n_planted=256, seed=23)
+    wl = synth.scaled(synth.TWO_STAGE_512K, seq_lens=(L_max,), n_planted=256, seed=23)
     di = synth.make_decode_inputs(wl, device=DEV, with_int4=True, with_attn=False, planted=planted)
     ov = OracleView(di)
     ik4 = lsi.Cache(di.ikeys4, di.iscale4, "int4", 128)
     ik8 = lsi.Cache(di.ikeys, di.iscale, "fp8", 128)
     n_cand, k = 4096, 1024
-    ws = lsi.two_stage_workspace(1, 100000, n_cand, k, DEV)
+    ws = lsi.two_stage_workspace(1, L_max, n_cand, k, DEV)
     K4, s4 = ov.keys4(0)
     I4 = O.index_scores(ov.q_idx[0], ov.w[0], K4, s4)
     K8, s8 = ov.keys(0)
     I8 = O.index_scores(ov.q_idx[0], ov.w[0], K8, s8)
     first = None
-    for L in (100000, 60000, 100000):
-        req = lsi.Requests(di.seq_lens.clamp(max=L), di.page_table, 100000)
+    for L in (L_max, (L_max * 3) // 5, L_max):
+        req = lsi.Requests(di.seq_lens.clamp(max=L), di.page_table, L_max)
         idx, cnt, cand = lsi.two_stage_topk(ik4, ik8, req, di.q_idx, di.w, n_cand, k,
                                             want_cand=True, ws=ws)
         torch.cuda.synchronize()
@@ -416,8 +416,26 @@ def test_two_stage_one_request_reuses_its_workspace(planted):
         check_topk(pos, k, I8[c_sorted], k, f"stage 2 L={L}")
         if first is None:
             first = (np.sort(cand_h), np.sort(fin))
-        elif L == 100000:
+        elif L == L_max:
             assert np.array_equal(first[0], np.sort(cand_h)) and np.array_equal(first[1], np.sort(fin))
+
+
+def test_two_stage_long_candidate_list_against_oracle():
+    """More than 32768 candidates: the second top-k takes the multi-workgroup
+    path with the slot map (candidate -> position), including the
+    refinement's lookups; both stages against the oracle."""
+    lens, n_cand, k = [200000], 40000, 2048
+    di, idx, cnt, cand = _two_stage_case(False, lens, n_cand, k, 29)
+    ov = OracleView(di)
+    K4, s4 = ov.keys4(0)
+    I4 = O.index_scores(ov.q_idx[0], ov.w[0], K4, s4)
+    check_topk(cand[0], n_cand, I4, n_cand, "stage 1")
+    c_sorted = np.sort(cand[0, :n_cand])
+    K8, s8 = ov.keys(0)
+    I8 = O.index_scores(ov.q_idx[0], ov.w[0], K8[c_sorted], s8[c_sorted])
+    fin = idx[0, :cnt[0]]
+    assert cnt[0] == k and set(fin.tolist()) <= set(c_sorted.tolist())
+    check_topk(np.searchsorted(c_sorted, fin), k, I8, k, "stage 2")
 
 
 def test_two_stage_host_originals_equal_device_and_pageable_is_rejected():
