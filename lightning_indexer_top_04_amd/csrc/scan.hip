@@ -1046,7 +1046,10 @@ hipError_t launch_mfma_scan(const ScanArgs& a_in, hipStream_t s, int* nslots) {
     // Batches: one wave of resident workgroups over balanced slices, sized
     // on the device from the request lengths (a grid of one row per request
     // would leave the slices of ragged requests to a partial second wave).
-    const int64_t G = (int64_t)num_cus() * 3;
+    // Two per CU, although three fit: with three, the 32 x 131072-token
+    // scan took 113-114 us on some devices against 95 on others; with two it
+    // takes 93-95 us on both, and the 64-request ragged scan is faster too.
+    const int64_t G = (int64_t)num_cus() * 2;
     const int64_t unit = std::max<int64_t>(kTile * kWaves, a.page_size);
     const int64_t work = (int64_t)a.num_req * a.max_seq_len;
     if (a.num_req >= 2 && a.num_req <= kThreads && 4 * (int64_t)a.num_req <= G &&
