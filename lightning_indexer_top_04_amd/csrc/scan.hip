@@ -390,6 +390,33 @@ __device__ __forceinline__ void lds_dma4(uint8_t* lds, const float* g) {
                                    (__attribute__((address_space(3))) void*)lds, 4, 0, kNonTemporal);
 }
 
+// LDS accesses to the ring's memory once no DMA is in flight (the
+// histogram), written out for the same reason as the tile reads: the
+// compiler would wait for every vector-memory operation first, the score
+// stores included.  Each statement completes its own accesses.
+__device__ __forceinline__ uint32_t lds_u32_addr(const uint32_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t*)p;
+}
+__device__ __forceinline__ void lds_zero16(uint32_t* p) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  asm volatile("ds_write_b128 %0, %1" : : "v"(lds_u32_addr(p)), "v"(z) : "memory");
+}
+// two LDS increments; returns the counts they found
+__device__ __forceinline__ void lds_inc2_rtn(uint32_t* p0, uint32_t* p1, uint32_t& r0, uint32_t& r1) {
+  asm volatile(
+      "ds_add_rtn_u32 %0, %2, %4\n\t"
+      "ds_add_rtn_u32 %1, %3, %4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(lds_u32_addr(p0)), "v"(lds_u32_addr(p1)), "v"(1u)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_read_u32(const uint32_t* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_u32_addr(p)) : "memory");
+  return v;
+}
+
 // The lane's 32 bytes of an int4 key row (two 16-byte reads) and the tile's
 // scale word, complete when the statement ends.
 __device__ __forceinline__ void lds_read_tile2_scale(u32x4 (&kr)[2], float& sc, const uint8_t* slot,
@@ -629,7 +656,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   }
   if (tid < npg_max) pages[tid] = page_in0;
   if (tid + kThreads < npg_max) pages[tid + kThreads] = page_in1;
-  __syncthreads();
+  lds_barrier();   // the page ids only: the query DMAs are waited for below
   const int end = min(begin + span, L);
   const int ntile = max(0, (end - begin + kTile - 1) / kTile);
 
@@ -657,15 +684,20 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   }
   const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
 
-  // Every refill is issued, so the count of vector-memory operations between
-  // a tile's DMA and its use is the same at every step: RING - 1 later tiles
-  // of TL::kOps DMAs each (four (fp8) or two (int4) 1 KB key moves and one
-  // for the 32 scales, which lanes 32..63 copy a second time).  vmcnt counts loads in issue order, so
-  // waiting until at most that many are outstanding means the tile has landed
-  // in LDS.  Refills past the wave's last tile (and every fill of a wave
-  // without tiles) read pool row 0, which all of them share in L2, into a
-  // slot that is never consumed.  A slot is refilled only after every read of
-  // it has completed (its reads end with their own wait).
+  // Tiles 0 .. RING - 1 are always issued (the query split's wait counts
+  // on them); a refill j + RING only when that tile exists.  So while a
+  // later tile has been issued, RING - 1 later tiles of TL::kOps DMAs each
+  // (four (fp8) or two (int4) 1 KB key moves and one for the 32 scales,
+  // which lanes 32..63 copy a second time) follow a tile's DMAs, and
+  // waiting until at most that many vector-memory operations are
+  // outstanding means the tile has landed in LDS (loads complete in issue
+  // order); the wave's last tile, with nothing issued after it, waits for
+  // all of them.  The initial fills past a short run (and every fill of a
+  // wave without tiles) read pool row 0, which all of them share in L2, into
+  // a slot that is never consumed; they are the only DMAs that can still be
+  // in flight once the run is done (when it has fewer than RING tiles).  A
+  // slot is refilled only after every read of it has completed (its reads
+  // end with their own wait).
   auto issue = [&](int j, uint8_t* slot) {
     int64_t row0 = 0;
     if (j < myn) {
@@ -796,8 +828,10 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   issue(RING - 1, slot[RING - 1]);    // the query rows are no longer needed
 
   // Score of token m of the wave's j-th tile (the same in lanes m and m + 32).
+  const int nissued = max(myn, RING);   // tiles whose DMAs are issued
   auto consume = [&](int j, uint8_t* slot) -> float {
-    wait_ring_tile<RING, TL::kOps>();
+    if (j + 1 < nissued) wait_ring_tile<RING, TL::kOps>();
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     float scale;
     f32x16 acc0 = {};
     f32x16 acc1 = {};
@@ -833,7 +867,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     const int page = pages[((my0 + j) * kTile) >> page_shift];
     const bool ok = page >= 0 && page < a.num_pages;
     // the slot's reads are complete (the MFMAs consumed them): refill it
-    issue(j + RING, slot);
+    if (j + RING < myn) issue(j + RING, slot);
     float part = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -904,8 +938,11 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
       if (jr + 1 == myn || (jr + 1) % kFlushTiles == 0) flush(jr);
     }
   }
-  // no DMA may still be writing this workgroup's LDS when it retires
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // No DMA may still be writing this workgroup's LDS when it retires or
+  // when the ring holds the histogram below.  A run of RING or more tiles
+  // has none left (its last tile waited for all); the score stores are not
+  // waited for (the barriers below are LDS-only).
+  if (myn < RING) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (a.range_slots != nullptr) {
     // the workgroup's key range (waves combined in LDS) into its slot: plain
     // stores (atomics from every workgroup on one row's pair of words
@@ -930,7 +967,8 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
   if (a.hist_rep != nullptr) {
     // The histogram of this workgroup's scores for the top-k that follows:
     // 12-bit and 6-bit top key digits, counted in the ring's LDS (no DMA is
-    // in flight any more) and added to one of the row's replicas (workgroups
+    // in flight any more; the barriers wait for LDS operations only, so the
+    // score stores stay in flight) and added to one of the row's replicas (workgroups
     // spread over kHistReps copies, so that the few hot bins take a sixteenth
     // of the atomics each).  Every score of the wave is still in its staging
     // buffer: the host enables this for slices of at most 32 tiles per wave.
@@ -939,9 +977,9 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
     // non-empty bin, no pass over all 4160 bins).
     uint32_t* lh = reinterpret_cast<uint32_t*>(&ring[0][0]);
     static_assert(sizeof(ring) >= kHistWords * 4 && kHistWords % 4 == 0, "the ring holds the histogram");
-    __syncthreads();
-    for (int i = tid; i < kHistWords / 4; i += kThreads) reinterpret_cast<u32x4*>(lh)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    lds_barrier();   // every wave is done with the ring
+    for (int i = tid; i < kHistWords / 4; i += kThreads) lds_zero16(lh + 4 * i);
+    lds_barrier();
     const int nsc = myn > 0 ? min(myn * kTile, (end - begin) - my0 * kTile) : 0;
     uint32_t* gh = a.hist_rep + ((size_t)b * kHistReps + blockIdx.x % kHistReps) * kHistWords;
     constexpr int kMaxPer = kFlushTiles * kTile / 64;   // scores per lane at most (the staging buffer)
@@ -955,17 +993,19 @@ __global__ __launch_bounds__(kThreads, 3) void scan_dma_kernel(ScanArgs a, int c
         const uint32_t key = float_key(stage[i]);
         bins[u][0] = key >> 20;
         bins[u][1] = 4096 + (key >> 26);
-        first |= (atomicAdd(&lh[bins[u][0]], 1u) == 0u ? 1u : 0u) << (2 * u);
-        first |= (atomicAdd(&lh[bins[u][1]], 1u) == 0u ? 1u : 0u) << (2 * u + 1);
+        uint32_t c0, c1;
+        lds_inc2_rtn(&lh[bins[u][0]], &lh[bins[u][1]], c0, c1);
+        first |= (c0 == 0u ? 1u : 0u) << (2 * u);
+        first |= (c1 == 0u ? 1u : 0u) << (2 * u + 1);
       }
       if (64 * (u + 1) >= nsc) break;
     }
-    __syncthreads();
+    lds_barrier();   // every count is in
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        if ((first >> (2 * u + e)) & 1u) atomicAdd(&gh[bins[u][e]], lh[bins[u][e]]);
+        if ((first >> (2 * u + e)) & 1u) atomicAdd(&gh[bins[u][e]], lds_read_u32(&lh[bins[u][e]]));
       if (64 * (u + 1) >= nsc) break;
     }
   }
