@@ -67,7 +67,8 @@ def parse():
                    help="skip every workload but the one-request step and the sustained scan")
     p.add_argument("--extra", default=",".join(EXTRAS),
                    help="which other workloads to measure (comma-separated subset of "
-                        + ", ".join(EXTRAS) + ")")
+                        + ", ".join(EXTRAS) + "; multilayer_r1: only retention 1 at "
+                        "131072 tokens, for kernel traces of the two schedules)")
     p.add_argument("--only-extra", action="store_true",
                    help="measure only the --extra workloads and print them (no step line; "
                         "for kernel traces of one workload group)")
@@ -593,10 +594,12 @@ def other_workloads(lsi, synth, torch, dev, extra=EXTRAS):
         torch.cuda.empty_cache()
     if "multilayer" in extra:
         out["multilayer_l131072_x61"] = multilayer(lsi, synth, torch, dev, graph_ms)
+    if "multilayer_r1" in extra:
+        out["multilayer_l131072_x61_r1"] = multilayer(lsi, synth, torch, dev, graph_ms, quick=True)
     return out
 
 
-def multilayer(lsi, synth, torch, dev, graph_ms, n_layers=61):
+def multilayer(lsi, synth, torch, dev, graph_ms, n_layers=61, quick=False):
     """Several layers of one decode step over one request, each layer with
     its own indexer keys and latent cache (one page table): an indexer in
     every layer, each finishing before its layer attends (serial), and the
@@ -641,14 +644,74 @@ def multilayer(lsi, synth, torch, dev, graph_ms, n_layers=61):
                 "speedup_vs_unmodified": {kk: base / v for kk, v in us.items()},
                 "hbm_roofline_frac": frac}
 
-    res = sweep(131072, (1, 2, 4, 8, 16, 32))
+    res = sweep(131072, (1,) if quick else (1, 2, 4, 8, 16, 32))
     res["layers"] = n_layers
+    if quick:
+        res["eager_overlap"] = eager_overlap(lsi, synth, torch, dev, n_layers, side)
+        return res
     res["by_context"] = {f"L{L}": sweep(L, (1, 4)) for L in (10240, 65536, 199680)}
     res["note"] = ("r = retention (one indexer every r layers); serial = each indexer finishes "
                    "before its layer attends; mli = the indexer of layer l runs beside layer l's "
                    "attention on a second stream, after layer l-1; speedups against r1_serial "
                    "of the same context")
     return res
+
+
+def eager_overlap(lsi, synth, torch, dev, n_layers, side, L=131072):
+    """Kernel timeline of one eager multi-layer step per schedule (r = 1),
+    from the start/stop events each dispatch carries (lsi_profile_events):
+    how long an indexer kernel (scan, top-k) and an attention kernel (MLA,
+    combine) run at the same time, against the summed kernel time."""
+    k, dv = 2048, 512
+    wl = synth.scaled(synth.DSA_128K, seq_lens=(L,))
+    dis = [synth.make_decode_inputs(wl, device=dev, planted=False, layer=l) for l in range(n_layers)]
+    req = lsi.Requests(dis[0].seq_lens, dis[0].page_table, L)
+    layers = lsi.Layers([lsi.Cache(d.ikeys, d.iscale, "fp8", 128) for d in dis],
+                        [lsi.Cache(d.kv, None, "bf16", 576) for d in dis], req,
+                        [d.q_idx for d in dis], [d.w for d in dis], [d.q_attn for d in dis], k, dv, 1)
+    out = {}
+    for sched in ("serial", "mli"):
+        for _ in range(3):
+            lsi.multilayer_decode(layers, wl.sm_scale, sched, index_stream=side)
+        torch.cuda.synchronize()
+        timer = lsi.KernelTimer(capacity=16 * n_layers)
+        # queued behind a sleep kernel, so that the whole step is enqueued
+        # before the device starts it and the host's launch time is not in
+        # the timeline
+        try:
+            torch.cuda._sleep(30_000_000)
+        except Exception:
+            pass
+        with timer:
+            lsi.multilayer_decode(layers, wl.sm_scale, sched, index_stream=side)
+        tl = timer.timeline()
+        idx_side = [(a, b) for n, a, b in tl if n.startswith(("scan", "topk"))]
+        att_side = [(a, b) for n, a, b in tl if n.startswith("mla")]
+
+        def union(iv):
+            tot, cs, ce = 0.0, None, None
+            for a, b in sorted(iv):
+                if ce is None or a > ce:
+                    if ce is not None:
+                        tot += ce - cs
+                    cs, ce = a, b
+                else:
+                    ce = max(ce, b)
+            return tot + (ce - cs if ce is not None else 0.0)
+
+        u_all = union(idx_side + att_side)
+        both = union(idx_side) + union(att_side) - u_all   # time with kernels of both kinds running
+        out[sched] = {"kernels": len(tl), "span_us": (max(b for _, _, b in tl) - min(a for _, a, _ in tl)) * 1e3,
+                      "kernel_sum_us": sum(b - a for _, a, b in tl) * 1e3,
+                      "busy_union_us": u_all * 1e3, "indexer_and_attention_concurrent_us": both * 1e3}
+    del layers, dis, req
+    torch.cuda.empty_cache()
+    out["note"] = ("one eager call per schedule, 61 layers at 131072 tokens, r = 1, enqueued behind "
+                   "a sleep kernel; times from the "
+                   "dispatch-carried HIP events of every kernel (lsi_profile_events): span of the "
+                   "step, summed kernel durations, their union, and the time during which an "
+                   "indexer kernel (scan, top-k) and an attention kernel (MLA, combine) run at once")
+    return out
 
 
 def measured_traffic(kernel):

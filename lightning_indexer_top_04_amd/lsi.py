@@ -160,6 +160,15 @@ class KernelTimer:
         return [(self._names[i].decode(), self.events[2 * i].elapsed_time(self.events[2 * i + 1]))
                 for i in range(self.n // 2)]
 
+    def timeline(self):
+        """(kernel name, start ms, end ms) of every kernel, measured from the
+        start of the first one (the events are device timestamps, so kernels
+        launched on different streams share the time axis)."""
+        torch.cuda.synchronize()
+        e0 = self.events[0]
+        return [(self._names[i].decode(), e0.elapsed_time(self.events[2 * i]),
+                 e0.elapsed_time(self.events[2 * i + 1])) for i in range(self.n // 2)]
+
 
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
