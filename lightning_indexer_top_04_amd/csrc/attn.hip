@@ -214,18 +214,24 @@ __global__ __launch_bounds__(kMThreads, 1) void mla_bf16_kernel(AttnArgs a, int 
       prow[i] = e < nr ? a.phys[(int64_t)b * a.k + r0 + e] : -1;
     }
   } else {
+    // every position load first, then every page-table load (at clamped,
+    // in-bounds indexes, masked afterwards): two round trips, where loads
+    // under per-element conditions were issued and waited for one by one
+    int pos[kRowsPerThread], pg[kRowsPerThread];
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
       const int e = tid + i * kMThreads;
-      prow[i] = -1;
-      if (e < nr) {
-        const int pos = a.idx[(int64_t)b * a.k + r0 + e];
-        if (pos >= 0 && pos < L) {
-          const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-          if ((unsigned)page < (unsigned)a.num_pages) prow[i] = page * a.page_size + pos % a.page_size;
-        }
-      }
+      pos[i] = a.idx[(int64_t)b * a.k + min(r0 + min(e, max(nr - 1, 0)), a.k - 1)];
     }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int e = tid + i * kMThreads;
+      if (e >= nr || pos[i] < 0 || pos[i] >= L) pos[i] = -1;
+      pg[i] = a.page_table[(int64_t)b * a.max_pages + (pos[i] >= 0 ? pos[i] / a.page_size : 0)];
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+      prow[i] = pos[i] >= 0 && (unsigned)pg[i] < (unsigned)a.num_pages ? pg[i] * a.page_size + pos[i] % a.page_size : -1;
   }
   bool unresolved = false;
 #pragma unroll
