@@ -192,3 +192,34 @@ def test_multilayer_long_request_graph_replays_match_eager():
             check_attention(t[0].float().cpu().numpy(), a[0].cpu().numpy().astype(np.float64),
                             f"replay {rep} layer {l}")
     _check(dis, layers, 1, "mli", "long graph")
+
+
+def test_kernel_timeline_of_a_two_stream_step():
+    """KernelTimer.timeline() (the per-kernel device timestamps bench.py uses
+    to measure how much the MLI schedule's two streams overlap): every kernel
+    of an eager multi-layer step gets one interval on a shared time axis that
+    starts at the first launched kernel, every interval is well formed and
+    agrees with the duration intervals() gives, and the results still match
+    the oracle."""
+    wl = _wl((5000, 2300), 256)
+    n_layers = 3
+    dis, layers = _build(wl, n_layers, 1)
+    side = torch.cuda.Stream()
+    lsi.multilayer_decode(layers, wl.sm_scale, "mli", index_stream=side)
+    torch.cuda.synchronize()
+    timer = lsi.KernelTimer(capacity=256)
+    with timer:
+        lsi.multilayer_decode(layers, wl.sm_scale, "mli", index_stream=side)
+    tl = timer.timeline()
+    torch.cuda.synchronize()
+    names = [n for n, _, _ in tl]
+    assert len(tl) == timer.n // 2 and len(tl) >= 3 * n_layers
+    assert sum(n.startswith("scan") for n in names) == n_layers
+    assert sum(n.startswith("mla_bf16") for n in names) == n_layers
+    assert tl[0][1] == 0.0           # the axis starts at the first launched kernel
+    for n, a, b in tl:
+        assert a <= b, (n, a, b)
+    # the same events as intervals(): durations agree
+    for (n1, d), (n2, a, b) in zip(timer.intervals(), tl):
+        assert n1 == n2 and abs(d - (b - a)) < 1e-3
+    _check(dis, layers, 1, "mli", "timeline")
