@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--extra", default=",".join(EXTRAS),
                    help="which other workloads to measure (comma-separated subset of "
                         + ", ".join(EXTRAS) + "; multilayer_r1: only retention 1 at "
-                        "131072 tokens, for kernel traces of the two schedules)")
+                        "131072 tokens, plus each schedule's eager kernel timeline)")
     p.add_argument("--only-extra", action="store_true",
                    help="measure only the --extra workloads and print them (no step line; "
                         "for kernel traces of one workload group)")

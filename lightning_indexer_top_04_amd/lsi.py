@@ -162,8 +162,8 @@ class KernelTimer:
 
     def timeline(self):
         """(kernel name, start ms, end ms) of every kernel, measured from the
-        start of the first one (the events are device timestamps, so kernels
-        launched on different streams share the time axis)."""
+        start of the first one launched (the events are device timestamps, so
+        kernels launched on different streams share the time axis)."""
         torch.cuda.synchronize()
         e0 = self.events[0]
         return [(self._names[i].decode(), e0.elapsed_time(self.events[2 * i]),
